@@ -1,0 +1,298 @@
+"""FP64 CPU oracle for the routed mixture-of-experts layer forward.
+
+TEST INFRASTRUCTURE ONLY. This module is the checker the HIP path is compared
+against. Only the test suite, the smoke check of ``__graft_entry__`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run it; the product path
+never does, and it shares no code, table or constant with the HIP kernels.
+
+Everything is plain NumPy in float64 and follows the order the reference pages
+give for the layer: router projection, top-k routing, per-expert SwiGLU over
+block-scaled weights, top-k weighted sum, shared-expert blend.
+
+Sources (the four reference pages, cited by title and section):
+  * "spark_model/layers/moe/forward_k3.rs", ``MoeLayer::forward_k3``: the
+    doc comment lists the five stages (router GEMV, batched top-K, fused expert
+    gate+up, fused silu+down, fused weighted sum + blend); step 2 chooses
+    sigmoid plus a correction bias or softmax and passes ``norm_topk_prob`` and
+    ``routed_scaling_factor``; the E8M0 guard comment and
+    ``k3_e8m0_needs_per_token`` fix the scale-group sizes (GS16 E4M3 for
+    NVFP4, GS32 E8M0 for MXFP4, ``inter*h/16`` against ``inter*h/32`` scale
+    bytes); the NVFP4 branches pass one ``scale2`` value per expert and
+    projection; the EP all-reduce block adds the shared expert once, by a plain
+    residual add when the layer has no shared-expert gate.
+  * "spark_model/layers/moe/forward_atomic_c4.rs",
+    ``MoeLayer::forward_atomic_c4_decode``: routed down projections are summed
+    in FP32 with their routing weights, then cast to BF16 and blended with the
+    shared expert.
+  * "metrale_model_layers/layers/moe/forward_batched.rs",
+    ``MoeLayer::forward_batched``: one router GEMM for all N tokens, then per
+    token routing, expert pair and blend; the grouped FP8 decode comment states
+    that grouping by expert keeps the per-token result.
+
+Readings where the pages are silent (each also listed in the design notes):
+  R1  softmax is taken over all E logits, then the top k are selected (under
+      renormalisation the order of the two does not matter);
+  R2  selection uses the logit (softmax) or sigmoid(logit)+bias (sigmoid),
+      never the exponentiated probabilities;
+  R3  the correction bias steers selection only; weights use sigmoid(logit);
+  R4  no group-limited routing;
+  R5  renormalisation (w /= sum w, no epsilon) comes first, then the routed
+      scaling factor multiplies the routed weights, in both scoring modes;
+  R6  equal selection scores resolve to the lowest expert index, and the
+      selected indices are listed in descending score order;
+  R7  scale groups run along the reduction (column) axis of each row;
+  R8  FP4 packing puts the even column in the low nibble;
+  R9  E4M3 is OCP E4M3FN (no infinities, S.1111.111 is NaN, max 448);
+  R10 NVFP4 carries one FP32 tensor scale per expert per projection;
+  R11 FP8 weights carry one FP32 scale per output row;
+  R12 the shared expert is added with gate 1 (no shared-expert gate).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "e2m1_to_f64", "e8m0_to_f64", "e4m3fn_to_f64", "bf16_to_f64",
+    "unpack_fp4", "dequant", "router_logits", "selection_scores", "route",
+    "silu", "swiglu_expert", "moe_forward", "FORMATS",
+]
+
+FORMATS = ("bf16", "fp8_rowscale", "mxfp4", "nvfp4")
+
+
+# --------------------------------------------------------------------------
+# Element codes, decoded from their bit fields by formula.
+# --------------------------------------------------------------------------
+
+def e2m1_to_f64(codes) -> np.ndarray:
+    """FP4 E2M1 code (4 bits: sign, 2-bit exponent with bias 1, 1-bit
+    mantissa) to float64. Exponent 0 is subnormal: value = 0.5*m.
+    Format named on "forward_k3.rs" (E8M0 guard: native MXFP4 values) and
+    used for NVFP4 values in the NVFP4 branches."""
+    c = np.asarray(codes).astype(np.int64)
+    s = (c >> 3) & 1
+    e = (c >> 1) & 3
+    m = c & 1
+    normal = np.ldexp(1.0 + 0.5 * m, e - 1)
+    sub = 0.5 * m
+    mag = np.where(e == 0, sub, normal)
+    return np.where(s == 1, -mag, mag)
+
+
+def e8m0_to_f64(b) -> np.ndarray:
+    """E8M0 scale byte (unsigned exponent, bias 127, no mantissa) to float64:
+    2**(b-127); 0xFF is NaN. The MXFP4 per-32 block scale ("forward_k3.rs",
+    E8M0 guard comment)."""
+    v = np.asarray(b).astype(np.int64)
+    out = np.ldexp(1.0, v - 127)
+    return np.where(v == 255, np.nan, out)
+
+
+def e4m3fn_to_f64(b) -> np.ndarray:
+    """OCP E4M3FN byte (sign, 4-bit exponent with bias 7, 3-bit mantissa) to
+    float64. Exponent 0 is subnormal: (m/8)*2**-6. S.1111.111 is NaN; there
+    are no infinities. Used for NVFP4 block scales (GS16, "forward_k3.rs"
+    E8M0 guard comment) and for FP8 expert weights (FP8 batch3 branch)."""
+    v = np.asarray(b).astype(np.int64)
+    s = (v >> 7) & 1
+    e = (v >> 3) & 15
+    m = v & 7
+    normal = np.ldexp(1.0 + m / 8.0, e - 7)
+    sub = np.ldexp(m / 8.0, -6)
+    mag = np.where(e == 0, sub, normal)
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
+def bf16_to_f64(u16) -> np.ndarray:
+    """BF16 bit pattern (the high half of an IEEE binary32) to float64."""
+    u = np.asarray(u16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return u.view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Block-scaled dequantisation (exact in float64).
+# --------------------------------------------------------------------------
+
+def unpack_fp4(packed) -> np.ndarray:
+    """[rows, cols/2] bytes -> [rows, cols] 4-bit codes. Reading R8: the low
+    nibble holds the even column."""
+    p = np.asarray(packed, dtype=np.uint8)
+    lo = p & 0x0F
+    hi = p >> 4
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def dequant(w: dict, e: int, rows=None) -> np.ndarray:
+    """Dense float64 [rows, cols] of expert ``e`` of projection ``w``.
+
+    ``w`` holds ``format`` (one of FORMATS), ``data`` ([count, rows, bytes per
+    row] uint8, or uint16 BF16 bits), ``scales``, ``tensor_scale``, ``rows``,
+    ``cols``, ``count``. ``rows`` optionally selects output rows.
+
+      mxfp4:        W = e2m1(q) * e8m0(s[r, c // 32])
+      nvfp4:        W = e2m1(q) * e4m3(s[r, c // 16]) * tensor_scale[e]
+      fp8_rowscale: W = e4m3(q) * rowscale[r]
+      bf16:         W = bf16(q)
+
+    Group sizes and scale counts follow "forward_k3.rs" (E8M0 guard comment
+    and ``k3_e8m0_needs_per_token``: ``inter*h/16`` E4M3 bytes against
+    ``inter*h/32`` E8M0 bytes); the per-expert ``scale2_vals`` of the NVFP4
+    branches give the tensor scale (reading R10); reading R11 gives the FP8
+    row scale.
+    """
+    fmt = w["format"]
+    sel = slice(None) if rows is None else np.asarray(rows)
+    data = np.asarray(w["data"][e])[sel]
+    cols = int(w["cols"])
+    if fmt == "bf16":
+        return bf16_to_f64(data)
+    if fmt == "fp8_rowscale":
+        rs = np.asarray(w["scales"][e], dtype=np.float64)[sel]
+        return e4m3fn_to_f64(data) * rs[:, None]
+    codes = unpack_fp4(data)
+    vals = e2m1_to_f64(codes)
+    sc = np.asarray(w["scales"][e])[sel]
+    if fmt == "mxfp4":
+        s = e8m0_to_f64(sc)
+        return vals * np.repeat(s, 32, axis=1)[:, :cols]
+    if fmt == "nvfp4":
+        s = e4m3fn_to_f64(sc)
+        ts = float(np.asarray(w["tensor_scale"], dtype=np.float64)[e])
+        return vals * np.repeat(s, 16, axis=1)[:, :cols] * ts
+    raise ValueError(f"unknown format {fmt!r}")
+
+
+# --------------------------------------------------------------------------
+# Router and routing.
+# --------------------------------------------------------------------------
+
+def router_logits(x: np.ndarray, wr: np.ndarray) -> np.ndarray:
+    """z[t, e] = sum_h x[t, h] * Wr[e, h]: one projection for all N tokens
+    ("forward_k3.rs" step 1, the gate GEMV that reads the router once for
+    the batch; "forward_batched.rs", one gate GEMM with M = N)."""
+    return np.asarray(x, np.float64) @ np.asarray(wr, np.float64).T
+
+
+def selection_scores(z: np.ndarray, scoring: str, bias=None) -> np.ndarray:
+    """Score used to pick the experts: the logit for softmax routing, or
+    sigmoid(logit) + correction bias for sigmoid routing ("forward_k3.rs"
+    step 2, sigmoid+bias for DeepSeek-V3-style routers; readings R2, R3)."""
+    z = np.asarray(z, np.float64)
+    if scoring == "softmax":
+        return z.copy()
+    if scoring == "sigmoid":
+        s = 1.0 / (1.0 + np.exp(-z))
+        if bias is not None:
+            s = s + np.asarray(bias, np.float64)[None, :]
+        return s
+    raise ValueError(f"unknown scoring {scoring!r}")
+
+
+def route(z: np.ndarray, k: int, scoring: str, bias=None,
+          renorm: bool = True, rsf: float = 1.0):
+    """Top-k routing for every token ("forward_k3.rs" step 2 and
+    "forward_atomic_c4.rs": ``moe_topk_{sigmoid,softmax}_batched`` with
+    ``norm_topk_prob`` and ``routed_scaling_factor``).
+
+    Returns ``idx`` [N, k] int64 in descending score order (lowest index first
+    among equal scores, reading R6) and ``w`` [N, k] float64.
+    """
+    z = np.asarray(z, np.float64)
+    n, num_e = z.shape
+    s = selection_scores(z, scoring, bias)
+    idx = np.empty((n, k), dtype=np.int64)
+    w = np.empty((n, k), dtype=np.float64)
+    ar = np.arange(num_e)
+    for t in range(n):
+        # primary key: score descending; secondary: index ascending
+        order = np.lexsort((ar, -s[t]))
+        sel = order[:k]
+        idx[t] = sel
+        if scoring == "softmax":
+            p = np.exp(z[t] - z[t].max())
+            p = p / p.sum()
+            wt = p[sel]
+        else:
+            wt = 1.0 / (1.0 + np.exp(-z[t, sel]))
+        if renorm:
+            wt = wt / wt.sum()
+        w[t] = wt * rsf
+    return idx, w
+
+
+# --------------------------------------------------------------------------
+# Experts.
+# --------------------------------------------------------------------------
+
+def silu(v):
+    """silu(v) = v / (1 + exp(-v))."""
+    v = np.asarray(v, np.float64)
+    return v / (1.0 + np.exp(-v))
+
+
+def swiglu_expert(wg: np.ndarray, wu: np.ndarray, wd: np.ndarray, xt: np.ndarray):
+    """One expert on one token: g = Wg x, u = Wu x, a = silu(g) * u,
+    d = Wd a (the gate+up then silu+down kernel pair named on every page).
+    Returns (g, u, a, d)."""
+    g = wg @ xt
+    u = wu @ xt
+    a = silu(g) * u
+    d = wd @ a
+    return g, u, a, d
+
+
+def moe_forward(cfg: dict, layer: dict, x_bits, rows=None) -> dict:
+    """The whole layer for N tokens, in float64.
+
+    ``cfg`` keys: H, I, E, k, I_s, scoring ('softmax' | 'sigmoid'), renorm,
+    rsf. ``layer`` holds ``router`` {weight: BF16 bits [E, H], bias: [E] or
+    None}, ``experts`` {gate, up, down} and ``shared`` (same, count 1) or None,
+    each projection a dict as taken by :func:`dequant`. ``x_bits`` is the BF16
+    bit pattern of the [N, H] input. ``rows`` optionally restricts the output
+    to those hidden rows (the down projections then use only those rows).
+
+    y[t] = sum_j w[t, j] * d_{idx[t, j]}(x_t) + s(x_t)   (reading R12)
+    """
+    x = bf16_to_f64(np.asarray(x_bits))
+    n, h = x.shape
+    assert h == cfg["H"]
+    wr = bf16_to_f64(np.asarray(layer["router"]["weight"]))
+    bias = layer["router"].get("bias")
+    bias = None if bias is None else np.asarray(bias, np.float64)
+    z = router_logits(x, wr)
+    idx, w = route(z, cfg["k"], cfg["scoring"], bias, cfg["renorm"], cfg["rsf"])
+
+    out_rows = np.arange(h) if rows is None else np.asarray(rows)
+    y = np.zeros((n, out_rows.size), dtype=np.float64)
+    ex = layer["experts"]
+    cache = {}
+    a_slots = np.zeros((n, cfg["k"], cfg["I"]), dtype=np.float64)
+    for t in range(n):
+        for j in range(cfg["k"]):
+            e = int(idx[t, j])
+            if e not in cache:
+                cache[e] = (dequant(ex["gate"], e), dequant(ex["up"], e),
+                            dequant(ex["down"], e, rows=out_rows))
+            wg, wu, wd = cache[e]
+            _, _, a, d = swiglu_expert(wg, wu, wd, x[t])
+            a_slots[t, j] = a
+            y[t] += w[t, j] * d
+    s_out = None
+    if layer.get("shared") is not None and cfg.get("I_s", 0) > 0:
+        sh = layer["shared"]
+        wg = dequant(sh["gate"], 0)
+        wu = dequant(sh["up"], 0)
+        wd = dequant(sh["down"], 0, rows=out_rows)
+        s_out = np.zeros_like(y)
+        for t in range(n):
+            _, _, _, d = swiglu_expert(wg, wu, wd, x[t])
+            s_out[t] = d
+        y = y + s_out
+    return {"y": y, "z": z, "idx": idx, "w": w, "a": a_slots,
+            "shared": s_out, "rows": out_rows}
