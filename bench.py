@@ -1,0 +1,218 @@
+"""Benchmark of the routed MoE layer forward on one MI355X.
+
+python bench.py [--steps K] [--warmup W] [--config NAME] [--n N]
+
+A step is one moe_forward call (router, top-k, expert gate+up, down, blend)
+on one batch of N synthetic tokens with the inputs already in HBM. Batches
+rotate through a pool and the weights through enough copies that a call does
+not find its experts in the 256 MB Infinity Cache left by earlier calls.
+Prints one JSON line (µs per call, expert-weight GB/s, roofline of the
+dominant kernel from HIP events recorded inside the call, and the FP64 oracle
+timed on the host cores as a reference point).
+"""
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+KERNELS = ["router", "topk_plan", "gate_up", "down", "blend"]
+
+
+def hip():
+    L = ctypes.CDLL("libamdhip64.so")
+    L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    L.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return L
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--config", default="qwen3_30b_a3b_mxfp4")
+    p.add_argument("--n", type=int, default=None, help="tokens per call")
+    p.add_argument("--accum", default=None, choices=[None, "slot", "atomic"])
+    p.add_argument("--pool", type=int, default=64, help="distinct token batches")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="budget of the oracle baseline (0 = skip)")
+    p.add_argument("--no-trace", action="store_true", help="time without per-kernel events")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(expert parallelism would shard experts across GPUs; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from mixture_experts_layer_35_amd import Layer, num_launches
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    cfg = dict(synth.CONFIGS[args.config])
+    n = args.n or cfg["n_list"][0]
+    layer = synth.make_layer(args.config, device=dev)
+    by = synth.layer_bytes(layer)
+
+    # rotate weight copies so that the traffic between two uses of a copy is
+    # more than twice the Infinity Cache
+    per_call_guess = min(cfg["E"], n * cfg["k"]) * by["expert"] + by["shared"]
+    copies = max(1, min(32, math.ceil(2 * MALL_BYTES / max(1, per_call_guess)) + 1))
+    layers = [layer] + [synth.clone_weights(layer) for _ in range(copies - 1)]
+    bound = [Layer(l, n, accum=args.accum) for l in layers]
+    xs = [synth.make_tokens(layer, n, 1000 + i) for i in range(args.pool)]
+    out = torch.empty_like(xs[0])
+    k = cfg["k"]
+    idx_all = torch.zeros((args.steps, n, k), dtype=torch.int32, device=dev)
+
+    H = hip()
+    nl = num_launches(bound[0].cfg, n)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def mk_events(count):
+        evs = []
+        for _ in range(count):
+            e = ctypes.c_void_p()
+            assert H.hipEventCreate(ctypes.byref(e)) == 0
+            evs.append(e.value)
+        return evs
+
+    ev = None if args.no_trace else [mk_events(nl + 1) for _ in range(args.steps)]
+
+    for i in range(args.warmup):
+        bound[i % copies].forward(xs[i % args.pool], out=out)
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        bound[(args.warmup + i) % copies].forward(
+            xs[i % args.pool], out=out, idx=idx_all[i],
+            events=None if ev is None else ev[i], stream=stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us_per_call = wall / args.steps * 1e6
+
+    # distinct experts per call -> algorithmic bytes
+    idx_np = idx_all.cpu().numpy()
+    U = np.array([len(np.unique(idx_np[i])) for i in range(args.steps)])
+    sgu = sdn = 0
+    if layer["shared"] is not None:
+        sh = layer["shared"]
+        sgu = synth.projection_bytes(sh["gate"]) + synth.projection_bytes(sh["up"])
+        sdn = synth.projection_bytes(sh["down"])
+    bytes_gu = U * by["expert_gate_up"] + sgu
+    bytes_dn = U * by["expert_down"] + sdn
+    expert_bytes = bytes_gu + bytes_dn
+    total_bytes = expert_bytes + by["router"]
+
+    per_kernel = {}
+    roof = None
+    if ev is not None:
+        durs = np.zeros((args.steps, nl), np.float64)
+        f = ctypes.c_float()
+        for i in range(args.steps):
+            for j in range(nl):
+                H.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(ev[i][j]),
+                                      ctypes.c_void_p(ev[i][j + 1]))
+                durs[i, j] = f.value * 1e3  # us
+        per_kernel = {KERNELS[j]: round(float(durs[:, j].mean()), 3) for j in range(nl)}
+        gu_us = durs[:, 2]
+        dn_us = durs[:, 3]
+        dom = "gate_up" if gu_us.mean() >= dn_us.mean() else "down"
+        d_us = gu_us if dom == "gate_up" else dn_us
+        d_bytes = bytes_gu if dom == "gate_up" else bytes_dn
+        achieved = float(d_bytes.sum() / (d_us.sum() * 1e-6) / 1e9)
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None,
+                "bytes_per_launch": float(d_bytes.mean()), "avg_launch_us": float(d_us.mean())}
+        experts_us = gu_us + dn_us
+        experts_gbs = float(expert_bytes.sum() / (experts_us.sum() * 1e-6) / 1e9)
+        for row in ev:
+            for e in row:
+                H.hipEventDestroy(ctypes.c_void_p(e))
+    else:
+        experts_gbs = None
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(layer, xs, n, args.cpu_seconds)
+
+    rec = {
+        "metric": "MoE layer us/call + expert-weight HBM GB/s (% peak) at N=1,3,4 tokens",
+        "value": round(us_per_call, 3),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_per_call / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config} H={cfg['H']} I={cfg['I']} E={cfg['E']} "
+                               f"k={k} I_s={cfg['I_s']} {cfg['routed_fmt']} N={n}",
+                   "n_tokens": n, "routed_format": cfg["routed_fmt"],
+                   "accum": args.accum or cfg["accum"], "weight_copies": copies,
+                   "token_batches": args.pool, "launch": "eager stream, 5 kernels"},
+        "expert_weight_gbps_call": round(float(expert_bytes.mean() / (us_per_call * 1e-6) / 1e9), 1),
+        "expert_weight_gbps_kernels": None if experts_gbs is None else round(experts_gbs, 1),
+        "pct_hbm_peak_kernels": None if experts_gbs is None else round(100 * experts_gbs / HBM_PEAK_GBS, 2),
+        "distinct_experts_mean": float(U.mean()),
+        "bytes_per_call_mean": float(total_bytes.mean()),
+        "per_kernel_us": per_kernel,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(layer, xs, n, budget_s):
+    """The FP64 oracle on the host: as many calls of the same workload as fit
+    in the budget (at least one), reported per call."""
+    import numpy as np
+    import torch
+    import synth
+    from oracle import moe_forward
+    from threadpoolctl import threadpool_limits
+    npl = synth.as_numpy(layer)
+    times = []
+    start = time.perf_counter()
+    i = 0
+    with threadpool_limits(1):
+        while True:
+            xb = xs[i % len(xs)].cpu().view(torch.int16).numpy().view(np.uint16)
+            t = time.perf_counter()
+            moe_forward(npl["cfg"], npl, xb)
+            times.append(time.perf_counter() - t)
+            i += 1
+            if time.perf_counter() - start > budget_s:
+                break
+    us = float(np.median(times) * 1e6)
+    return {"value": round(us, 1), "unit": "us/call", "cores": 1, "kind": "oracle",
+            "sample": f"{len(times)} full calls of the same workload (N={n}), median, "
+                      f"single-threaded NumPy FP64"}
+
+
+if __name__ == "__main__":
+    main()

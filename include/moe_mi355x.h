@@ -1,0 +1,187 @@
+/*
+ * moe_mi355x.h - C ABI of the routed mixture-of-experts layer forward for
+ * small token batches on AMD Instinct MI355X (gfx950).
+ *
+ * One call computes, for N tokens x[N,H] (BF16):
+ *   z      = x * Wr^T                                    router projection
+ *   idx, w = top-k of z (softmax) or of sigmoid(z)+bias (sigmoid),
+ *            optional renormalisation, times the routed scaling factor
+ *   a      = silu(Wg[e] x) * (Wu[e] x)  per routed (token, expert) pair
+ *   y[t]   = sum_j w[t,j] * Wd[idx[t,j]] a  +  shared expert(x[t])
+ *   out    = BF16(y) (round to nearest even)
+ *
+ * The stages and their arguments follow the reference pages:
+ *   "spark_model/layers/moe/forward_k3.rs", MoeLayer::forward_k3 (the five
+ *     stages of the fused forward; step 2 for sigmoid+bias vs softmax routing,
+ *     norm_topk_prob and routed_scaling_factor; the E8M0 guard for GS32 E8M0
+ *     against GS16 E4M3 scales; scale2 per expert for NVFP4; the plain
+ *     residual add of the shared expert when there is no shared-expert gate);
+ *   "spark_model/layers/moe/forward_atomic_c4.rs",
+ *     MoeLayer::forward_atomic_c4_decode (FP32 accumulation of the weighted
+ *     down projections into an [N,H] buffer, then the BF16 cast; the scratch
+ *     size check that refuses with a need/have message);
+ *   "metrale_model_layers/layers/moe/forward_batched.rs",
+ *     MoeLayer::forward_batched (one router GEMM with M = N; the grouped FP8
+ *     decode in which every expert streams its weights once for all rows and
+ *     the result equals the per-token loop's).
+ *
+ * Memory ownership: the caller owns every buffer (weights, x, out, top-k
+ * outputs, workspace). The library never allocates, frees or synchronises
+ * and never reads device memory on the host. Pointers marked "device" must be
+ * device memory of the current HIP device; results are valid once the stream
+ * reaches them, and every input must stay alive until then.
+ *
+ * Errors: every argument is validated on the host before anything is
+ * enqueued; an invalid call returns a non-zero moe_status and enqueues
+ * nothing. moe_last_error() then gives a thread-local message. There are no
+ * silent fallbacks: a combination the library does not implement is refused
+ * with MOE_ERR_UNSUPPORTED.
+ *
+ * Concurrency: calls are re-entrant. Two calls that share a workspace must be
+ * ordered (same stream, or synchronised); the workspace carries per-call
+ * state.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* a null, misaligned, mis-sized or out-of-range argument */
+  MOE_ERR_UNSUPPORTED = 2, /* a valid request this library does not implement */
+  MOE_ERR_WORKSPACE = 3,   /* workspace too small ("need X bytes, have Y") */
+  MOE_ERR_HIP = 4          /* a HIP launch or runtime error */
+} moe_status;
+
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_scoring;
+
+/* How routed down projections are summed.
+ * SLOT: each output row tile sums its experts in a fixed order (bitwise
+ *       deterministic run to run).
+ * ATOMIC_F32: FP32 atomic adds of w * down into an [N,H] accumulator in the
+ *       workspace, then a BF16 cast ("forward_atomic_c4.rs"); summation order
+ *       varies run to run. */
+typedef enum { MOE_ACCUM_SLOT = 0, MOE_ACCUM_ATOMIC_F32 = 1 } moe_accum;
+
+/* Which kernel family runs the experts. DECODE streams each selected expert
+ * once for all of its tokens with VALU dot products (N <= 4). GROUPED sorts
+ * the (token, expert) pairs by expert and runs them as per-expert tiles on
+ * MFMA (N <= MOE_MAX_TOKENS). AUTO picks DECODE for N <= 4. */
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_GROUPED = 2 } moe_path;
+
+/* Weight element formats (all little-endian, row-major):
+ *   BF16          data [count, rows, cols] BF16; no scales.
+ *   FP8_ROWSCALE  data [count, rows, cols] OCP E4M3FN bytes;
+ *                 scales [count, rows] FP32, one per output row.
+ *   MXFP4         data [count, rows, cols/2] E2M1 pairs, even column in the
+ *                 low nibble; scales [count, rows, cols/32] E8M0 bytes.
+ *   NVFP4         data as MXFP4; scales [count, rows, cols/16] E4M3FN bytes;
+ *                 tensor_scale [count] FP32 (one per expert).
+ * W[e,r,c] = value(data) * block or row scale (* tensor_scale[e] for NVFP4).
+ * Scale groups run along the reduction axis (columns). */
+typedef enum {
+  MOE_FMT_BF16 = 0,
+  MOE_FMT_FP8_ROWSCALE = 1,
+  MOE_FMT_MXFP4 = 2,
+  MOE_FMT_NVFP4 = 3
+} moe_format;
+
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOPK 16
+#define MOE_MAX_DECODE_TOKENS 4
+#define MOE_MAX_TOKENS 4096
+
+typedef struct {
+  int32_t hidden;               /* H: model width (columns of gate/up, rows of down) */
+  int32_t inter;                /* I: routed expert intermediate size */
+  int32_t num_experts;          /* E: 1..MOE_MAX_EXPERTS */
+  int32_t top_k;                /* k: 1..min(E, MOE_MAX_TOPK) */
+  int32_t shared_inter;         /* I_s: shared expert intermediate size, 0 = none */
+  int32_t scoring;              /* moe_scoring */
+  int32_t norm_topk_prob;       /* 1: divide the k weights by their sum */
+  float routed_scaling_factor;  /* multiplies the routed weights (after renorm) */
+  int32_t accum_mode;           /* moe_accum */
+  int32_t path;                 /* moe_path */
+} moe_cfg;
+
+typedef struct {
+  const void* weight;  /* device, BF16 [E, H], 16-byte aligned */
+  const float* bias;   /* device, FP32 [E] correction bias for sigmoid scoring, or NULL */
+} moe_router;
+
+typedef struct {
+  int32_t format;            /* moe_format */
+  const void* data;          /* device, 16-byte aligned */
+  size_t data_bytes;         /* must equal the size implied by format/count/rows/cols */
+  const void* scales;        /* device; NULL for BF16 */
+  size_t scale_bytes;        /* must equal the size implied by the format */
+  const float* tensor_scale; /* device FP32 [count] for NVFP4, else NULL */
+  int32_t rows, cols, count;
+} moe_weight;
+
+/* gate and up: rows = I (I_s), cols = H; down: rows = H, cols = I (I_s).
+ * All three projections of one set share one format. */
+typedef struct {
+  moe_weight gate, up, down;
+} moe_experts;
+
+/* Optional per-call outputs (each pointer may be NULL, device memory). */
+typedef struct {
+  uint32_t* idx;  /* [N, k] selected experts, descending score, lowest index on ties */
+  float* weights; /* [N, k] routing weights (after renorm and scaling) */
+  float* logits;  /* [N, E] router logits (FP32) */
+} moe_topk_out;
+
+/* Optional timing hook: when non-NULL, events[i] is recorded on the stream
+ * right before launch i of the call and events[num_launches] after the last
+ * one. count must be >= num_launches + 1 (moe_num_launches gives the
+ * number). The events must be created by the caller. */
+typedef struct {
+  void** events; /* hipEvent_t[count] */
+  int32_t count;
+} moe_trace;
+
+/* Bytes of workspace moe_forward needs for cfg and up to max_tokens tokens.
+ * Returns 0 if cfg is invalid (moe_last_error() says why). */
+size_t moe_workspace_bytes(const moe_cfg* cfg, int32_t max_tokens);
+
+/* Validates a call exactly as moe_forward does, without enqueueing anything.
+ * Host only; never touches device memory. */
+moe_status moe_validate(const moe_cfg* cfg, const moe_router* router,
+                        const moe_experts* experts, const moe_experts* shared,
+                        int32_t n_tokens, size_t workspace_bytes);
+
+/* Number of kernel launches moe_forward makes for this call (for moe_trace).
+ * Returns -1 if the call is invalid. */
+int32_t moe_num_launches(const moe_cfg* cfg, int32_t n_tokens);
+
+/* The layer forward. x: device BF16 [n_tokens, H]; out: device BF16
+ * [n_tokens, H] (every element is written); shared: NULL iff
+ * cfg->shared_inter == 0; topk, trace: optional. workspace: device, 256-byte
+ * aligned, at least moe_workspace_bytes(cfg, n_tokens) bytes; its first 256
+ * bytes must be zero before the first call that uses it (every call leaves
+ * them zero). stream: hipStream_t (NULL = default stream). */
+moe_status moe_forward(const moe_cfg* cfg, const moe_router* router,
+                       const moe_experts* experts, const moe_experts* shared,
+                       const void* x, int32_t n_tokens, void* out,
+                       const moe_topk_out* topk, void* workspace,
+                       size_t workspace_bytes, void* stream,
+                       const moe_trace* trace);
+
+const char* moe_status_str(moe_status status);
+const char* moe_last_error(void);
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

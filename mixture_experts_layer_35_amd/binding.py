@@ -1,0 +1,226 @@
+"""ctypes binding of libmoe_mi355x.so (argument marshalling only).
+
+Every step of the layer runs in the library's HIP kernels; this module only
+turns torch tensors into the C structs of ``include/moe_mi355x.h``. It raises
+if the library has not been built: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+SCORING = {"softmax": 0, "sigmoid": 1}
+ACCUM = {"slot": 0, "atomic": 1}
+PATH = {"auto": 0, "decode": 1, "grouped": 2}
+FORMAT = {"bf16": 0, "fp8_rowscale": 1, "mxfp4": 2, "nvfp4": 3}
+
+EXPORTED = ("moe_abi_version", "moe_last_error", "moe_status_str", "moe_workspace_bytes",
+            "moe_validate", "moe_num_launches", "moe_forward")
+
+
+class MoeCfg(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("shared_inter", ctypes.c_int32), ("scoring", ctypes.c_int32),
+                ("norm_topk_prob", ctypes.c_int32), ("routed_scaling_factor", ctypes.c_float),
+                ("accum_mode", ctypes.c_int32), ("path", ctypes.c_int32)]
+
+
+class MoeRouter(ctypes.Structure):
+    _fields_ = [("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
+
+
+class MoeWeight(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("data", ctypes.c_void_p),
+                ("data_bytes", ctypes.c_size_t), ("scales", ctypes.c_void_p),
+                ("scale_bytes", ctypes.c_size_t), ("tensor_scale", ctypes.c_void_p),
+                ("rows", ctypes.c_int32), ("cols", ctypes.c_int32), ("count", ctypes.c_int32)]
+
+
+class MoeExperts(ctypes.Structure):
+    _fields_ = [("gate", MoeWeight), ("up", MoeWeight), ("down", MoeWeight)]
+
+
+class MoeTopkOut(ctypes.Structure):
+    _fields_ = [("idx", ctypes.c_void_p), ("weights", ctypes.c_void_p),
+                ("logits", ctypes.c_void_p)]
+
+
+class MoeTrace(ctypes.Structure):
+    _fields_ = [("events", ctypes.c_void_p), ("count", ctypes.c_int32)]
+
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{status_str(status)}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mixture_experts_layer_35_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.moe_abi_version.restype = ctypes.c_int32
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_status_str.restype = ctypes.c_char_p
+        L.moe_status_str.argtypes = [ctypes.c_int]
+        L.moe_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_workspace_bytes.argtypes = [ctypes.POINTER(MoeCfg), ctypes.c_int32]
+        L.moe_validate.restype = ctypes.c_int
+        L.moe_validate.argtypes = [ctypes.POINTER(MoeCfg), ctypes.POINTER(MoeRouter),
+                                   ctypes.POINTER(MoeExperts), ctypes.POINTER(MoeExperts),
+                                   ctypes.c_int32, ctypes.c_size_t]
+        L.moe_num_launches.restype = ctypes.c_int32
+        L.moe_num_launches.argtypes = [ctypes.POINTER(MoeCfg), ctypes.c_int32]
+        L.moe_forward.restype = ctypes.c_int
+        L.moe_forward.argtypes = [ctypes.POINTER(MoeCfg), ctypes.POINTER(MoeRouter),
+                                  ctypes.POINTER(MoeExperts), ctypes.POINTER(MoeExperts),
+                                  ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                  ctypes.POINTER(MoeTopkOut), ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p, ctypes.POINTER(MoeTrace)]
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().moe_status_str(int(status)).decode()
+
+
+def last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def abi_version() -> int:
+    return int(lib().moe_abi_version())
+
+
+# ------------------------------------------------------------------ structs
+
+def make_cfg(cfg: dict, accum: str | None = None, path: str = "auto") -> MoeCfg:
+    c = MoeCfg()
+    c.hidden = cfg["H"]
+    c.inter = cfg["I"]
+    c.num_experts = cfg["E"]
+    c.top_k = cfg["k"]
+    c.shared_inter = cfg.get("I_s", 0) or 0
+    c.scoring = SCORING[cfg["scoring"]]
+    c.norm_topk_prob = 1 if cfg["renorm"] else 0
+    c.routed_scaling_factor = float(cfg["rsf"])
+    c.accum_mode = ACCUM[accum or cfg.get("accum", "slot")]
+    c.path = PATH[path]
+    return c
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def make_weight(p: dict) -> MoeWeight:
+    w = MoeWeight()
+    w.format = FORMAT[p["format"]]
+    w.data = _ptr(p["data"])
+    w.data_bytes = _nbytes(p["data"])
+    w.scales = _ptr(p.get("scales"))
+    w.scale_bytes = _nbytes(p.get("scales"))
+    w.tensor_scale = _ptr(p.get("tensor_scale"))
+    w.rows, w.cols, w.count = p["rows"], p["cols"], p["count"]
+    return w
+
+
+def make_experts(s: dict | None) -> MoeExperts | None:
+    if s is None:
+        return None
+    e = MoeExperts()
+    e.gate = make_weight(s["gate"])
+    e.up = make_weight(s["up"])
+    e.down = make_weight(s["down"])
+    return e
+
+
+def make_router(r: dict) -> MoeRouter:
+    m = MoeRouter()
+    m.weight = _ptr(r["weight"])
+    m.bias = _ptr(r.get("bias"))
+    return m
+
+
+def _ref(obj):
+    return None if obj is None else ctypes.byref(obj)
+
+
+# ------------------------------------------------------------------ calls
+
+def workspace_bytes(cfg: MoeCfg, max_tokens: int) -> int:
+    n = lib().moe_workspace_bytes(ctypes.byref(cfg), int(max_tokens))
+    if n == 0:
+        raise MoeError(MOE_ERR_INVALID_ARG, last_error())
+    return int(n)
+
+
+def num_launches(cfg: MoeCfg, n_tokens: int) -> int:
+    return int(lib().moe_num_launches(ctypes.byref(cfg), int(n_tokens)))
+
+
+def validate(cfg: MoeCfg, router: MoeRouter, experts: MoeExperts, shared: MoeExperts | None,
+             n_tokens: int, ws_bytes: int) -> int:
+    return int(lib().moe_validate(ctypes.byref(cfg), ctypes.byref(router), _ref(experts),
+                                  _ref(shared), int(n_tokens), int(ws_bytes)))
+
+
+class Layer:
+    """A packed layer (dict of device tensors from ``synth.make_layer`` or the
+    caller's own) bound to the C structs, plus its workspace."""
+
+    def __init__(self, layer: dict, max_tokens: int, accum: str | None = None,
+                 path: str = "auto"):
+        import torch
+        self.layer = layer
+        self.cfg = make_cfg(layer["cfg"], accum, path)
+        self.router = make_router(layer["router"])
+        self.experts = make_experts(layer["experts"])
+        self.shared = make_experts(layer["shared"])
+        self.max_tokens = max_tokens
+        nbytes = workspace_bytes(self.cfg, max_tokens)
+        dev = layer["router"]["weight"].device
+        # zero-filled once: the first 256 bytes must start at zero
+        self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+
+    def forward(self, x, out=None, idx=None, weights=None, logits=None, stream=None,
+                events=None):
+        import torch
+        n = x.shape[0]
+        if out is None:
+            out = torch.empty_like(x)
+        topk = None
+        if idx is not None or weights is not None or logits is not None:
+            topk = MoeTopkOut(_ptr(idx), _ptr(weights), _ptr(logits))
+        trace = None
+        if events is not None:
+            arr = (ctypes.c_void_p * len(events))(*[int(e.cuda_event) if hasattr(e, "cuda_event")
+                                                    else int(e) for e in events])
+            trace = MoeTrace(ctypes.cast(arr, ctypes.c_void_p), len(events))
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+        st = lib().moe_forward(ctypes.byref(self.cfg), ctypes.byref(self.router),
+                               _ref(self.experts), _ref(self.shared), x.data_ptr(), int(n),
+                               out.data_ptr(), _ref(topk), self.workspace.data_ptr(),
+                               self.workspace.numel(), ctypes.c_void_p(stream), _ref(trace))
+        if st != MOE_OK:
+            raise MoeError(st, last_error())
+        return out

@@ -128,6 +128,14 @@ def unpack_fp4(packed) -> np.ndarray:
     return out
 
 
+def _decode(fn, codes, ncodes: int) -> np.ndarray:
+    """Apply a per-code decoder to an array of codes by decoding each of the
+    ``ncodes`` possible codes once and indexing (same values as calling
+    ``fn`` element by element)."""
+    table = fn(np.arange(ncodes))
+    return table[np.asarray(codes, dtype=np.intp)]
+
+
 def dequant(w: dict, e: int, rows=None) -> np.ndarray:
     """Dense float64 [rows, cols] of expert ``e`` of projection ``w``.
 
@@ -154,17 +162,17 @@ def dequant(w: dict, e: int, rows=None) -> np.ndarray:
         return bf16_to_f64(data)
     if fmt == "fp8_rowscale":
         rs = np.asarray(w["scales"][e], dtype=np.float64)[sel]
-        return e4m3fn_to_f64(data) * rs[:, None]
-    codes = unpack_fp4(data)
-    vals = e2m1_to_f64(codes)
+        return _decode(e4m3fn_to_f64, data, 256) * rs[:, None]
+    vals = _decode(e2m1_to_f64, unpack_fp4(data), 16)
     sc = np.asarray(w["scales"][e])[sel]
+    nrows = vals.shape[0]
     if fmt == "mxfp4":
-        s = e8m0_to_f64(sc)
-        return vals * np.repeat(s, 32, axis=1)[:, :cols]
+        s = _decode(e8m0_to_f64, sc, 256)
+        return (vals.reshape(nrows, cols // 32, 32) * s[:, :, None]).reshape(nrows, cols)
     if fmt == "nvfp4":
-        s = e4m3fn_to_f64(sc)
+        s = _decode(e4m3fn_to_f64, sc, 256)
         ts = float(np.asarray(w["tensor_scale"], dtype=np.float64)[e])
-        return vals * np.repeat(s, 16, axis=1)[:, :cols] * ts
+        return (vals.reshape(nrows, cols // 16, 16) * (s * ts)[:, :, None]).reshape(nrows, cols)
     raise ValueError(f"unknown format {fmt!r}")
 
 

@@ -73,12 +73,12 @@ def seed_for(*parts) -> int:
     return int((int(st[0]) << 31) ^ int(st[1])) & ((1 << 63) - 1)
 
 
-def reduced(name: str, **over) -> dict:
-    """A copy of config ``name`` with some fields replaced (smaller shapes for
+def reduced(base: str, **over) -> dict:
+    """A copy of config ``base`` with some fields replaced (smaller shapes for
     tests that the oracle finishes in seconds)."""
-    c = copy.deepcopy(CONFIGS[name])
+    c = copy.deepcopy(CONFIGS[base])
     c.update(over)
-    c["name"] = over.get("name", name + "_reduced")
+    c["name"] = over.get("name", base + "_reduced")
     return c
 
 

@@ -1,0 +1,85 @@
+"""Shared helpers for the GPU parity tests: tie-free token filter (through
+the oracle), running the HIP path, and the comparison bar."""
+
+import numpy as np
+import torch
+
+import synth
+from oracle import moe_forward, router_logits, selection_scores, bf16_to_f64
+
+# consecutive gap among the top k+1 selection scores; about 100x the FP32
+# error of a router logit at H = 7168
+TIE_GAP = 1e-3
+# per-token relative L2 error of the BF16 output
+OUT_RTOL = 1e-2
+# routing weights
+W_RTOL = 1e-5
+
+
+def tie_free_filter(npl, gap=TIE_GAP):
+    cfg = npl["cfg"]
+    wr = bf16_to_f64(npl["router"]["weight"])
+    bias = npl["router"]["bias"]
+    k = cfg["k"]
+
+    def accept(x_cpu):
+        xb = x_cpu.view(torch.int16).numpy().view(np.uint16)
+        s = selection_scores(router_logits(bf16_to_f64(xb), wr), cfg["scoring"], bias)
+        srt = -np.sort(-s, axis=1)[:, :min(k + 1, s.shape[1])]
+        if srt.shape[1] < 2:
+            return np.ones(s.shape[0], bool)
+        return (np.diff(-srt, axis=1) >= gap).all(axis=1)
+
+    return accept
+
+
+def bits(t):
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def run_hip(layer, x, accum=None, out=None):
+    from mixture_experts_layer_35_amd import Layer
+    n = x.shape[0]
+    cfg = layer["cfg"]
+    L = Layer(layer, n, accum=accum)
+    dev = x.device
+    idx = torch.full((n, cfg["k"]), 0xFFFF, dtype=torch.int32, device=dev)
+    w = torch.full((n, cfg["k"]), float("nan"), dtype=torch.float32, device=dev)
+    logits = torch.full((n, cfg["E"]), float("nan"), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.full_like(x, float("nan"))
+    L.forward(x, out=out, idx=idx, weights=w, logits=logits)
+    torch.cuda.synchronize()
+    return out, idx, w, logits, L
+
+
+def rel_l2_per_token(got, want):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    num = np.linalg.norm(got - want, axis=1)
+    den = np.linalg.norm(want, axis=1)
+    return num / den
+
+
+def check_against_oracle(layer, x, accum=None, rows=None, label=""):
+    """Run the HIP path and the oracle on the same inputs and assert the
+    bar: indices bit-exact, weights within W_RTOL, logits within 1e-5 (abs,
+    relative to their scale), per-token relative L2 of the output within
+    OUT_RTOL. Returns the measured errors."""
+    npl = synth.as_numpy(layer)
+    xb = bits(x)
+    ref = moe_forward(npl["cfg"], npl, xb, rows=rows)
+    out, idx, w, logits, _ = run_hip(layer, x, accum=accum)
+    got_idx = idx.cpu().numpy().astype(np.int64)
+    assert np.array_equal(got_idx, ref["idx"]), f"{label}: indices differ\n{got_idx}\n{ref['idx']}"
+    got_w = w.cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(got_w, ref["w"], rtol=W_RTOL, atol=0, err_msg=label)
+    got_z = logits.cpu().numpy().astype(np.float64)
+    zscale = np.abs(ref["z"]).max()
+    assert np.abs(got_z - ref["z"]).max() <= 1e-5 * max(1.0, zscale), label
+    o = bf16_to_f64(bits(out))
+    assert np.isfinite(o).all(), f"{label}: non-finite output (unwritten rows?)"
+    sel = ref["rows"]
+    err = rel_l2_per_token(o[:, sel], ref["y"])
+    assert err.max() <= OUT_RTOL, f"{label}: rel L2 {err}"
+    return {"rel_l2": float(err.max()), "out": out}

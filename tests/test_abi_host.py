@@ -1,0 +1,197 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+header declares, and refuses bad calls by name before enqueueing anything.
+No GPU: moe_validate and moe_workspace_bytes never touch device memory."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_35_amd as moe
+from mixture_experts_layer_35_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "moe_mi355x.h")
+
+FAKE = 0x7f0000000000  # never dereferenced: validation only reads sizes and alignment
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_symbols_exported():
+    lib = moe.lib()
+    names = _declared()
+    assert set(names) == set(B.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version():
+    assert moe.abi_version() == 1
+
+
+def _fake_weight(fmt, rows, cols, count, base):
+    w = B.MoeWeight()
+    w.format = B.FORMAT[fmt]
+    w.rows, w.cols, w.count = rows, cols, count
+    w.data = base
+    if fmt == "bf16":
+        w.data_bytes = count * rows * cols * 2
+    elif fmt == "fp8_rowscale":
+        w.data_bytes = count * rows * cols
+        w.scales, w.scale_bytes = base + (1 << 36), count * rows * 4
+    elif fmt == "mxfp4":
+        w.data_bytes = count * rows * cols // 2
+        w.scales, w.scale_bytes = base + (1 << 36), count * rows * cols // 32
+    else:
+        w.data_bytes = count * rows * cols // 2
+        w.scales, w.scale_bytes = base + (1 << 36), count * rows * cols // 16
+        w.tensor_scale = base + (1 << 37)
+    return w
+
+
+def _fake_set(fmt, H, inter, count, base):
+    s = B.MoeExperts()
+    s.gate = _fake_weight(fmt, inter, H, count, base)
+    s.up = _fake_weight(fmt, inter, H, count, base + (1 << 32))
+    s.down = _fake_weight(fmt, H, inter, count, base + (2 << 32))
+    return s
+
+
+def _c3():
+    cfg = dict(H=7168, I=2048, E=256, k=8, I_s=2048, scoring="sigmoid", renorm=True, rsf=2.5)
+    c = B.make_cfg(cfg, accum="atomic")
+    r = B.MoeRouter(FAKE, FAKE + 4096)
+    ex = _fake_set("nvfp4", 7168, 2048, 256, FAKE)
+    sh = _fake_set("bf16", 7168, 2048, 1, FAKE + (8 << 32))
+    return c, r, ex, sh
+
+
+def test_valid_call_passes_validation():
+    c, r, ex, sh = _c3()
+    ws = B.workspace_bytes(c, 4)
+    assert B.validate(c, r, ex, sh, 4, ws) == B.MOE_OK
+    assert B.num_launches(c, 4) == 5
+
+
+def test_workspace_too_small_names_need_and_have():
+    c, r, ex, sh = _c3()
+    ws = B.workspace_bytes(c, 4)
+    assert B.validate(c, r, ex, sh, 4, ws - 1) == B.MOE_ERR_WORKSPACE
+    msg = B.last_error()
+    assert f"need {ws} bytes" in msg and f"have {ws - 1}" in msg
+
+
+def test_workspace_grows_with_tokens():
+    c, *_ = _c3()
+    assert B.workspace_bytes(c, 1) < B.workspace_bytes(c, 4)
+
+
+def test_scale_byte_count_mismatch_refused():
+    # the GS16-kernel-on-GS32-buffer class: a scale buffer sized for a
+    # different group size is refused before anything runs
+    c, r, ex, sh = _c3()
+    ex.gate.scale_bytes = 256 * 2048 * 7168 // 32
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
+    assert "scales" in B.last_error()
+
+
+def test_data_byte_count_mismatch_refused():
+    c, r, ex, sh = _c3()
+    ex.down.data_bytes += 16
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
+
+
+def test_misaligned_and_null_refused():
+    c, r, ex, sh = _c3()
+    ex.up.data = FAKE + 8
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
+    c, r, ex, sh = _c3()
+    ex.up.data = None
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
+    c, r, ex, sh = _c3()
+    r.weight = None
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
+
+
+def test_missing_tensor_scale_refused():
+    c, r, ex, sh = _c3()
+    ex.gate.tensor_scale = None
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
+
+
+def test_shape_mismatch_refused():
+    c, r, ex, sh = _c3()
+    ex.down = _fake_weight("nvfp4", 2048, 7168, 256, FAKE)   # transposed
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
+
+
+def test_group_size_divisibility_refused():
+    cfg = dict(H=2048 + 16, I=768, E=8, k=2, I_s=0, scoring="softmax", renorm=True, rsf=1.0)
+    c = B.make_cfg(cfg, accum="slot")
+    ex = _fake_set("mxfp4", 2048 + 16, 768, 8, FAKE)
+    st = B.validate(c, B.MoeRouter(FAKE, None), ex, None, 1, 1 << 40)
+    assert st == B.MOE_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("field,val", [("top_k", 0), ("top_k", 17), ("num_experts", 257),
+                                       ("hidden", 0), ("scoring", 5), ("accum_mode", 9),
+                                       ("norm_topk_prob", 2)])
+def test_bad_cfg_refused(field, val):
+    c, r, ex, sh = _c3()
+    setattr(c, field, val)
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) != B.MOE_OK
+
+
+def test_topk_above_num_experts_refused():
+    c, r, ex, sh = _c3()
+    c.num_experts, c.top_k = 4, 8
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("n", [0, -1, 5000])
+def test_token_count_range(n):
+    c, r, ex, sh = _c3()
+    assert B.validate(c, r, ex, sh, n, 1 << 40) != B.MOE_OK
+
+
+def test_decode_token_limit_and_grouped_not_built():
+    c, r, ex, sh = _c3()
+    c.path = B.PATH["decode"]
+    assert B.validate(c, r, ex, sh, 5, 1 << 40) == B.MOE_ERR_UNSUPPORTED
+    c.path = B.PATH["auto"]
+    assert B.validate(c, r, ex, sh, 16, 1 << 40) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_shared_presence_must_match_cfg():
+    c, r, ex, sh = _c3()
+    assert B.validate(c, r, ex, None, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
+    c.shared_inter = 0
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
+
+
+def test_shared_format_must_be_bf16_or_routed():
+    c, r, ex, sh = _c3()
+    sh = _fake_set("mxfp4", 7168, 2048, 1, FAKE)
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_mixed_formats_within_set_refused():
+    c, r, ex, sh = _c3()
+    ex.down = _fake_weight("mxfp4", 7168, 2048, 256, FAKE)
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_softmax_with_bias_refused():
+    c, r, ex, sh = _c3()
+    c.scoring = B.SCORING["softmax"]
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_status_strings():
+    assert moe.status_str(0) == "MOE_OK"
+    assert moe.status_str(3) == "MOE_ERR_WORKSPACE"
