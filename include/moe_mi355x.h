@@ -140,9 +140,9 @@ typedef struct {
   float* logits;  /* [N, E] router logits (FP32) */
 } moe_topk_out;
 
-/* Optional timing hook: when non-NULL, events[i] is recorded on the stream
- * right before launch i of the call and events[num_launches] after the last
- * one. count must be >= num_launches + 1 (moe_num_launches gives the
+/* Optional timing hook: when non-NULL, events[0] is recorded on the stream
+ * right before the call's first launch and events[num_launches] after its
+ * last one; count must be >= num_launches + 1 (moe_num_launches gives the
  * number). The events must be created by the caller. */
 typedef struct {
   void** events; /* hipEvent_t[count] */
@@ -166,9 +166,13 @@ int32_t moe_num_launches(const moe_cfg* cfg, int32_t n_tokens);
 /* The layer forward. x: device BF16 [n_tokens, H]; out: device BF16
  * [n_tokens, H] (every element is written); shared: NULL iff
  * cfg->shared_inter == 0; topk, trace: optional. workspace: device, 256-byte
- * aligned, at least moe_workspace_bytes(cfg, n_tokens) bytes; its first 256
- * bytes must be zero before the first call that uses it (every call leaves
- * them zero). stream: hipStream_t (NULL = default stream). */
+ * aligned, at least moe_workspace_bytes(cfg, n_tokens) bytes, zero-filled
+ * before the first call that uses it. Its head holds per-call counters (and,
+ * in ATOMIC_F32 mode, the accumulator) that every call returns to zero, so a
+ * workspace sized for max_tokens serves any later call with the same cfg and
+ * n_tokens <= max_tokens. Bytes 128..131 are a sticky device error word: non-zero
+ * if a workgroup's bounded wait for another expired (results of that call are
+ * then not valid). stream: hipStream_t (NULL = default stream). */
 moe_status moe_forward(const moe_cfg* cfg, const moe_router* router,
                        const moe_experts* experts, const moe_experts* shared,
                        const void* x, int32_t n_tokens, void* out,

@@ -198,29 +198,44 @@ class Layer:
         self.max_tokens = max_tokens
         nbytes = workspace_bytes(self.cfg, max_tokens)
         dev = layer["router"]["weight"].device
-        # zero-filled once: the first 256 bytes must start at zero
+        # zero-filled once: the counter head must start at zero (calls keep it so)
         self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
 
-    def forward(self, x, out=None, idx=None, weights=None, logits=None, stream=None,
-                events=None):
+    def prepare(self, x, out, idx=None, weights=None, logits=None, stream=None, events=None):
+        """Marshal one call's arguments once; returns a no-argument callable
+        that enqueues the call (raises MoeError on a refused call)."""
         import torch
         n = x.shape[0]
-        if out is None:
-            out = torch.empty_like(x)
         topk = None
         if idx is not None or weights is not None or logits is not None:
             topk = MoeTopkOut(_ptr(idx), _ptr(weights), _ptr(logits))
         trace = None
+        keep = []
         if events is not None:
-            arr = (ctypes.c_void_p * len(events))(*[int(e.cuda_event) if hasattr(e, "cuda_event")
-                                                    else int(e) for e in events])
+            arr = (ctypes.c_void_p * len(events))(*[int(e) for e in events])
+            keep.append(arr)
             trace = MoeTrace(ctypes.cast(arr, ctypes.c_void_p), len(events))
         if stream is None:
             stream = torch.cuda.current_stream(x.device).cuda_stream
-        st = lib().moe_forward(ctypes.byref(self.cfg), ctypes.byref(self.router),
-                               _ref(self.experts), _ref(self.shared), x.data_ptr(), int(n),
-                               out.data_ptr(), _ref(topk), self.workspace.data_ptr(),
-                               self.workspace.numel(), ctypes.c_void_p(stream), _ref(trace))
-        if st != MOE_OK:
-            raise MoeError(st, last_error())
+        args = (ctypes.byref(self.cfg), ctypes.byref(self.router), _ref(self.experts),
+                _ref(self.shared), ctypes.c_void_p(x.data_ptr()), ctypes.c_int32(n),
+                ctypes.c_void_p(out.data_ptr()), _ref(topk),
+                ctypes.c_void_p(self.workspace.data_ptr()),
+                ctypes.c_size_t(self.workspace.numel()), ctypes.c_void_p(stream), _ref(trace))
+        fn = lib().moe_forward
+        keep += [topk, trace, x, out, idx, weights, logits]
+
+        def call():
+            st = fn(*args)
+            if st != MOE_OK:
+                raise MoeError(st, last_error())
+            return keep
+        return call
+
+    def forward(self, x, out=None, idx=None, weights=None, logits=None, stream=None,
+                events=None):
+        import torch
+        if out is None:
+            out = torch.empty_like(x)
+        self.prepare(x, out, idx, weights, logits, stream, events)()
         return out

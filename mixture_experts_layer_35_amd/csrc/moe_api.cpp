@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <cmath>
+#include <cstddef>
 
 #include "../../include/moe_mi355x.h"
 #include "moe_internal.h"
@@ -165,33 +166,57 @@ moe_status resolve_path(const moe_cfg* c, int32_t n, int* path) {
   return MOE_OK;
 }
 
-// Workspace layout for the decode path (offsets from the base, 256-aligned).
-moe::Workspace layout(const moe_cfg* c, int32_t n, char* base) {
-  moe::Workspace w;
+// Workspace layout of the decode path. The head (counters and, in atomic mode,
+// the FP32 accumulator) has a fixed size for a given cfg and must be zero at
+// rest; every call leaves it zero. The per-call buffers after it depend on N.
+struct Layout {
+  size_t head_bytes = 0;
+  size_t total = 0;
+  size_t unit_done = 0, blend_ctr = 0, acc = 0;
+  size_t a_routed = 0, a_shared = 0, dbuf = 0;
+};
+
+Layout layout(const moe_cfg* c, int32_t n) {
+  Layout L;
   const size_t N = n, E = c->num_experts, k = c->top_k, H = c->hidden, I = c->inter,
                Is = c->shared_inter;
-  const size_t maxu = (N * k < E) ? N * k : E;
-  size_t off = 256;  // counters
+  size_t off = sizeof(moe::Ctl);
   auto take = [&](size_t bytes) {
     size_t o = off;
     off = align_up(off + bytes, 256);
-    return base ? base + o : nullptr;
+    return o;
   };
-  w.logits = (float*)take(N * E * 4);
-  w.idx = (uint32_t*)take(N * k * 4);
-  w.wts = (float*)take(N * k * 4);
-  w.num_units = (int32_t*)take(16);
-  w.unit_expert = (int32_t*)take(maxu * 4);
-  w.unit_slot = (int32_t*)take(maxu * moe::kNmax * 4);
-  w.unit_w = (float*)take(maxu * moe::kNmax * 4);
-  w.a_routed = (uint16_t*)take(N * k * I * 2);
-  w.a_shared = (uint16_t*)take(N * (Is ? Is : 1) * 2);
-  if (c->accum_mode == MOE_ACCUM_ATOMIC_F32)
-    w.acc = (float*)take(N * H * 4);
-  else
-    w.dbuf = (float*)take((N * k + N) * H * 4);
-  w.total = off;
-  return w;
+  L.unit_done = take((MOE_MAX_EXPERTS + 1) * moe::kLineWords * 4);
+  L.blend_ctr = take((H + 3) / 4 * moe::kLineWords * 4);
+  if (c->accum_mode == MOE_ACCUM_ATOMIC_F32) L.acc = take((size_t)moe::kNmax * H * 4);
+  L.head_bytes = off;
+  L.a_routed = take(N * k * I * 8);
+  L.a_shared = take(N * (Is ? Is : 1) * 8);
+  if (c->accum_mode != MOE_ACCUM_ATOMIC_F32) L.dbuf = take((N * k + N) * H * 8);
+  L.total = off;
+  return L;
+}
+
+// Gate+up geometry: a workgroup stages x once (tokens * H BF16 into LDS) and
+// then streams `sub` row blocks, enough that the staged bytes stay under a
+// quarter of the weight bytes, while keeping about two workgroups per compute
+// unit.
+moe::StageGeom gate_up_geom(int fmt, int H, int rows, int rpl, int tokens, int units) {
+  int64_t db, sb;
+  expected_bytes(fmt, 1, H, &db, &sb);
+  const int64_t row_bytes = db + sb;
+  const moe::StageGeom one = moe::stage_geom(fmt, H, rows, rpl, 1);
+  const int64_t block_bytes = (int64_t)one.rows_per_wg * 2 * row_bytes;
+  const int64_t staged = (int64_t)tokens * H * 2;
+  int sub = (int)((4 * staged + block_bytes - 1) / block_bytes);
+  sub = sub < 1 ? 1 : (sub > 8 ? 8 : sub);
+  // at most 64 workgroups report to one expert's done counter
+  while (sub < 16 && (rows + one.rows_per_wg * sub - 1) / (one.rows_per_wg * sub) > 64) ++sub;
+  while (sub > 1 &&
+         (int64_t)units * ((rows + one.rows_per_wg * sub - 1) / (one.rows_per_wg * sub)) < 512 &&
+         (rows + one.rows_per_wg * (sub - 1) - 1) / (one.rows_per_wg * (sub - 1)) <= 64)
+    --sub;
+  return moe::stage_geom(fmt, H, rows, rpl, sub);
 }
 
 moe::DevProj to_dev(const moe_weight& w) {
@@ -234,7 +259,7 @@ size_t moe_workspace_bytes(const moe_cfg* cfg, int32_t max_tokens) {
   if (check_cfg(cfg)) return 0;
   int path;
   if (resolve_path(cfg, max_tokens, &path)) return 0;
-  return layout(cfg, max_tokens, nullptr).total;
+  return layout(cfg, max_tokens).total;
 }
 
 moe_status moe_validate(const moe_cfg* cfg, const moe_router* router, const moe_experts* experts,
@@ -267,7 +292,7 @@ moe_status moe_validate(const moe_cfg* cfg, const moe_router* router, const moe_
   } else if (shared) {
     return fail(MOE_ERR_INVALID_ARG, "shared is given but shared_inter == 0");
   }
-  const size_t need = layout(cfg, n_tokens, nullptr).total;
+  const size_t need = layout(cfg, n_tokens).total;
   if (workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace too small: need %zu bytes, have %zu", need,
                 workspace_bytes);
@@ -278,7 +303,7 @@ int32_t moe_num_launches(const moe_cfg* cfg, int32_t n_tokens) {
   if (check_cfg(cfg)) return -1;
   int path;
   if (resolve_path(cfg, n_tokens, &path)) return -1;
-  return moe::decode_num_launches();
+  return 1;
 }
 
 moe_status moe_forward(const moe_cfg* cfg, const moe_router* router, const moe_experts* experts,
@@ -297,60 +322,75 @@ moe_status moe_forward(const moe_cfg* cfg, const moe_router* router, const moe_e
         (topk->logits && !aligned(topk->logits, 4)))
       return fail(MOE_ERR_INVALID_ARG, "top-k outputs must be 4-byte aligned");
   }
-  const int launches = moe::decode_num_launches();
-  if (trace && (!trace->events || trace->count < launches + 1))
-    return fail(MOE_ERR_INVALID_ARG, "trace needs %d events", launches + 1);
+  if (trace && (!trace->events || trace->count < 2))
+    return fail(MOE_ERR_INVALID_ARG, "trace needs 2 events");
 
-  moe::Call c;
-  c.N = n_tokens;
-  c.H = cfg->hidden;
-  c.I = cfg->inter;
-  c.E = cfg->num_experts;
-  c.k = cfg->top_k;
-  c.I_s = cfg->shared_inter;
-  c.scoring = cfg->scoring;
-  c.renorm = cfg->norm_topk_prob;
-  c.atomic = cfg->accum_mode == MOE_ACCUM_ATOMIC_F32;
-  c.rsf = cfg->routed_scaling_factor;
-  c.maxu = (c.N * c.k < c.E) ? c.N * c.k : c.E;
-  c.x = static_cast<const uint16_t*>(x);
-  c.out = static_cast<uint16_t*>(out);
-  c.router_w = static_cast<const uint16_t*>(router->weight);
-  c.router_bias = router->bias;
-  c.gate = to_dev(experts->gate);
-  c.up = to_dev(experts->up);
-  c.down = to_dev(experts->down);
-  if (c.I_s > 0) {
-    c.sgate = to_dev(shared->gate);
-    c.sup = to_dev(shared->up);
-    c.sdown = to_dev(shared->down);
-  } else {
-    c.sgate.fmt = c.sup.fmt = c.sdown.fmt = moe::FMT_NONE_HOST;
+  moe::DecodeArgs a{};
+  a.N = n_tokens;
+  a.H = cfg->hidden;
+  a.I = cfg->inter;
+  a.E = cfg->num_experts;
+  a.k = cfg->top_k;
+  a.I_s = cfg->shared_inter;
+  a.scoring = cfg->scoring;
+  a.renorm = cfg->norm_topk_prob;
+  a.atomic = cfg->accum_mode == MOE_ACCUM_ATOMIC_F32;
+  a.rsf = cfg->routed_scaling_factor;
+  a.maxu = (a.N * a.k < a.E) ? a.N * a.k : a.E;
+  a.x = static_cast<const uint16_t*>(x);
+  a.out = static_cast<uint16_t*>(out);
+  a.router_w = static_cast<const uint16_t*>(router->weight);
+  a.router_bias = router->bias;
+  a.gate = to_dev(experts->gate);
+  a.up = to_dev(experts->up);
+  a.down = to_dev(experts->down);
+  const int fr = experts->gate.format;
+  int fs = moe::FMT_NONE_HOST;
+  if (a.I_s > 0) {
+    a.sgate = to_dev(shared->gate);
+    a.sup = to_dev(shared->up);
+    a.sdown = to_dev(shared->down);
+    fs = shared->gate.format;
   }
-  c.gu_r = moe::plan_stage(c.gate.fmt, c.H, c.I, c.maxu, true);
-  c.dn_r = moe::plan_stage(c.down.fmt, c.I, c.H, c.maxu, false);
-  if (c.I_s > 0) {
-    c.gu_s = moe::plan_stage(c.sgate.fmt, c.H, c.I_s, 1, true);
-    c.dn_s = moe::plan_stage(c.sdown.fmt, c.I_s, c.H, 1, false);
-  } else {
-    c.gu_s.tiles = 0;
-    c.dn_s.tiles = 0;
+  // two rows per lane group when the routed gate+up grid still gives at
+  // least two workgroups per compute unit
+  const moe::StageGeom g2 = moe::stage_geom(fr, a.H, a.I, 2, 1);
+  const int rpl = ((long)a.maxu * g2.tiles >= 512) ? 2 : 1;
+  a.gr = gate_up_geom(fr, a.H, a.I, rpl, 1, a.maxu);
+  a.dr = moe::stage_geom(fr, a.I, a.H, rpl, 1);
+  if (a.I_s > 0) {
+    a.gs = gate_up_geom(fs, a.H, a.I_s, rpl, a.N, 1);
+    a.ds = moe::stage_geom(fs, a.I_s, a.H, rpl, 1);
   }
-  // the shared unit shares the row-per-lane choice of its kernel launch
-  c.gu_s.rpl = c.gu_r.rpl;
-  c.gu_s.rows_per_wg = (moe::kThreads / 64) * (64 / c.gu_s.lpr) * c.gu_s.rpl;
-  if (c.I_s > 0) c.gu_s.tiles = (c.I_s + c.gu_s.rows_per_wg - 1) / c.gu_s.rows_per_wg;
-  c.dn_s.rpl = c.dn_r.rpl;
-  c.dn_s.rows_per_wg = (moe::kThreads / 64) * (64 / c.dn_s.lpr) * c.dn_s.rpl;
-  if (c.I_s > 0) c.dn_s.tiles = (c.H + c.dn_s.rows_per_wg - 1) / c.dn_s.rows_per_wg;
-  c.ws = layout(cfg, n_tokens, static_cast<char*>(workspace));
+  a.nR = (a.E + 3) / 4;
+  a.nGs = a.I_s > 0 ? a.gs.tiles : 0;
+  a.nGr = a.maxu * a.gr.tiles;
+  a.nDs = a.I_s > 0 ? a.ds.tiles : 0;
+  a.nDr = a.maxu * a.dr.tiles;
+  a.blend_rows = a.dr.rows_per_wg;
+  if (a.I_s > 0 && a.ds.rows_per_wg > a.blend_rows) a.blend_rows = a.ds.rows_per_wg;
+  a.spin_limit = 1u << 22;
+
+  char* base = static_cast<char*>(workspace);
+  const Layout L = layout(cfg, n_tokens);
+  a.ctl = reinterpret_cast<moe::Ctl*>(base);
+  a.unit_done = reinterpret_cast<unsigned*>(base + L.unit_done);
+  a.blend_ctr = reinterpret_cast<unsigned*>(base + L.blend_ctr);
+  a.acc = a.atomic ? reinterpret_cast<float*>(base + L.acc) : nullptr;
+  a.a_routed = reinterpret_cast<unsigned long long*>(base + L.a_routed);
+  a.a_shared = reinterpret_cast<unsigned long long*>(base + L.a_shared);
+  a.dbuf = a.atomic ? nullptr : reinterpret_cast<unsigned long long*>(base + L.dbuf);
   if (topk) {
-    c.out_idx = topk->idx;
-    c.out_w = topk->weights;
-    c.out_logits = topk->logits;
+    a.out_idx = topk->idx;
+    a.out_w = topk->weights;
+    a.out_logits = topk->logits;
   }
+  const size_t lds = moe::decode_lds_bytes(a.H, a.I, a.I_s);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
   hipEvent_t* ev = trace ? reinterpret_cast<hipEvent_t*>(trace->events) : nullptr;
-  hipError_t err = moe::launch_decode(c, static_cast<hipStream_t>(stream), ev);
+  if (ev) hipEventRecord(ev[0], hs);
+  hipError_t err = moe::launch_decode(a, fr, fs, rpl, lds, hs);
+  if (ev) hipEventRecord(ev[1], hs);
   if (err != hipSuccess)
     return fail(MOE_ERR_HIP, "launch failed: %s", hipGetErrorString(err));
   return MOE_OK;

@@ -1,5 +1,5 @@
 // Internal interface between the host entry points (moe_api.cpp) and the
-// kernel launchers (moe_kernels.hip). Not part of the public ABI.
+// kernel launcher (moe_kernels.hip). Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -7,6 +7,10 @@
 #include <stdint.h>
 
 namespace moe {
+
+constexpr int kNmax = 4;          // tokens per call on the decode path
+constexpr int kThreads = 256;     // threads per workgroup (4 waves)
+constexpr int FMT_NONE_HOST = 7;  // no shared expert (same value as FMT_NONE)
 
 // One projection for all experts of a set, in the canonical layout.
 struct DevProj {
@@ -20,59 +24,79 @@ struct DevProj {
   int32_t rows = 0, cols = 0, fmt = 0;
 };
 
-// Per-call device pointers carved out of the workspace.
-struct Workspace {
-  float* logits = nullptr;      // [N, E]
-  uint32_t* idx = nullptr;      // [N, k]
-  float* wts = nullptr;         // [N, k]
-  int32_t* num_units = nullptr; // [1]
-  int32_t* unit_expert = nullptr;  // [maxu]
-  int32_t* unit_slot = nullptr;    // [maxu, NMAX] slot t*k+j or -1
-  float* unit_w = nullptr;         // [maxu, NMAX]
-  uint16_t* a_routed = nullptr;    // [N*k, I] BF16
-  uint16_t* a_shared = nullptr;    // [N, I_s] BF16
-  float* dbuf = nullptr;           // [N*k + N, H] FP32 (slot mode)
-  float* acc = nullptr;            // [N, H] FP32 (atomic mode)
-  size_t total = 0;
+// Per-call state at the start of the workspace. It starts zero-filled; the
+// counters are zero again after every call, and the tagged words (logits,
+// plan) carry the call's tag, so they never need clearing. Counters sit on
+// their own 128-byte lines so pollers and atomics do not pile onto one line.
+constexpr int kLineWords = 32;    // 128 bytes
+constexpr int kDoneGroups = 64;   // workgroup i reports to done group i % 64
+constexpr int kPlanStride = 16;   // 64-bit plan words per unit (one line)
+struct Ctl {
+  unsigned done;   // done groups finished
+  unsigned pad0[kLineWords - 1];
+  unsigned error;  // sticky: 1 plan wait, 2 activation wait, 4 logits wait, 8 blend wait expired
+  unsigned pad1[kLineWords - 1];
+  unsigned epoch;  // calls completed on this workspace; the call's tag is epoch + 1
+  unsigned pad2[kLineWords - 1];
+  unsigned group_done[kDoneGroups * kLineWords];  // per done group, one line each
+  // router logits, tagged; token t, expert e at t * 256 + e
+  unsigned long long zlog[kNmax * 256];
+  // the plan: unit u, token t: words u * kPlanStride + 2t (info) and + 2t + 1
+  // (routing weight), both tagged
+  unsigned long long plan[256 * kPlanStride];
 };
+// the error word is bytes 128..131
+static_assert(sizeof(Ctl) == 384 + kDoneGroups * 128 + kNmax * 256 * 8 + 256 * kPlanStride * 8,
+              "Ctl layout");
 
-constexpr int kNmax = 4;      // tokens per call on the decode path
-constexpr int FMT_NONE_HOST = 7;  // no shared expert (same value as FMT_NONE)
-constexpr int kThreads = 256; // threads per workgroup (4 waves)
+// Plan info word (high half of the tagged word):
+constexpr unsigned kPlanAbsent = 1u << 30;  // unit index >= number of distinct experts
+constexpr unsigned kPlanPresent = 1u << 8;  // the token routes to this unit
+// expert id in bits 16..23, top-k position j in bits 0..4
 
 struct StageGeom {
   int lpr = 64;          // lanes per row (power of two, 8..64)
   int rpl = 1;           // rows per lane group
+  int sub = 1;           // row blocks per workgroup (one activation staging)
   int rows_per_wg = 4;   // rows (gate/up: row pairs) per workgroup
   int tiles = 0;         // workgroups per unit
 };
 
-struct Call {
-  int N = 0, H = 0, I = 0, E = 0, k = 0, I_s = 0;
-  int scoring = 0, renorm = 1, atomic = 0;
-  float rsf = 1.f;
-  int maxu = 0;  // max distinct experts: min(E, N*k)
-  const uint16_t* x = nullptr;
-  uint16_t* out = nullptr;
-  const uint16_t* router_w = nullptr;
-  const float* router_bias = nullptr;
-  DevProj gate, up, down;
-  DevProj sgate, sup, sdown;  // fmt FMT_NONE (7) when absent
-  StageGeom gu_r, gu_s, dn_r, dn_s;
-  Workspace ws;
-  uint32_t* out_idx = nullptr;
-  float* out_w = nullptr;
-  float* out_logits = nullptr;
+struct DecodeArgs {
+  // inputs
+  const uint16_t* x;
+  const uint16_t* router_w;
+  const float* router_bias;
+  DevProj gate, up, down, sgate, sup, sdown;
+  int N, H, I, E, k, I_s, scoring, renorm, atomic, maxu;
+  float rsf;
+  // phases (workgroup id ranges, in this order): router, shared gate+up,
+  // routed gate+up, shared down, routed down
+  int nR, nGs, nGr, nDs, nDr;
+  StageGeom gr, gs, dr, ds;
+  int blend_rows;  // output rows per blend block
+  unsigned spin_limit;
+  // workspace
+  Ctl* ctl;
+  unsigned* unit_done;  // [(maxu + 1) * kLineWords]; entry maxu is the shared expert
+  unsigned* blend_ctr;  // [ceil(H / blend_rows) * kLineWords]
+  unsigned long long* a_routed;  // [N*k, I] tagged FP32 SiLU(gate)*up
+  unsigned long long* a_shared;  // [N, I_s] tagged FP32
+  unsigned long long* dbuf;      // slot mode [N*k + N, H] tagged FP32 w*down
+  float* acc;                    // atomic mode [N, H], zero at rest
+  // outputs
+  uint16_t* out;
+  uint32_t* out_idx;
+  float* out_w;
+  float* out_logits;
 };
 
-// Lanes per row and rows per workgroup for a (format, cols, rows) stream.
-StageGeom plan_stage(int fmt, int cols, int rows, int units, bool two_mats);
+int lanes_per_row(int fmt, int cols);
+StageGeom stage_geom(int fmt, int cols, int rows, int rpl, int sub);
+size_t decode_lds_bytes(int H, int I, int I_s);
 
-// Number of launches of the decode path.
-int decode_num_launches();
-
-// Enqueue the decode path. events (optional) are recorded before each launch
-// and after the last. Returns hipSuccess or the first launch error.
-hipError_t launch_decode(const Call& c, hipStream_t stream, hipEvent_t* events);
+// Enqueue the fused decode kernel (formats: routed fr, shared fs or FMT_NONE).
+hipError_t launch_decode(const DecodeArgs& a, int fr, int fs, int rpl, size_t lds,
+                         hipStream_t stream);
 
 }  // namespace moe

@@ -1,27 +1,46 @@
-// gfx950 kernels of the routed MoE layer forward, decode path (N <= 4).
+// gfx950 kernel of the routed MoE layer forward, decode path (N <= 4).
 //
-// Five launches, in stream order:
-//   1. k_router     z[N,E] = x Wr^T. One wave per router row; the row is read
-//                   once for all N tokens (the batched router GEMV of
-//                   "forward_k3.rs", MoeLayer::forward_k3, step 1).
-//   2. k_topk_plan  one wave per token: top-k over E <= 256 scores, lowest
-//                   index first on ties; softmax or sigmoid+bias weights,
-//                   renorm, routed scaling factor ("forward_k3.rs" step 2).
-//                   Then the batch's distinct experts ("units") are listed in
-//                   ascending expert order with, per token, the slot t*k+j
-//                   that routed to them, so every expert is streamed once.
-//   3. k_gate_up    one workgroup per (unit, row tile): g = Wg x, u = Wu x for
-//                   the unit's tokens (x staged in LDS), a = silu(g) * u.
-//                   The shared expert runs as one more unit with all tokens.
-//   4. k_down       one workgroup per (unit, row tile): d = Wd a for the
-//                   unit's tokens (a staged in LDS); either stores w*d per slot
-//                   (slot mode) or atomically adds w*d into an FP32 [N,H]
-//                   accumulator ("forward_atomic_c4.rs").
-//   5. k_blend / k_finalize  y = sum_j w*d + shared, cast to BF16 (RNE).
+// One launch runs the whole layer. Its workgroups fall into phases by id, and
+// a workgroup only ever waits for work of lower ids, so every wait ends:
+// workgroups are dispatched in id order, and producers never wait for their
+// consumers. Every wait is also bounded; on expiry a sticky error word is set
+// instead of hanging.
+//
+//   R   router  z[N,E] = x Wr^T, one wave per router row, the row read once
+//               for all N tokens ("forward_k3.rs", MoeLayer::forward_k3,
+//               step 1). The last router workgroup runs top-k for every token
+//               (one wave per token, a (score, -index) argmax per round with
+//               DPP reductions; softmax or sigmoid+bias weights, renorm,
+//               routed scaling factor: step 2), lists the batch's distinct
+//               experts ("units") in ascending expert order and publishes,
+//               per (unit, token), the top-k position and routing weight.
+//   GU  gate+up one workgroup per (unit, row tile): g = Wg x and u = Wu x for
+//               the unit's tokens (x staged in LDS); a = silu(g) * u. The
+//               shared expert is one more unit that takes every token and
+//               needs no plan, so it streams while the router runs.
+//   D   down    one workgroup per (unit, row tile): loads its weights first,
+//               then waits for the unit's activations, d = Wd a. Slot mode
+//               stores w*d per (slot, row); atomic mode adds w*d into an FP32
+//               [N,H] accumulator ("forward_atomic_c4.rs"). The last
+//               contributor to a block of output rows sums it (slot mode: in
+//               slot order, then the shared expert) and writes BF16 (round
+//               to nearest even).
+//
+// Hand-offs between workgroups. The 8 XCDs have separate L2 caches and an
+// agent-scope fence writes back or invalidates a whole L2, so there are no
+// fences: a word handed to another workgroup is written and read with
+// relaxed agent-scope atomics (coherent per access, sc1). Data words are
+// 64-bit, value in the high half and the call's tag in the low half; a reader
+// accepts a word only with the current tag, so nothing has to be cleared
+// between calls and a producer never waits for its stores to complete. Per
+// unit and per row-block counters only say when to start reading. The tag is
+// the workspace's call counter plus one; the last workgroup to finish bumps
+// the counter and clears the counters.
 //
 // Weights are read with 128-bit loads, `lpr` lanes per row, and dequantised
 // in registers: FP4/FP8 pairs go to BF16 pairs with the gfx950 scaled
-// converts, then into v_dot2_f32_bf16 against BF16 activations, FP32
+// converts, then into v_dot2_f32_bf16 against BF16 activations; block scales
+// multiply per-chunk partial sums, row and tensor scales the row result; FP32
 // accumulation throughout.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -31,24 +50,168 @@
 
 namespace moe {
 
-constexpr int IT = 4;  // 16-byte chunks per lane per row held in flight
+constexpr int IT = 4;  // 16-byte chunks per lane per row in flight per pass
+constexpr int SB = 4;  // staging loads in flight per thread
+
+typedef unsigned long long u64;
+
+// ---------------------------------------------------------------------------
+// Coherent (agent-scope relaxed atomic) loads and stores, tagged words.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned ld_coh(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coh(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u64 ld_coh64(const u64* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh64(u64* p, u64 v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u64 tagged(float v, unsigned tag) {
+  return ((u64)__builtin_bit_cast(unsigned, v) << 32) | tag;
+}
+__device__ __forceinline__ u64 tagged_u(unsigned v, unsigned tag) { return ((u64)v << 32) | tag; }
+__device__ __forceinline__ float tag_value(u64 w) {
+  return __builtin_bit_cast(float, (unsigned)(w >> 32));
+}
+
+__device__ __forceinline__ void set_error(const DecodeArgs& a, unsigned code) {
+  __hip_atomic_fetch_or(&a.ctl->error, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Thread 0 spins until *p >= target (bounded), then the workgroup proceeds.
+__device__ __forceinline__ void wg_wait_geq(const DecodeArgs& a, const unsigned* p,
+                                            unsigned target, unsigned code) {
+  if (threadIdx.x == 0) {
+    unsigned spins = 0;
+    while (ld_coh(p) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > a.spin_limit) {
+        set_error(a, code);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Add 1 to *p once every wave of the workgroup got here; returns the old
+// value to every thread. With `complete`, this thread's memory operations
+// finish first (needed where the reader does not check tags).
+__device__ __forceinline__ unsigned wg_signal(unsigned* p, unsigned* s_tmp, bool complete) {
+  if (complete) __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *s_tmp = __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  return *s_tmp;
+}
+
+// Add 1 to *p once every wave of the workgroup got here, without waiting for
+// the atomic to return.
+__device__ __forceinline__ void wg_signal_noret(unsigned* p) {
+  __syncthreads();
+  if (threadIdx.x == 0)
+    (void)__hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// DPP reductions.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               ROW_MASK, 0xf, false));
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f32<0x111, 0xf>(v);
+  v += dpp_f32<0x112, 0xf>(v);
+  v += dpp_f32<0x114, 0xf>(v);
+  v += dpp_f32<0x118, 0xf>(v);
+  v += dpp_f32<0x142, 0xa>(v);
+  v += dpp_f32<0x143, 0xc>(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Sum over aligned groups of `width` lanes (8..64); the sum lands in the last
+// lane of each group.
+__device__ __forceinline__ float group_sum_last(float v, int width) {
+  v += dpp_f32<0x111, 0xf>(v);
+  v += dpp_f32<0x112, 0xf>(v);
+  v += dpp_f32<0x114, 0xf>(v);
+  if (width >= 16) v += dpp_f32<0x118, 0xf>(v);
+  if (width >= 32) v += dpp_f32<0x142, 0xa>(v);
+  if (width >= 64) v += dpp_f32<0x143, 0xc>(v);
+  return v;
+}
+
+// max over finite-or--inf floats via their ordered integer images
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  const uint32_t m = wave_max_u32(ordered_bits(v));
+  const uint32_t b = (m & 0x80000000u) ? (m & 0x7fffffffu) : ~m;
+  return __builtin_bit_cast(float, b);
+}
+
+template <typename T>
+__device__ __forceinline__ T sel4(int i, T v0, T v1, T v2, T v3) {
+  return i == 0 ? v0 : (i == 1 ? v1 : (i == 2 ? v2 : v3));
+}
+
+// j-th set bit of a 4-bit mask (j < popcount)
+__device__ __forceinline__ int nth_token(uint32_t mask, int j) {
+  const int t0 = __builtin_ctz(mask | 16u);
+  const uint32_t m1 = mask & (mask - 1);
+  const int t1 = __builtin_ctz(m1 | 16u);
+  const uint32_t m2 = m1 & (m1 - 1);
+  const int t2 = __builtin_ctz(m2 | 16u);
+  const uint32_t m3 = m2 & (m2 - 1);
+  const int t3 = __builtin_ctz(m3 | 16u);
+  return sel4(j, t0, t1, t2, t3);
+}
 
 // ---------------------------------------------------------------------------
 // Streaming core: RPL rows of NM matrices (same shape and format) against the
-// staged activations of up to NT tokens. Lane group (lpr lanes) g of the wave
-// owns rows row_base .. row_base+RPL-1; lane li of the group owns chunks
-// li, li+lpr, ... of each row. acc[m][r][t] gets the lane's partial sums.
+// staged activations of up to kNmax tokens. Lane group (lpr lanes) of the
+// wave owns rows row_base .. row_base+RPL-1; lane li of the group owns chunks
+// li, li+lpr, ... of each row. One pass covers lpr*IT chunks of every row.
 // ---------------------------------------------------------------------------
-template <int F, int NM, int RPL, int NT>
-__device__ __forceinline__ void stream_rows(const MatView (&mv)[NM], int row_base, int nrows,
-                                            int cpr, int lpr, const uint32_t* xs,
-                                            int xs_tok_words, uint32_t tokmask,
-                                            float (&acc)[NM][RPL][NT]) {
-  constexpr int XW = Fmt<F>::VPC / 2;  // 32-bit activation words per chunk
-  const int li = (threadIdx.x & 63) & (lpr - 1);
-  for (int c0 = 0; c0 < cpr; c0 += lpr * IT) {
-    uint4 wq[IT][NM][RPL];
-    uint32_t sc[IT][NM][RPL];
+template <int F, int NM, int RPL>
+struct Stream {
+  uint4 wq[IT][NM][RPL];
+  uint32_t sc[IT][NM][RPL];
+  float acc[NM][RPL][kNmax];
+
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int r = 0; r < RPL; ++r)
+#pragma unroll
+        for (int t = 0; t < kNmax; ++t) acc[m][r][t] = 0.f;
+  }
+
+  __device__ __forceinline__ void load(const MatView (&mv)[NM], int row_base, int nrows, int cpr,
+                                       int lpr, int li, int c0) {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int c = c0 + it * lpr + li;
@@ -68,13 +231,18 @@ __device__ __forceinline__ void stream_rows(const MatView (&mv)[NM], int row_bas
         }
       }
     }
+  }
+
+  __device__ __forceinline__ void compute(int cpr, int lpr, int li, int c0, const uint32_t* xs,
+                                          int xs_tok_words, uint32_t mask) {
+    constexpr int XW = Fmt<F>::VPC / 2;  // 32-bit activation words per chunk
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int c = c0 + it * lpr + li;
       if (c >= cpr) continue;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (!((tokmask >> t) & 1u)) continue;
+      for (int t = 0; t < kNmax; ++t) {
+        if (!((mask >> t) & 1u)) continue;
         uint32_t xv[XW];
         const uint4* xp = reinterpret_cast<const uint4*>(xs + t * xs_tok_words + c * XW);
 #pragma unroll
@@ -88,24 +256,24 @@ __device__ __forceinline__ void stream_rows(const MatView (&mv)[NM], int row_bas
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
-          for (int r = 0; r < RPL; ++r) acc[m][r][t] += chunk_dot<F>(wq[it][m][r], sc[it][m][r], xv);
+          for (int r = 0; r < RPL; ++r)
+            acc[m][r][t] += chunk_dot<F>(wq[it][m][r], sc[it][m][r], xv);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
-}
 
-// Copy the BF16 rows of the tokens in `mask` (row length `cols`) into LDS;
-// token t lands at LDS word t * cols/2.
-__device__ __forceinline__ void stage_rows(uint4* lds, const uint16_t* const* src, uint32_t mask,
-                                           int cols) {
-  const int per = cols / 8;  // uint4 per row
-  for (int i = threadIdx.x; i < kNmax * per; i += kThreads) {
-    const int t = i / per;
-    const int q = i - t * per;
-    if ((mask >> t) & 1u)
-      lds[t * per + q] = *reinterpret_cast<const uint4*>(src[t] + (size_t)q * 8);
+  // row sums land in the last lane of each lane group
+  __device__ __forceinline__ void reduce(int lpr, uint32_t mask) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int r = 0; r < RPL; ++r)
+#pragma unroll
+        for (int t = 0; t < kNmax; ++t)
+          if ((mask >> t) & 1u) acc[m][r][t] = group_sum_last(acc[m][r][t], lpr);
   }
-}
+};
 
 __device__ __forceinline__ MatView view_of(const DevProj& p, int e) {
   MatView v;
@@ -118,108 +286,136 @@ __device__ __forceinline__ MatView view_of(const DevProj& p, int e) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. Router projection.
+// Staging of activation rows into LDS (token t's row at LDS word
+// t * cols/2). Only tokens in `mask` are copied; each thread issues up to SB
+// loads before it stores any.
 // ---------------------------------------------------------------------------
-struct RouterArgs {
-  const uint16_t* x;
-  const uint16_t* w;
-  float* logits;
-  int N, H, E;
-};
-
-__global__ __launch_bounds__(kThreads) void k_router(RouterArgs a) {
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * (kThreads / 64) + wave;
-  if (e >= a.E) return;
-  const int t0 = blockIdx.y * kNmax;
-  const int nt = min(kNmax, a.N - t0);
-  const int cpr = a.H / 8;
-  const uint8_t* wrow = reinterpret_cast<const uint8_t*>(a.w) + (size_t)e * a.H * 2;
-  const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.x) + (size_t)t0 * a.H * 2;
-  float acc[kNmax] = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < cpr; c0 += 64 * IT) {
-    uint4 wq[IT];
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int c = c0 + it * 64 + lane;
-      wq[it] = c < cpr ? ldg16(wrow + (size_t)c * 16) : make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int c = c0 + it * 64 + lane;
-      if (c >= cpr) continue;
-#pragma unroll
-      for (int t = 0; t < kNmax; ++t) {
-        if (t >= nt) continue;
-        const uint4 xq = ldg16(xb + (size_t)t * a.H * 2 + (size_t)c * 16);
-        const uint32_t xv[4] = {xq.x, xq.y, xq.z, xq.w};
-        acc[t] += chunk_dot<FMT_BF16>(wq[it], 0u, xv);
-      }
-    }
+// BF16 input rows: token t at x + t * cols
+__device__ __forceinline__ void stage_x(uint4* lds, const uint16_t* x, uint32_t mask, int cols) {
+  const int m = __builtin_popcount(mask);
+  const int per = cols / 8;  // uint4 per row
+  const int total = m * per;
+  auto src = [&](int i) {
+    const int j = i / per;
+    return reinterpret_cast<const uint4*>(x + (size_t)nth_token(mask, j) * cols) + (i - j * per);
+  };
+  auto dst = [&](int i) {
+    const int j = i / per;
+    return lds + nth_token(mask, j) * per + (i - j * per);
+  };
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  for (int i0 = threadIdx.x; i0 < total; i0 += kThreads * SB) {
+    const int i1 = i0 + kThreads, i2 = i0 + 2 * kThreads, i3 = i0 + 3 * kThreads;
+    const uint4 v0 = *src(i0);
+    const uint4 v1 = i1 < total ? *src(i1) : z;
+    const uint4 v2 = i2 < total ? *src(i2) : z;
+    const uint4 v3 = i3 < total ? *src(i3) : z;
+    *dst(i0) = v0;
+    if (i1 < total) *dst(i1) = v1;
+    if (i2 < total) *dst(i2) = v2;
+    if (i3 < total) *dst(i3) = v3;
   }
-#pragma unroll
-  for (int t = 0; t < kNmax; ++t) {
-    const float s = wave_sum(acc[t]);
-    if (lane == 0 && t < nt) a.logits[(size_t)(t0 + t) * a.E + e] = s;
+}
+
+// Tagged FP32 activation rows from other workgroups: token t's row at
+// base + row_t * cols words. Words without the current tag are read again
+// (bounded). Rounded to BF16 (nearest even) into LDS.
+__device__ __forceinline__ void stage_tagged(const DecodeArgs& a, uint4* lds, const u64* base,
+                                             int r0, int r1, int r2, int r3, uint32_t mask,
+                                             int cols, unsigned tag) {
+  const int m = __builtin_popcount(mask);
+  uint32_t* w = reinterpret_cast<uint32_t*>(lds);
+  const int per = cols / 2;  // BF16 pairs per row
+  const int total = m * per;
+  auto src = [&](int i, int half) {
+    const int j = i / per;
+    const int row = sel4(nth_token(mask, j), r0, r1, r2, r3);
+    return base + (size_t)row * cols + 2 * (i - j * per) + half;
+  };
+  auto put = [&](int i, u64 lo, u64 hi) {
+    const int j = i / per;
+    w[nth_token(mask, j) * per + (i - j * per)] =
+        (uint32_t)f32_to_bf16_rne(tag_value(lo)) | ((uint32_t)f32_to_bf16_rne(tag_value(hi)) << 16);
+  };
+  for (int i0 = threadIdx.x; i0 < total; i0 += kThreads * 2) {
+    const int i1 = i0 + kThreads;
+    const bool has1 = i1 < total;
+    u64 v0 = ld_coh64(src(i0, 0)), v1 = ld_coh64(src(i0, 1));
+    u64 v2 = has1 ? ld_coh64(src(i1, 0)) : (u64)tag;
+    u64 v3 = has1 ? ld_coh64(src(i1, 1)) : (u64)tag;
+    unsigned spins = 0;
+    while ((unsigned)v0 != tag || (unsigned)v1 != tag || (unsigned)v2 != tag ||
+           (unsigned)v3 != tag) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > a.spin_limit) {
+        set_error(a, 2u);
+        break;
+      }
+      if ((unsigned)v0 != tag) v0 = ld_coh64(src(i0, 0));
+      if ((unsigned)v1 != tag) v1 = ld_coh64(src(i0, 1));
+      if ((unsigned)v2 != tag) v2 = ld_coh64(src(i1, 0));
+      if ((unsigned)v3 != tag) v3 = ld_coh64(src(i1, 1));
+    }
+    put(i0, v0, v1);
+    if (has1) put(i1, v2, v3);
   }
 }
 
 // ---------------------------------------------------------------------------
-// 2. Top-k routing and the expert plan (one workgroup, one wave per token).
+// Phase R: router rows, then (last router workgroup) top-k and the plan.
 // ---------------------------------------------------------------------------
-struct TopkArgs {
-  const float* logits;   // [N, E]
-  const float* bias;     // [E] or null
-  int N, E, k, scoring, renorm, maxu;
-  float rsf;
-  uint32_t* idx;         // [N, k]
-  float* wts;            // [N, k]
-  uint32_t* out_idx;     // optional copies
-  float* out_w;
-  float* out_logits;
-  int32_t* num_units;
-  int32_t* unit_expert;  // [maxu]
-  int32_t* unit_slot;    // [maxu, kNmax]
-  float* unit_w;         // [maxu, kNmax]
+struct TopkScratch {
+  int idx[kNmax * 16];
+  float w[kNmax * 16];
+  int present[256];
+  int unit_of[256];
+  int uexp[256];
+  int jpos[256 * kNmax];
+  float uw[256 * kNmax];
+  int nunits;
 };
 
-__global__ __launch_bounds__(kThreads) void k_topk_plan(TopkArgs a) {
-  __shared__ int s_idx[kNmax * 16];
-  __shared__ float s_w[kNmax * 16];
-  __shared__ int s_present[256];
-  __shared__ int s_unit_of[256];
-  __shared__ int s_slot[256 * kNmax];
-  __shared__ float s_uw[256 * kNmax];
-  __shared__ int s_uexp[256];
-  __shared__ int s_nunits;
-
+__device__ __forceinline__ void topk_and_plan(const DecodeArgs& a, TopkScratch* s, unsigned tag) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-
-  s_present[tid] = 0;
+  s->present[tid] = 0;
   for (int i = tid; i < 256 * kNmax; i += kThreads) {
-    s_slot[i] = -1;
-    s_uw[i] = 0.f;
+    s->jpos[i] = -1;
+    s->uw[i] = 0.f;
   }
-
   for (int t = wave; t < a.N; t += kThreads / 64) {
-    const float* z = a.logits + (size_t)t * a.E;
+    const u64* zrow = a.ctl->zlog + t * 256;
+    u64 zw[4] = {(u64)tag, (u64)tag, (u64)tag, (u64)tag};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i < a.E) zw[i] = ld_coh64(zrow + lane + 64 * i);
+    unsigned spins = 0;
+    while (!__all((unsigned)zw[0] == tag && (unsigned)zw[1] == tag && (unsigned)zw[2] == tag &&
+                  (unsigned)zw[3] == tag)) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > a.spin_limit) {
+        if (lane == 0) set_error(a, 4u);
+        break;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if ((unsigned)zw[i] != tag) zw[i] = ld_coh64(zrow + lane + 64 * i);
+    }
     float zv[4];
     uint32_t khi[4], klo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
       if (e < a.E) {
-        const float zz = z[e];
-        float s = zz;
+        const float zz = tag_value(zw[i]);
+        float sc = zz;
         if (a.scoring == 1) {
-          s = 1.0f / (1.0f + expf(-zz));
-          if (a.bias) s += a.bias[e];
+          sc = 1.0f / (1.0f + expf(-zz));
+          if (a.router_bias) sc += a.router_bias[e];
         }
         zv[i] = zz;
-        khi[i] = ordered_bits(s);
+        khi[i] = ordered_bits(sc);
         klo[i] = 0xffffffffu - (uint32_t)e;
         if (a.out_logits) a.out_logits[(size_t)t * a.E + e] = zz;
       } else {
@@ -230,17 +426,16 @@ __global__ __launch_bounds__(kThreads) void k_topk_plan(TopkArgs a) {
     }
     float zmax = 0.f, zsum = 1.f;
     if (a.scoring == 0) {
-      zmax = wave_max(fmaxf(fmaxf(zv[0], zv[1]), fmaxf(zv[2], zv[3])));
+      zmax = wave_max_dpp(fmaxf(fmaxf(zv[0], zv[1]), fmaxf(zv[2], zv[3])));
       float p = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (lane + 64 * i < a.E) p += expf(zv[i] - zmax);
-      zsum = wave_sum(p);
+      zsum = wave_sum_dpp(p);
     }
     int my_e = 0;
     float my_z = 0.f;
     for (int j = 0; j < a.k; ++j) {
-      // lane-local best
       uint32_t bh = khi[0], bl = klo[0];
 #pragma unroll
       for (int i = 1; i < 4; ++i) {
@@ -249,23 +444,23 @@ __global__ __launch_bounds__(kThreads) void k_topk_plan(TopkArgs a) {
           bl = klo[i];
         }
       }
-      // wave argmax on (score, -index)
-#pragma unroll
-      for (int m = 32; m > 0; m >>= 1) {
-        const uint32_t oh = __shfl_xor(bh, m, 64);
-        const uint32_t ol = __shfl_xor(bl, m, 64);
-        if (oh > bh || (oh == bh && ol > bl)) {
-          bh = oh;
-          bl = ol;
-        }
-      }
-      const int e = (int)(0xffffffffu - bl);
+      // the largest score; its lane's key when it is unique, else the
+      // largest key among the tied lanes
+      const uint32_t mh = wave_max_u32(bh);
+      const unsigned long long tied = __ballot(bh == mh);
+      uint32_t ml;
+      if (__popcll(tied) == 1)
+        ml = (uint32_t)__builtin_amdgcn_readlane((int)bl, __ffsll((long long)tied) - 1);
+      else
+        ml = wave_max_u32(bh == mh ? bl : 0u);
+      const int e = (int)(0xffffffffu - ml);
       const int slot = e >> 6;
       float zloc = zv[0];
 #pragma unroll
       for (int i = 1; i < 4; ++i)
         if (slot == i) zloc = zv[i];
-      const float zsel = __shfl(zloc, e & 63, 64);
+      const float zsel = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, zloc), e & 63));
       if (lane == (e & 63)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -281,33 +476,28 @@ __global__ __launch_bounds__(kThreads) void k_topk_plan(TopkArgs a) {
     }
     float w = 0.f;
     if (lane < a.k) w = (a.scoring == 0) ? expf(my_z - zmax) / zsum : 1.0f / (1.0f + expf(-my_z));
-    if (a.renorm) {
-      const float tot = wave_sum(w);
-      w = w / tot;
-    }
+    if (a.renorm) w = w / wave_sum_dpp(w);
     w *= a.rsf;
     if (lane < a.k) {
-      const int s = t * a.k + lane;
-      a.idx[s] = (uint32_t)my_e;
-      a.wts[s] = w;
-      if (a.out_idx) a.out_idx[s] = (uint32_t)my_e;
-      if (a.out_w) a.out_w[s] = w;
-      s_idx[s] = my_e;
-      s_w[s] = w;
+      const int sl = t * a.k + lane;
+      if (a.out_idx) a.out_idx[sl] = (uint32_t)my_e;
+      if (a.out_w) a.out_w[sl] = w;
+      s->idx[sl] = my_e;
+      s->w[sl] = w;
     }
   }
   __syncthreads();
   const int nslots = a.N * a.k;
-  if (tid < nslots) s_present[s_idx[tid]] = 1;
+  if (tid < nslots) s->present[s->idx[tid]] = 1;
   __syncthreads();
   if (wave == 0) {
-    // ascending expert order: exclusive scan of the presence flags
+    // units in ascending expert order: exclusive scan of the presence flags
     int cnt = 0;
     int loc[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       loc[q] = cnt;
-      cnt += s_present[lane * 4 + q];
+      cnt += s->present[lane * 4 + q];
     }
     int incl = cnt;
 #pragma unroll
@@ -317,180 +507,269 @@ __global__ __launch_bounds__(kThreads) void k_topk_plan(TopkArgs a) {
     }
     const int base = incl - cnt;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) s_unit_of[lane * 4 + q] = base + loc[q];
-    if (lane == 63) s_nunits = incl;
+    for (int q = 0; q < 4; ++q) s->unit_of[lane * 4 + q] = base + loc[q];
+    if (lane == 63) s->nunits = incl;
   }
   __syncthreads();
   if (tid < nslots) {
-    const int e = s_idx[tid];
-    const int u = s_unit_of[e];
+    const int e = s->idx[tid];
+    const int u = s->unit_of[e];
     const int t = tid / a.k;
-    s_uexp[u] = e;
-    s_slot[u * kNmax + t] = tid;
-    s_uw[u * kNmax + t] = s_w[tid];
+    s->uexp[u] = e;
+    s->jpos[u * kNmax + t] = tid - t * a.k;
+    s->uw[u * kNmax + t] = s->w[tid];
   }
   __syncthreads();
-  const int nu = s_nunits;
-  if (tid == 0) *a.num_units = nu;
+  // publish two tagged words per (unit, token): the plan info and the weight
+  const int nu = s->nunits;
   for (int i = tid; i < a.maxu * kNmax; i += kThreads) {
-    a.unit_slot[i] = s_slot[i];
-    a.unit_w[i] = s_uw[i];
+    const int u = i / kNmax;
+    const int t = i - u * kNmax;
+    unsigned info = 0u;
+    float wt = 0.f;
+    if (u >= nu) {
+      info = kPlanAbsent;
+    } else {
+      info = (unsigned)s->uexp[u] << 16;
+      const int j = s->jpos[i];
+      if (j >= 0) {
+        info |= kPlanPresent | (unsigned)j;
+        wt = s->uw[i];
+      }
+    }
+    u64* p = a.ctl->plan + u * kPlanStride + 2 * t;
+    st_coh64(p, tagged_u(info, tag));
+    st_coh64(p + 1, tagged(wt, tag));
   }
-  for (int i = tid; i < a.maxu; i += kThreads) a.unit_expert[i] = (i < nu) ? s_uexp[i] : 0;
+}
+
+__device__ __forceinline__ void router_phase(const DecodeArgs& a, int wg, uint4* smem, unsigned tag) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int e = wg * (kThreads / 64) + wave;
+  if (e < a.E) {
+    const int cpr = a.H / 8;
+    const uint8_t* wrow = reinterpret_cast<const uint8_t*>(a.router_w) + (size_t)e * a.H * 2;
+    const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.x);
+    float acc[kNmax] = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < cpr; c0 += 64 * IT) {
+      // router and token loads go out together
+      uint4 wq[IT], xq[IT][kNmax];
+      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int c = c0 + it * 64 + lane;
+        const bool in = c < cpr;
+        wq[it] = in ? ldg16(wrow + (size_t)c * 16) : z;
+#pragma unroll
+        for (int t = 0; t < kNmax; ++t)
+          xq[it][t] = (in && t < a.N) ? ldg16(xb + (size_t)t * a.H * 2 + (size_t)c * 16) : z;
+      }
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+#pragma unroll
+        for (int t = 0; t < kNmax; ++t) {
+          const uint32_t xv[4] = {xq[it][t].x, xq[it][t].y, xq[it][t].z, xq[it][t].w};
+          acc[t] += chunk_dot<FMT_BF16>(wq[it], 0u, xv);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kNmax; ++t) {
+      const float s = wave_sum_dpp(acc[t]);
+      if (lane == 0 && t < a.N) st_coh64(a.ctl->zlog + t * 256 + e, tagged(s, tag));
+    }
+  }
+  // the last router workgroup (it waits only on lower ids) routes
+  if (wg != a.nR - 1) return;
+  topk_and_plan(a, reinterpret_cast<TopkScratch*>(smem), tag);
+}
+
+// Unit u's plan (polling its tagged words). Returns false if the unit is
+// absent. slots[t] = t*k + j for tokens routed to the unit, else -1.
+__device__ __forceinline__ bool read_plan(const DecodeArgs& a, int u, unsigned tag, int& expert,
+                                          int (&slots)[kNmax], float (&wt)[kNmax],
+                                          uint32_t& mask, u64* s_words) {
+  if (threadIdx.x < 2 * kNmax) {
+    const u64* p = a.ctl->plan + u * kPlanStride + threadIdx.x;
+    u64 v = ld_coh64(p);
+    unsigned spins = 0;
+    while ((unsigned)v != tag) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > a.spin_limit) {
+        set_error(a, 1u);
+        break;
+      }
+      v = ld_coh64(p);
+    }
+    s_words[threadIdx.x] = v;
+  }
+  __syncthreads();
+  const unsigned info0 = (unsigned)(s_words[0] >> 32);
+  if (info0 & kPlanAbsent) return false;
+  expert = (int)((info0 >> 16) & 0xffu);
+  mask = 0;
+#pragma unroll
+  for (int t = 0; t < kNmax; ++t) {
+    const unsigned info = (unsigned)(s_words[2 * t] >> 32);
+    const bool present = t < a.N && (info & kPlanPresent);
+    slots[t] = present ? t * a.k + (int)(info & 31u) : -1;
+    wt[t] = tag_value(s_words[2 * t + 1]);
+    if (present) mask |= 1u << t;
+  }
+  return true;
 }
 
 // ---------------------------------------------------------------------------
-// 3. Expert gate + up projections and SiLU(gate) * up.
+// Phase GU: gate + up and SiLU(gate) * up. A workgroup covers g.sub row
+// blocks with one staging of x.
 // ---------------------------------------------------------------------------
-struct GateUpArgs {
-  DevProj gate, up, sgate, sup;
-  const uint16_t* x;
-  int N, H, k, I, I_s;
-  StageGeom gr, gs;
-  const int32_t* num_units;
-  const int32_t* unit_expert;
-  const int32_t* unit_slot;
-  uint16_t* a_routed;  // [N*k, I]
-  uint16_t* a_shared;  // [N, I_s]
-  float* zero_buf;     // atomic mode: accumulator cleared here
-  int zero_count;
-};
-
 template <int F, int RPL>
-__device__ __forceinline__ void gate_up_tile(const GateUpArgs& a, const DevProj& pg,
+__device__ __forceinline__ void gate_up_tile(const DecodeArgs& a, const DevProj& pg,
                                              const DevProj& pu, int e, int tile,
-                                             const StageGeom& g, int nrows, const uint32_t* xs,
-                                             uint32_t mask, const int (&slots)[kNmax],
-                                             uint16_t* dst) {
+                                             const StageGeom& g, int nrows, uint4* smem,
+                                             uint32_t mask, const int (&slots)[kNmax], u64* dst,
+                                             unsigned tag) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lpr = g.lpr;
-  const int groups = 64 / lpr;
-  const int row_base = tile * g.rows_per_wg + (wave * groups + lane / lpr) * RPL;
+  const int li = lane & (lpr - 1);
+  const int cpr = a.H / Fmt<F>::VPC;
+  const int block_rows = g.rows_per_wg / g.sub;
+  const int lane_row = (wave * (64 / lpr) + lane / lpr) * RPL;
   const MatView mv[2] = {view_of(pg, e), view_of(pu, e)};
-  float acc[2][RPL][kNmax];
+  const uint32_t* xs = reinterpret_cast<const uint32_t*>(smem);
+  // one row block at a time: nothing stays live across blocks, and the
+  // other workgroups on the compute unit keep the memory pipe busy
+#pragma nounroll
+  for (int sb = 0; sb < g.sub; ++sb) {
+    if (tile * g.rows_per_wg + sb * block_rows >= nrows) break;  // uniform
+    const int row_base = tile * g.rows_per_wg + sb * block_rows + lane_row;
+    Stream<F, 2, RPL> st;
+    st.zero();
+    for (int c0 = 0; c0 < cpr; c0 += lpr * IT) {
+      st.load(mv, row_base, nrows, cpr, lpr, li, c0);
+      st.compute(cpr, lpr, li, c0, xs, a.H / 2, mask);
+    }
+    st.reduce(lpr, mask);
+    if (li == lpr - 1) {
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+      for (int r = 0; r < RPL; ++r) {
+        const int row = row_base + r;
+        if (row >= nrows) continue;
+        const float sg = row_scale<F>(mv[0], row);
+        const float su = row_scale<F>(mv[1], row);
 #pragma unroll
-    for (int r = 0; r < RPL; ++r)
-#pragma unroll
-      for (int t = 0; t < kNmax; ++t) acc[m][r][t] = 0.f;
-  stream_rows<F, 2, RPL, kNmax>(mv, row_base, nrows, a.H / Fmt<F>::VPC, lpr, xs, a.H / 2, mask,
-                                acc);
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int r = 0; r < RPL; ++r)
-#pragma unroll
-      for (int t = 0; t < kNmax; ++t)
-        if ((mask >> t) & 1u) acc[m][r][t] = group_sum(acc[m][r][t], lpr);
-  if ((lane & (lpr - 1)) == 0) {
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      const int row = row_base + r;
-      if (row >= nrows) continue;
-      const float sg = row_scale<F>(mv[0], row);
-      const float su = row_scale<F>(mv[1], row);
-#pragma unroll
-      for (int t = 0; t < kNmax; ++t) {
-        if (!((mask >> t) & 1u)) continue;
-        const float gv = acc[0][r][t] * sg;
-        const float uv = acc[1][r][t] * su;
-        dst[(size_t)slots[t] * nrows + row] = f32_to_bf16_rne(silu_f32(gv) * uv);
+        for (int t = 0; t < kNmax; ++t) {
+          if (!((mask >> t) & 1u)) continue;
+          const float gv = st.acc[0][r][t] * sg;
+          const float uv = st.acc[1][r][t] * su;
+          const int slot = sel4(t, slots[0], slots[1], slots[2], slots[3]);
+          st_coh64(dst + (size_t)slot * nrows + row, tagged(silu_f32(gv) * uv, tag));
+        }
       }
     }
   }
 }
 
 template <int FR, int FS, int RPL>
-__global__ __launch_bounds__(kThreads) void k_gate_up(GateUpArgs a) {
-  extern __shared__ uint4 smem[];
-  const int bid = blockIdx.x;
-  if (a.zero_buf) {
-    const int per = (a.zero_count + gridDim.x - 1) / gridDim.x;
-    const int lo = bid * per;
-    const int hi = min(a.zero_count, lo + per);
-    for (int i = lo + threadIdx.x; i < hi; i += kThreads) a.zero_buf[i] = 0.f;
-  }
-  const bool is_shared = bid < a.gs.tiles;
-  int e = 0, tile = 0;
-  uint32_t mask = 0;
+__device__ __forceinline__ void gate_up_phase(const DecodeArgs& a, int wg, uint4* smem, unsigned* s_tmp,
+                              u64* s_words, unsigned tag) {
   int slots[kNmax];
-  const uint16_t* src[kNmax];
-  if (is_shared) {
-    tile = bid;
-#pragma unroll
-    for (int t = 0; t < kNmax; ++t) {
-      slots[t] = t;
-      src[t] = a.x + (size_t)t * a.H;
-      if (t < a.N) mask |= 1u << t;
-    }
-  } else {
-    const int r = bid - a.gs.tiles;
-    const int unit = r / a.gr.tiles;
-    tile = r - unit * a.gr.tiles;
-    if (unit >= *a.num_units) return;
-    e = a.unit_expert[unit];
-#pragma unroll
-    for (int t = 0; t < kNmax; ++t) {
-      const int s = a.unit_slot[unit * kNmax + t];
-      slots[t] = s;
-      src[t] = a.x + (size_t)t * a.H;
-      if (s >= 0) mask |= 1u << t;
-    }
-  }
-  stage_rows(smem, src, mask, a.H);
+  uint32_t mask = 0;
+  // x does not depend on the routing: stage every token now, while the
+  // router and top-k still run
+  const uint32_t all = (1u << a.N) - 1u;
+  stage_x(smem, a.x, all, a.H);
   __syncthreads();
-  const uint32_t* xs = reinterpret_cast<const uint32_t*>(smem);
-  if (is_shared) {
-    if constexpr (FS != FMT_NONE)
-      gate_up_tile<FS, RPL>(a, a.sgate, a.sup, 0, tile, a.gs, a.I_s, xs, mask, slots, a.a_shared);
-  } else {
-    gate_up_tile<FR, RPL>(a, a.gate, a.up, e, tile, a.gr, a.I, xs, mask, slots, a.a_routed);
+  if (wg < a.nGs) {
+    if constexpr (FS != FMT_NONE) {
+#pragma unroll
+      for (int t = 0; t < kNmax; ++t) slots[t] = t;
+      gate_up_tile<FS, RPL>(a, a.sgate, a.sup, 0, wg, a.gs, a.I_s, smem, all, slots, a.a_shared,
+                            tag);
+      wg_signal_noret(&a.unit_done[a.maxu * kLineWords]);
+    }
+    return;
   }
+  const int r = wg - a.nGs;
+  const int unit = r / a.gr.tiles;
+  const int tile = r - unit * a.gr.tiles;
+  int e;
+  float wt[kNmax];
+  if (!read_plan(a, unit, tag, e, slots, wt, mask, s_words)) return;
+  gate_up_tile<FR, RPL>(a, a.gate, a.up, e, tile, a.gr, a.I, smem, mask, slots, a.a_routed, tag);
+  wg_signal_noret(&a.unit_done[unit * kLineWords]);
 }
 
 // ---------------------------------------------------------------------------
-// 4. Down projections.
+// Phase D: down projections and the blend of each finished row block.
 // ---------------------------------------------------------------------------
-struct DownArgs {
-  DevProj down, sdown;
-  const uint16_t* a_routed;
-  const uint16_t* a_shared;
-  int N, H, k, I, I_s;
-  StageGeom gr, gs;
-  const int32_t* num_units;
-  const int32_t* unit_expert;
-  const int32_t* unit_slot;
-  const float* unit_w;
-  float* dbuf;  // slot mode: [N*k + N, H]
-  float* acc;   // atomic mode: [N, H]
-};
+__device__ __forceinline__ void blend_block(const DecodeArgs& a, int bt, unsigned tag) {
+  const int r0 = bt * a.blend_rows;
+  const int r1 = min(a.H, r0 + a.blend_rows);
+  const int rows = r1 - r0;
+  for (int i = threadIdx.x; i < a.N * rows; i += kThreads) {
+    const int t = i / rows;
+    const int r = r0 + (i - t * rows);
+    float y = 0.f;
+    if (a.atomic) {
+      float* p = a.acc + (size_t)t * a.H + r;
+      y = ld_coh(p);
+      st_coh(p, 0.f);  // leave the accumulator zeroed for the next call
+    } else {
+      // slots in order, then the shared expert
+      const int ns = a.k + (a.I_s > 0 ? 1 : 0);
+      for (int j = 0; j < ns; ++j) {
+        const int slot = j < a.k ? t * a.k + j : a.N * a.k + t;
+        const u64* p = a.dbuf + (size_t)slot * a.H + r;
+        u64 v = ld_coh64(p);
+        unsigned spins = 0;
+        while ((unsigned)v != tag) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins > a.spin_limit) {
+            set_error(a, 8u);
+            break;
+          }
+          v = ld_coh64(p);
+        }
+        y += tag_value(v);
+      }
+    }
+    a.out[(size_t)t * a.H + r] = f32_to_bf16_rne(y);
+  }
+}
 
 template <int F, int RPL>
-__device__ __forceinline__ void down_tile(const DownArgs& a, const DevProj& pd, int e, int tile,
-                                          const StageGeom& g, int cols, const uint32_t* xs,
+__device__ __forceinline__ void down_tile(const DecodeArgs& a, const DevProj& pd, int e, int tile,
+                                          const StageGeom& g, int cols, uint4* smem,
                                           uint32_t mask, const int (&slots)[kNmax],
-                                          const float (&wt)[kNmax], bool shared) {
+                                          const float (&wt)[kNmax], const u64* src, bool shared,
+                                          const unsigned* ready, unsigned ready_target,
+                                          unsigned tag) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lpr = g.lpr;
-  const int groups = 64 / lpr;
-  const int row_base = tile * g.rows_per_wg + (wave * groups + lane / lpr) * RPL;
+  const int li = lane & (lpr - 1);
+  const int row_base = tile * g.rows_per_wg + (wave * (64 / lpr) + lane / lpr) * RPL;
+  const int cpr = cols / Fmt<F>::VPC;
   const MatView mv[1] = {view_of(pd, e)};
-  float acc[1][RPL][kNmax];
-#pragma unroll
-  for (int r = 0; r < RPL; ++r)
-#pragma unroll
-    for (int t = 0; t < kNmax; ++t) acc[0][r][t] = 0.f;
-  stream_rows<F, 1, RPL, kNmax>(mv, row_base, a.H, cols / Fmt<F>::VPC, lpr, xs, cols / 2, mask,
-                                acc);
-#pragma unroll
-  for (int r = 0; r < RPL; ++r)
-#pragma unroll
-    for (int t = 0; t < kNmax; ++t)
-      if ((mask >> t) & 1u) acc[0][r][t] = group_sum(acc[0][r][t], lpr);
-  if ((lane & (lpr - 1)) == 0) {
+  Stream<F, 1, RPL> st;
+  st.zero();
+  st.load(mv, row_base, a.H, cpr, lpr, li, 0);
+  // weights are in flight; now wait for this unit's activations
+  wg_wait_geq(a, ready, ready_target, 2u);
+  stage_tagged(a, smem, src, slots[0] < 0 ? 0 : slots[0], slots[1] < 0 ? 0 : slots[1],
+               slots[2] < 0 ? 0 : slots[2], slots[3] < 0 ? 0 : slots[3], mask, cols, tag);
+  __syncthreads();
+  const uint32_t* xs = reinterpret_cast<const uint32_t*>(smem);
+  st.compute(cpr, lpr, li, 0, xs, cols / 2, mask);
+  for (int c0 = lpr * IT; c0 < cpr; c0 += lpr * IT) {
+    st.load(mv, row_base, a.H, cpr, lpr, li, c0);
+    st.compute(cpr, lpr, li, c0, xs, cols / 2, mask);
+  }
+  st.reduce(lpr, mask);
+  if (li == lpr - 1) {
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
       const int row = row_base + r;
@@ -499,12 +778,13 @@ __device__ __forceinline__ void down_tile(const DownArgs& a, const DevProj& pd, 
 #pragma unroll
       for (int t = 0; t < kNmax; ++t) {
         if (!((mask >> t) & 1u)) continue;
-        const float v = acc[0][r][t] * rs * wt[t];
-        if (a.acc) {
-          unsafeAtomicAdd(a.acc + (size_t)t * a.H + row, v);
+        const float v = st.acc[0][r][t] * rs * sel4(t, wt[0], wt[1], wt[2], wt[3]);
+        if (a.atomic) {
+          __hip_atomic_fetch_add(a.acc + (size_t)t * a.H + row, v, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
         } else {
-          const int s = shared ? a.N * a.k + t : slots[t];
-          a.dbuf[(size_t)s * a.H + row] = v;
+          const int s = shared ? a.N * a.k + t : sel4(t, slots[0], slots[1], slots[2], slots[3]);
+          st_coh64(a.dbuf + (size_t)s * a.H + row, tagged(v, tag));
         }
       }
     }
@@ -512,70 +792,97 @@ __device__ __forceinline__ void down_tile(const DownArgs& a, const DevProj& pd, 
 }
 
 template <int FR, int FS, int RPL>
-__global__ __launch_bounds__(kThreads) void k_down(DownArgs a) {
-  extern __shared__ uint4 smem[];
-  const int bid = blockIdx.x;
-  const bool is_shared = bid < a.gs.tiles;
-  int e = 0, tile = 0, cols = 0;
-  uint32_t mask = 0;
+__device__ __forceinline__ void down_phase(const DecodeArgs& a, int wg, uint4* smem, unsigned* s_tmp,
+                           u64* s_words, unsigned tag) {
   int slots[kNmax];
   float wt[kNmax];
-  const uint16_t* src[kNmax];
-  if (is_shared) {
-    tile = bid;
-    cols = a.I_s;
+  uint32_t mask = 0;
+  int row0;
+  if (wg < a.nDs) {
+    if constexpr (FS == FMT_NONE) {
+      return;
+    } else {
 #pragma unroll
-    for (int t = 0; t < kNmax; ++t) {
-      slots[t] = t;
-      wt[t] = 1.0f;
-      src[t] = a.a_shared + (size_t)t * a.I_s;
-      if (t < a.N) mask |= 1u << t;
+      for (int t = 0; t < kNmax; ++t) {
+        slots[t] = t;
+        wt[t] = 1.0f;
+        if (t < a.N) mask |= 1u << t;
+      }
+      row0 = wg * a.ds.rows_per_wg;
+      down_tile<FS, RPL>(a, a.sdown, 0, wg, a.ds, a.I_s, smem, mask, slots, wt, a.a_shared, true,
+                         &a.unit_done[a.maxu * kLineWords], (unsigned)a.nGs, tag);
     }
   } else {
-    const int r = bid - a.gs.tiles;
-    const int unit = r / a.gr.tiles;
-    tile = r - unit * a.gr.tiles;
-    if (unit >= *a.num_units) return;
-    e = a.unit_expert[unit];
-    cols = a.I;
-#pragma unroll
-    for (int t = 0; t < kNmax; ++t) {
-      const int s = a.unit_slot[unit * kNmax + t];
-      slots[t] = s;
-      wt[t] = a.unit_w[unit * kNmax + t];
-      src[t] = a.a_routed + (size_t)(s < 0 ? 0 : s) * a.I;
-      if (s >= 0) mask |= 1u << t;
-    }
+    const int r = wg - a.nDs;
+    const int unit = r / a.dr.tiles;
+    const int tile = r - unit * a.dr.tiles;
+    row0 = tile * a.dr.rows_per_wg;
+    int e;
+    if (read_plan(a, unit, tag, e, slots, wt, mask, s_words))
+      down_tile<FR, RPL>(a, a.down, e, tile, a.dr, a.I, smem, mask, slots, wt, a.a_routed, false,
+                         &a.unit_done[unit * kLineWords], (unsigned)a.gr.tiles, tag);
   }
-  stage_rows(smem, src, mask, cols);
-  __syncthreads();
-  const uint32_t* xs = reinterpret_cast<const uint32_t*>(smem);
-  if (is_shared) {
-    if constexpr (FS != FMT_NONE)
-      down_tile<FS, RPL>(a, a.sdown, 0, tile, a.gs, cols, xs, mask, slots, wt, true);
-  } else {
-    down_tile<FR, RPL>(a, a.down, e, tile, a.gr, cols, xs, mask, slots, wt, false);
+  const int bt = row0 / a.blend_rows;
+  const int rows_bt = min(a.blend_rows, a.H - bt * a.blend_rows);
+  if (!a.atomic) {
+    // slot mode: the highest-id contributor to the row block (the last unit's
+    // last tile in it) blends; it reads tagged words, so nobody signals
+    const int last_tile = (bt * a.blend_rows + rows_bt + a.dr.rows_per_wg - 1) / a.dr.rows_per_wg - 1;
+    const int r = wg - a.nDs;
+    if (wg >= a.nDs && r / a.dr.tiles == a.maxu - 1 && r - (a.maxu - 1) * a.dr.tiles == last_tile)
+      blend_block(a, bt, tag);
+    return;
   }
+  // atomic mode: every routed unit slot (absent ones too) and the shared
+  // expert take a ticket; the last one casts the accumulator
+  const unsigned expect =
+      (unsigned)a.maxu * (unsigned)((rows_bt + a.dr.rows_per_wg - 1) / a.dr.rows_per_wg) +
+      (a.I_s > 0 ? (unsigned)((rows_bt + a.ds.rows_per_wg - 1) / a.ds.rows_per_wg) : 0u);
+  const unsigned old = wg_signal(&a.blend_ctr[bt * kLineWords], s_tmp, true);
+  if (old + 1 != expect) return;
+  if (threadIdx.x == 0) st_coh(&a.blend_ctr[bt * kLineWords], 0u);
+  blend_block(a, bt, tag);
 }
 
 // ---------------------------------------------------------------------------
-// 5. Weighted sum + shared blend (slot mode) or accumulator cast (atomic).
+// The kernel.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void k_blend(const float* dbuf, uint16_t* out, int N, int H,
-                                                   int k, int has_shared) {
-  const int i = blockIdx.x * kThreads + threadIdx.x;
-  if (i >= N * H) return;
-  const int t = i / H;
-  const int r = i - t * H;
-  float y = 0.f;
-  for (int j = 0; j < k; ++j) y += dbuf[(size_t)(t * k + j) * H + r];
-  if (has_shared) y += dbuf[(size_t)(N * k + t) * H + r];
-  out[i] = f32_to_bf16_rne(y);
-}
-
-__global__ __launch_bounds__(kThreads) void k_finalize(const float* acc, uint16_t* out, int n) {
-  const int i = blockIdx.x * kThreads + threadIdx.x;
-  if (i < n) out[i] = f32_to_bf16_rne(acc[i]);
+template <int FR, int FS, int RPL>
+__global__ __launch_bounds__(kThreads) void k_moe_decode(DecodeArgs a) {
+  extern __shared__ uint4 smem[];
+  __shared__ unsigned s_tmp;
+  __shared__ u64 s_words[2 * kNmax];
+  const int bid = blockIdx.x;
+  // this call's tag: the workspace call counter + 1 (never 0, the value of
+  // zero-filled memory); stable until the last workgroup has finished
+  const unsigned tag = ld_coh(&a.ctl->epoch) + 1u;
+  if (bid < a.nR) {
+    router_phase(a, bid, smem, tag);
+  } else if (bid < a.nR + a.nGs + a.nGr) {
+    gate_up_phase<FR, FS, RPL>(a, bid - a.nR, smem, &s_tmp, s_words, tag);
+  } else {
+    down_phase<FR, FS, RPL>(a, bid - a.nR - a.nGs - a.nGr, smem, &s_tmp, s_words, tag);
+  }
+  // The last workgroup to finish advances the call counter and clears the
+  // unit counters. Completion is counted in two levels (per done group, then
+  // groups) so that no single counter takes an atomic from every workgroup.
+  const unsigned total = (unsigned)(a.nR + a.nGs + a.nGr + a.nDs + a.nDr);
+  const unsigned g = (unsigned)bid % kDoneGroups;
+  const unsigned in_group = (total - g + kDoneGroups - 1) / kDoneGroups;
+  const unsigned groups = total < (unsigned)kDoneGroups ? total : (unsigned)kDoneGroups;
+  const unsigned d = wg_signal(&a.ctl->group_done[g * kLineWords], &s_tmp, false);
+  if (d + 1 != in_group) return;
+  if (threadIdx.x == 0) {
+    st_coh(&a.ctl->group_done[g * kLineWords], 0u);
+    const unsigned top =
+        __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (top + 1 == groups) {
+      for (int u = 0; u <= a.maxu; ++u) st_coh(&a.unit_done[u * kLineWords], 0u);
+      st_coh(&a.ctl->done, 0u);
+      const unsigned next = tag == 0xffffffffu ? 0u : tag;  // keep the next tag non-zero
+      st_coh(&a.ctl->epoch, next);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -589,157 +896,60 @@ static int vpc_of(int fmt) {
   }
 }
 
-StageGeom plan_stage(int fmt, int cols, int rows, int units, bool /*two_mats*/) {
-  StageGeom g;
+int lanes_per_row(int fmt, int cols) {
   const int cpr = cols / vpc_of(fmt);
-  int want = (cpr + IT - 1) / IT;
+  const int want = (cpr + IT - 1) / IT;
   int lpr = 8;
   while (lpr < want && lpr < 64) lpr <<= 1;
-  g.lpr = lpr;
-  const int groups = 64 / lpr;
-  // two rows per lane group when that still leaves at least two workgroups
-  // per compute unit
-  const int rows_wg2 = (kThreads / 64) * groups * 2;
-  const long wgs2 = (long)units * ((rows + rows_wg2 - 1) / rows_wg2);
-  g.rpl = (wgs2 >= 512) ? 2 : 1;
-  g.rows_per_wg = (kThreads / 64) * groups * g.rpl;
+  return lpr;
+}
+
+StageGeom stage_geom(int fmt, int cols, int rows, int rpl, int sub) {
+  StageGeom g;
+  g.lpr = lanes_per_row(fmt, cols);
+  g.rpl = rpl;
+  g.sub = sub;
+  g.rows_per_wg = (kThreads / 64) * (64 / g.lpr) * rpl * sub;
   g.tiles = (rows + g.rows_per_wg - 1) / g.rows_per_wg;
   return g;
 }
 
-int decode_num_launches() { return 5; }
+size_t decode_lds_bytes(int H, int I, int I_s) {
+  int maxc = H > I ? H : I;
+  maxc = maxc > I_s ? maxc : I_s;
+  size_t b = (size_t)kNmax * maxc * 2;
+  if (b < sizeof(TopkScratch)) b = sizeof(TopkScratch);
+  return (b + 15) / 16 * 16;
+}
 
 template <int FR, int FS>
-static hipError_t launch_experts(const Call& c, hipStream_t st, hipEvent_t* ev) {
-  // gate + up
-  GateUpArgs ga;
-  ga.gate = c.gate;
-  ga.up = c.up;
-  ga.sgate = c.sgate;
-  ga.sup = c.sup;
-  ga.x = c.x;
-  ga.N = c.N;
-  ga.H = c.H;
-  ga.k = c.k;
-  ga.I = c.I;
-  ga.I_s = c.I_s;
-  ga.gr = c.gu_r;
-  ga.gs = c.gu_s;
-  ga.num_units = c.ws.num_units;
-  ga.unit_expert = c.ws.unit_expert;
-  ga.unit_slot = c.ws.unit_slot;
-  ga.a_routed = c.ws.a_routed;
-  ga.a_shared = c.ws.a_shared;
-  ga.zero_buf = c.atomic ? c.ws.acc : nullptr;
-  ga.zero_count = c.N * c.H;
-  const int gu_blocks = c.gu_s.tiles + c.maxu * c.gu_r.tiles;
-  const size_t gu_lds = (size_t)kNmax * c.H * 2;
-  if (ev) hipEventRecord(ev[2], st);
-  if (c.gu_r.rpl == 2)
-    hipLaunchKernelGGL((k_gate_up<FR, FS, 2>), dim3(gu_blocks), dim3(kThreads), gu_lds, st, ga);
+static hipError_t launch(const DecodeArgs& a, int rpl, size_t lds, hipStream_t st) {
+  const int blocks = a.nR + a.nGs + a.nGr + a.nDs + a.nDr;
+  if (rpl == 2)
+    hipLaunchKernelGGL((k_moe_decode<FR, FS, 2>), dim3(blocks), dim3(kThreads), lds, st, a);
   else
-    hipLaunchKernelGGL((k_gate_up<FR, FS, 1>), dim3(gu_blocks), dim3(kThreads), gu_lds, st, ga);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-
-  // down
-  DownArgs da;
-  da.down = c.down;
-  da.sdown = c.sdown;
-  da.a_routed = c.ws.a_routed;
-  da.a_shared = c.ws.a_shared;
-  da.N = c.N;
-  da.H = c.H;
-  da.k = c.k;
-  da.I = c.I;
-  da.I_s = c.I_s;
-  da.gr = c.dn_r;
-  da.gs = c.dn_s;
-  da.num_units = c.ws.num_units;
-  da.unit_expert = c.ws.unit_expert;
-  da.unit_slot = c.ws.unit_slot;
-  da.unit_w = c.ws.unit_w;
-  da.dbuf = c.atomic ? nullptr : c.ws.dbuf;
-  da.acc = c.atomic ? c.ws.acc : nullptr;
-  const int dn_blocks = c.dn_s.tiles + c.maxu * c.dn_r.tiles;
-  const int max_cols = c.I > c.I_s ? c.I : c.I_s;
-  const size_t dn_lds = (size_t)kNmax * max_cols * 2;
-  if (ev) hipEventRecord(ev[3], st);
-  if (c.dn_r.rpl == 2)
-    hipLaunchKernelGGL((k_down<FR, FS, 2>), dim3(dn_blocks), dim3(kThreads), dn_lds, st, da);
-  else
-    hipLaunchKernelGGL((k_down<FR, FS, 1>), dim3(dn_blocks), dim3(kThreads), dn_lds, st, da);
+    hipLaunchKernelGGL((k_moe_decode<FR, FS, 1>), dim3(blocks), dim3(kThreads), lds, st, a);
   return hipGetLastError();
 }
 
-// The shared expert (if any) uses the routed format or BF16.
 template <int FR>
-static hipError_t dispatch_shared(const Call& c, hipStream_t st, hipEvent_t* ev) {
-  switch (c.sgate.fmt) {
-    case FMT_NONE: return launch_experts<FR, FMT_NONE>(c, st, ev);
-    case FMT_BF16: return launch_experts<FR, FMT_BF16>(c, st, ev);
-    default: break;
-  }
-  if (c.sgate.fmt == FR) return launch_experts<FR, FR>(c, st, ev);
+static hipError_t dispatch_shared(const DecodeArgs& a, int fs, int rpl, size_t lds,
+                                  hipStream_t st) {
+  if (fs == FMT_NONE) return launch<FR, FMT_NONE>(a, rpl, lds, st);
+  if (fs == FMT_BF16) return launch<FR, FMT_BF16>(a, rpl, lds, st);
+  if (fs == FR) return launch<FR, FR>(a, rpl, lds, st);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(const Call& c, hipStream_t st, hipEvent_t* ev) {
-  // 1. router
-  RouterArgs ra{c.x, c.router_w, c.ws.logits, c.N, c.H, c.E};
-  dim3 rgrid((c.E + 3) / 4, (c.N + kNmax - 1) / kNmax);
-  if (ev) hipEventRecord(ev[0], st);
-  hipLaunchKernelGGL(k_router, rgrid, dim3(kThreads), 0, st, ra);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-
-  // 2. top-k + plan
-  TopkArgs ta;
-  ta.logits = c.ws.logits;
-  ta.bias = c.router_bias;
-  ta.N = c.N;
-  ta.E = c.E;
-  ta.k = c.k;
-  ta.scoring = c.scoring;
-  ta.renorm = c.renorm;
-  ta.maxu = c.maxu;
-  ta.rsf = c.rsf;
-  ta.idx = c.ws.idx;
-  ta.wts = c.ws.wts;
-  ta.out_idx = c.out_idx;
-  ta.out_w = c.out_w;
-  ta.out_logits = c.out_logits;
-  ta.num_units = c.ws.num_units;
-  ta.unit_expert = c.ws.unit_expert;
-  ta.unit_slot = c.ws.unit_slot;
-  ta.unit_w = c.ws.unit_w;
-  if (ev) hipEventRecord(ev[1], st);
-  hipLaunchKernelGGL(k_topk_plan, dim3(1), dim3(kThreads), 0, st, ta);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-
-  // 3-4. experts
-  switch (c.gate.fmt) {
-    case FMT_BF16: err = dispatch_shared<FMT_BF16>(c, st, ev); break;
-    case FMT_FP8: err = dispatch_shared<FMT_FP8>(c, st, ev); break;
-    case FMT_MXFP4: err = dispatch_shared<FMT_MXFP4>(c, st, ev); break;
-    case FMT_NVFP4: err = dispatch_shared<FMT_NVFP4>(c, st, ev); break;
-    default: err = hipErrorInvalidValue; break;
+hipError_t launch_decode(const DecodeArgs& a, int fr, int fs, int rpl, size_t lds,
+                         hipStream_t st) {
+  switch (fr) {
+    case FMT_BF16: return dispatch_shared<FMT_BF16>(a, fs, rpl, lds, st);
+    case FMT_FP8: return dispatch_shared<FMT_FP8>(a, fs, rpl, lds, st);
+    case FMT_MXFP4: return dispatch_shared<FMT_MXFP4>(a, fs, rpl, lds, st);
+    case FMT_NVFP4: return dispatch_shared<FMT_NVFP4>(a, fs, rpl, lds, st);
+    default: return hipErrorInvalidValue;
   }
-  if (err != hipSuccess) return err;
-
-  // 5. epilogue
-  const int n = c.N * c.H;
-  if (ev) hipEventRecord(ev[4], st);
-  if (c.atomic)
-    hipLaunchKernelGGL(k_finalize, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, st,
-                       c.ws.acc, c.out, n);
-  else
-    hipLaunchKernelGGL(k_blend, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, st,
-                       c.ws.dbuf, c.out, c.N, c.H, c.k, c.I_s > 0 ? 1 : 0);
-  err = hipGetLastError();
-  if (ev) hipEventRecord(ev[5], st);
-  return err;
 }
 
 }  // namespace moe

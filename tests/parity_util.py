@@ -50,7 +50,13 @@ def run_hip(layer, x, accum=None, out=None):
         out = torch.full_like(x, float("nan"))
     L.forward(x, out=out, idx=idx, weights=w, logits=logits)
     torch.cuda.synchronize()
+    assert device_error(L) == 0, "a workgroup wait expired"
     return out, idx, w, logits, L
+
+
+def device_error(L):
+    """The sticky error word at bytes 128..131 of the workspace."""
+    return int(L.workspace[128:132].view(torch.int32).item())
 
 
 def rel_l2_per_token(got, want):

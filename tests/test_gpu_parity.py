@@ -16,6 +16,8 @@ from parity_util import (OUT_RTOL, bits, check_against_oracle, run_hip, tie_free
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
+# per-call counters at the head of the workspace
+HEAD_BYTES = 384 + 64 * 128
 
 
 def _case(cfg_or_name, n, seed=0, accum=None, rows=None, label=None):
@@ -151,20 +153,30 @@ def test_atomic_and_slot_agree():
     assert err <= OUT_RTOL / 2
 
 
-def test_repeated_calls_reuse_workspace():
-    # the atomic accumulator and the plan live in the workspace; a second
-    # call with other tokens must not see the first call's state
-    print("[parity] workspace reuse", flush=True)
+@pytest.mark.parametrize("accum", ["atomic", "slot"])
+def test_repeated_calls_reuse_workspace(accum):
+    # counters, the plan and (atomic mode) the accumulator live in the
+    # workspace; calls with other tokens and other N must not see the
+    # previous call's state
+    print(f"[parity] workspace reuse {accum}", flush=True)
     from mixture_experts_layer_35_amd import Layer
+    from parity_util import device_error
     layer = synth.make_layer(NV_SMALL, device=DEV)
     npl = synth.as_numpy(layer)
     acc = tie_free_filter(npl)
-    L = Layer(layer, 4, accum="atomic")
-    for seed, n in ((70, 4), (71, 2), (72, 3)):
+    L = Layer(layer, 4, accum=accum)
+    for seed, n in ((70, 4), (71, 2), (72, 3), (73, 1), (74, 4)):
         x = synth.make_tokens(layer, n, seed, accept=acc)
         out = L.forward(x)
         torch.cuda.synchronize()
+        assert device_error(L) == 0
         ref = moe_forward(npl["cfg"], npl, bits(x))
         o = out.double().cpu().numpy()
         err = np.linalg.norm(o - ref["y"], axis=1) / np.linalg.norm(ref["y"], axis=1)
         assert err.max() <= OUT_RTOL, (seed, err)
+    # counters are back to zero, no wait expired, and the call counter
+    # advanced once per call (words: done 0, error 32, epoch 64, done groups
+    # from 96, one 32-word line each)
+    head = L.workspace[:HEAD_BYTES].view(torch.int32).cpu().numpy()
+    assert head[0] == 0 and head[32] == 0 and head[64] == 5, head[[0, 32, 64]]
+    assert not head[96:96 + 64 * 32].any()
