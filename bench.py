@@ -49,7 +49,24 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="budget of the oracle baseline (0 = skip)")
     p.add_argument("--no-trace", action="store_true", help="time without per-kernel events")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 256 MiB device copy three times (for scaling "
+                        "FETCH_SIZE / WRITE_SIZE counter readings) and exit")
     return p.parse_args()
+
+
+def copy_calibration():
+    """A plain copy kernel of known size: 256 MiB read and 256 MiB written
+    per dispatch, so counter readings of it give the counters' scale."""
+    import torch
+    nbytes = 256 << 20
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").random_(0, 255)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_dispatch": nbytes, "dispatches": 3}), flush=True)
 
 
 def main():
@@ -59,6 +76,9 @@ def main():
               "(expert parallelism would shard experts across GPUs; see the design notes).",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import numpy as np
     import torch

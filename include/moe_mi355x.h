@@ -140,10 +140,10 @@ typedef struct {
   float* logits;  /* [N, E] router logits (FP32) */
 } moe_topk_out;
 
-/* Optional timing hook: when non-NULL, events[0] is recorded on the stream
- * right before the call's first launch and events[num_launches] after its
- * last one; count must be >= num_launches + 1 (moe_num_launches gives the
- * number). The events must be created by the caller. */
+/* Optional timing hook: when non-NULL, launch i of the call (0 <=
+ * i < moe_num_launches) is made with hipExtLaunchKernel so that events[2i]
+ * and events[2i+1] record that kernel's own start and end; count must be
+ * >= 2 * moe_num_launches. The events must be created by the caller. */
 typedef struct {
   void** events; /* hipEvent_t[count] */
   int32_t count;
@@ -159,20 +159,46 @@ moe_status moe_validate(const moe_cfg* cfg, const moe_router* router,
                         const moe_experts* experts, const moe_experts* shared,
                         int32_t n_tokens, size_t workspace_bytes);
 
-/* Number of kernel launches moe_forward makes for this call (for moe_trace).
- * Returns -1 if the call is invalid. */
+/* Number of kernel launches moe_forward makes for this call (for moe_trace):
+ * 1 on the decode path (one fused kernel); 6 on the grouped path (router,
+ * top-k, grouping, gate+up, down, combine). Returns -1 if the call is
+ * invalid. */
 int32_t moe_num_launches(const moe_cfg* cfg, int32_t n_tokens);
+
+/* Where a grouped-path call keeps the result of its grouping step
+ * ("forward_batched.rs", MoeLayer::forward_batched: tokens grouped by expert
+ * so that each expert is streamed once for all of its rows). Byte offsets
+ * into the workspace, valid after the call has run on its stream and until
+ * the next call that uses the workspace. All arrays are int32:
+ *   info       [2 + 30 + 3 * 256]: U (distinct experts), M (rows in use),
+ *              30 unused, then uexp[256], ubase[256], ucount[256]: unit u's
+ *              expert (ascending), first row (a multiple of 16) and count;
+ *   perm_tok   [rows]: token of each grouped row, -1 on padding rows;
+ *   perm_slot  [rows]: slot t*k + j of each grouped row, -1 on padding;
+ *   inv        [n_tokens * k]: grouped row of each slot.
+ * Rows of one expert keep ascending slot order; each expert's rows are
+ * padded to a multiple of 16. */
+typedef struct {
+  size_t info, perm_tok, perm_slot, inv;
+  int32_t rows; /* capacity of perm_tok and perm_slot */
+} moe_group_view;
+
+/* Fills *view for a grouped-path call with this cfg and n_tokens. Returns
+ * MOE_ERR_UNSUPPORTED if such a call would take the decode path. Host only. */
+moe_status moe_group_layout(const moe_cfg* cfg, int32_t n_tokens, moe_group_view* view);
 
 /* The layer forward. x: device BF16 [n_tokens, H]; out: device BF16
  * [n_tokens, H] (every element is written); shared: NULL iff
  * cfg->shared_inter == 0; topk, trace: optional. workspace: device, 256-byte
  * aligned, at least moe_workspace_bytes(cfg, n_tokens) bytes, zero-filled
- * before the first call that uses it. Its head holds per-call counters (and,
- * in ATOMIC_F32 mode, the accumulator) that every call returns to zero, so a
+ * before the first call that uses it. Its head holds the decode path's
+ * per-call counters (and, in ATOMIC_F32 mode, its accumulator) that every
+ * decode call returns to zero and the grouped path leaves alone, so a
  * workspace sized for max_tokens serves any later call with the same cfg and
- * n_tokens <= max_tokens. Bytes 128..131 are a sticky device error word: non-zero
- * if a workgroup's bounded wait for another expired (results of that call are
- * then not valid). stream: hipStream_t (NULL = default stream). */
+ * n_tokens <= max_tokens, on either path. Bytes 128..131 are a sticky device
+ * error word: non-zero if a decode workgroup's bounded wait for another
+ * expired (results of that call are then not valid). stream: hipStream_t
+ * (NULL = default stream). */
 moe_status moe_forward(const moe_cfg* cfg, const moe_router* router,
                        const moe_experts* experts, const moe_experts* shared,
                        const void* x, int32_t n_tokens, void* out,

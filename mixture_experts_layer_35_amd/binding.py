@@ -20,7 +20,7 @@ PATH = {"auto": 0, "decode": 1, "grouped": 2}
 FORMAT = {"bf16": 0, "fp8_rowscale": 1, "mxfp4": 2, "nvfp4": 3}
 
 EXPORTED = ("moe_abi_version", "moe_last_error", "moe_status_str", "moe_workspace_bytes",
-            "moe_validate", "moe_num_launches", "moe_forward")
+            "moe_validate", "moe_num_launches", "moe_group_layout", "moe_forward")
 
 
 class MoeCfg(ctypes.Structure):
@@ -55,7 +55,18 @@ class MoeTrace(ctypes.Structure):
     _fields_ = [("events", ctypes.c_void_p), ("count", ctypes.c_int32)]
 
 
+class MoeGroupView(ctypes.Structure):
+    _fields_ = [("info", ctypes.c_size_t), ("perm_tok", ctypes.c_size_t),
+                ("perm_slot", ctypes.c_size_t), ("inv", ctypes.c_size_t),
+                ("rows", ctypes.c_int32)]
+
+
 _lib = None
+
+
+def _torch():
+    import torch
+    return torch
 
 
 class MoeError(RuntimeError):
@@ -82,6 +93,9 @@ def lib() -> ctypes.CDLL:
         L.moe_validate.argtypes = [ctypes.POINTER(MoeCfg), ctypes.POINTER(MoeRouter),
                                    ctypes.POINTER(MoeExperts), ctypes.POINTER(MoeExperts),
                                    ctypes.c_int32, ctypes.c_size_t]
+        L.moe_group_layout.restype = ctypes.c_int
+        L.moe_group_layout.argtypes = [ctypes.POINTER(MoeCfg), ctypes.c_int32,
+                                       ctypes.POINTER(MoeGroupView)]
         L.moe_num_launches.restype = ctypes.c_int32
         L.moe_num_launches.argtypes = [ctypes.POINTER(MoeCfg), ctypes.c_int32]
         L.moe_forward.restype = ctypes.c_int
@@ -177,6 +191,14 @@ def num_launches(cfg: MoeCfg, n_tokens: int) -> int:
     return int(lib().moe_num_launches(ctypes.byref(cfg), int(n_tokens)))
 
 
+def group_layout(cfg: MoeCfg, n_tokens: int) -> MoeGroupView:
+    v = MoeGroupView()
+    st = lib().moe_group_layout(ctypes.byref(cfg), int(n_tokens), ctypes.byref(v))
+    if st != MOE_OK:
+        raise MoeError(st, last_error())
+    return v
+
+
 def validate(cfg: MoeCfg, router: MoeRouter, experts: MoeExperts, shared: MoeExperts | None,
              n_tokens: int, ws_bytes: int) -> int:
     return int(lib().moe_validate(ctypes.byref(cfg), ctypes.byref(router), _ref(experts),
@@ -231,6 +253,24 @@ class Layer:
                 raise MoeError(st, last_error())
             return keep
         return call
+
+    def num_launches(self, n_tokens: int) -> int:
+        return num_launches(self.cfg, n_tokens)
+
+    def grouping(self, n_tokens: int) -> dict:
+        """The grouping step's result of the last grouped-path call with
+        n_tokens tokens, read from the workspace (host NumPy int32 arrays)."""
+        v = group_layout(self.cfg, n_tokens)
+        ws = self.workspace
+        k = self.cfg.top_k
+
+        def arr(off, count):
+            return ws[off:off + 4 * count].view(dtype=_torch().int32).cpu().numpy()
+        info = arr(v.info, 32 + 3 * 256)
+        return {"U": int(info[0]), "M": int(info[1]), "uexp": info[32:288],
+                "ubase": info[288:544], "ucount": info[544:800],
+                "perm_tok": arr(v.perm_tok, v.rows), "perm_slot": arr(v.perm_slot, v.rows),
+                "inv": arr(v.inv, n_tokens * k)}
 
     def forward(self, x, out=None, idx=None, weights=None, logits=None, stream=None,
                 events=None):

@@ -146,6 +146,25 @@ moe_status check_cfg(const moe_cfg* c) {
   return MOE_OK;
 }
 
+// Shape limits of each path (named refusals; no silent fallback).
+moe_status check_path_shape(const moe_cfg* c, int path) {
+  if (path == MOE_PATH_DECODE) {
+    // x (and a) rows of every token of a unit are staged in LDS
+    const int maxc = c->hidden > c->inter ? c->hidden : c->inter;
+    const int maxc2 = maxc > c->shared_inter ? maxc : c->shared_inter;
+    if ((size_t)moe::kNmax * maxc2 * 2 > 65536)
+      return fail(MOE_ERR_UNSUPPORTED, "decode path stages %d x %d BF16 in LDS; max width 8192",
+                  moe::kNmax, maxc2);
+  } else {
+    // the expert GEMMs step K in 128-column chunks
+    if (c->hidden % moe::kGKC || c->inter % moe::kGKC || c->shared_inter % moe::kGKC)
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "grouped path needs H, I and I_shared to be multiples of %d (H=%d I=%d I_s=%d)",
+                  moe::kGKC, c->hidden, c->inter, c->shared_inter);
+  }
+  return MOE_OK;
+}
+
 moe_status resolve_path(const moe_cfg* c, int32_t n, int* path) {
   if (n < 1 || n > MOE_MAX_TOKENS)
     return fail(MOE_ERR_INVALID_ARG, "n_tokens=%d outside 1..%d", n, MOE_MAX_TOKENS);
@@ -154,32 +173,63 @@ moe_status resolve_path(const moe_cfg* c, int32_t n, int* path) {
   if (p == MOE_PATH_DECODE && n > MOE_MAX_DECODE_TOKENS)
     return fail(MOE_ERR_UNSUPPORTED, "decode path takes at most %d tokens (n=%d)",
                 MOE_MAX_DECODE_TOKENS, n);
-  if (p == MOE_PATH_GROUPED)
-    return fail(MOE_ERR_UNSUPPORTED, "grouped path is not built yet (n=%d)", n);
-  // x (and a) rows of every token of a unit are staged in LDS
-  const int maxc = c->hidden > c->inter ? c->hidden : c->inter;
-  const int maxc2 = maxc > c->shared_inter ? maxc : c->shared_inter;
-  if ((size_t)moe::kNmax * maxc2 * 2 > 65536)
-    return fail(MOE_ERR_UNSUPPORTED, "decode path stages %d x %d BF16 in LDS; max width 8192",
-                moe::kNmax, maxc2);
+  moe_status st = check_path_shape(c, p);
+  if (st) return st;
   *path = p;
   return MOE_OK;
 }
 
-// Workspace layout of the decode path. The head (counters and, in atomic mode,
-// the FP32 accumulator) has a fixed size for a given cfg and must be zero at
-// rest; every call leaves it zero. The per-call buffers after it depend on N.
+// Launch plan of the grouped path for n tokens.
+struct GPlan {
+  int nt, W, maxu, ksplit, kcps, r_rb, r_tg, s_tg, gu_s, gu_r, dn_s, dn_r;
+  size_t mcap;  // rows of the permuted buffers
+};
+
+GPlan gplan(const moe_cfg* c, int n) {
+  GPlan g;
+  const int mmax = n < 128 ? n : 128;  // tokens of one expert per pass
+  g.nt = mmax <= 16 ? 1 : (mmax <= 32 ? 2 : (mmax <= 64 ? 4 : 8));
+  const int T = 16 * g.nt;
+  g.W = (n + 31) / 32;
+  const int64_t slots = (int64_t)n * c->top_k;
+  g.maxu = (int)(slots < c->num_experts ? slots : c->num_experts);
+  const int chunks = c->hidden / moe::kGKC;
+  g.r_rb = (c->num_experts + moe::kGRowsPerWG - 1) / moe::kGRowsPerWG;
+  g.r_tg = (n + T - 1) / T;
+  // split H so that the router has about 256 workgroups
+  int want = (256 + g.r_rb * g.r_tg - 1) / (g.r_rb * g.r_tg);
+  want = want < 1 ? 1 : (want > chunks ? chunks : want);
+  g.kcps = (chunks + want - 1) / want;
+  g.ksplit = (chunks + g.kcps - 1) / g.kcps;
+  g.s_tg = (n + T - 1) / T;
+  g.gu_r = c->inter / 64;
+  g.dn_r = c->hidden / moe::kGRowsPerWG;
+  g.gu_s = c->shared_inter > 0 ? (c->shared_inter / 64) * g.s_tg : 0;
+  g.dn_s = c->shared_inter > 0 ? g.dn_r * g.s_tg : 0;
+  g.mcap = align_up((size_t)slots + (size_t)15 * g.maxu, 16);
+  return g;
+}
+
+// Workspace layout. The head (decode-path counters and, in atomic mode, the
+// decode FP32 accumulator) has a fixed size for a given cfg and must be zero
+// at rest; every decode call leaves it zero and the grouped path does not
+// touch it. The per-call buffers after it depend on the path and on N.
 struct Layout {
   size_t head_bytes = 0;
   size_t total = 0;
+  // decode
   size_t unit_done = 0, blend_ctr = 0, acc = 0;
   size_t a_routed = 0, a_shared = 0, dbuf = 0;
+  // grouped
+  size_t g_zpart = 0, g_mask = 0, g_idx = 0, g_wts = 0, g_info = 0, g_ptok = 0, g_pslot = 0,
+         g_inv = 0, g_aperm = 0, g_ashared = 0, g_dperm = 0, g_dshared = 0, g_acc = 0;
 };
 
-Layout layout(const moe_cfg* c, int32_t n) {
+Layout layout(const moe_cfg* c, int32_t n, int path) {
   Layout L;
-  const size_t N = n, E = c->num_experts, k = c->top_k, H = c->hidden, I = c->inter,
-               Is = c->shared_inter;
+  const size_t N = n, k = c->top_k, H = c->hidden, I = c->inter, Is = c->shared_inter,
+               E = c->num_experts;
+  const bool atomic = c->accum_mode == MOE_ACCUM_ATOMIC_F32;
   size_t off = sizeof(moe::Ctl);
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -188,13 +238,40 @@ Layout layout(const moe_cfg* c, int32_t n) {
   };
   L.unit_done = take((MOE_MAX_EXPERTS + 1) * moe::kLineWords * 4);
   L.blend_ctr = take((H + 3) / 4 * moe::kLineWords * 4);
-  if (c->accum_mode == MOE_ACCUM_ATOMIC_F32) L.acc = take((size_t)moe::kNmax * H * 4);
+  if (atomic) L.acc = take((size_t)moe::kNmax * H * 4);
   L.head_bytes = off;
-  L.a_routed = take(N * k * I * 8);
-  L.a_shared = take(N * (Is ? Is : 1) * 8);
-  if (c->accum_mode != MOE_ACCUM_ATOMIC_F32) L.dbuf = take((N * k + N) * H * 8);
+  if (path == MOE_PATH_DECODE) {
+    L.a_routed = take(N * k * I * 8);
+    L.a_shared = take(N * (Is ? Is : 1) * 8);
+    if (!atomic) L.dbuf = take((N * k + N) * H * 8);
+  } else {
+    const GPlan g = gplan(c, n);
+    L.g_mask = take(E * g.W * 4);
+    L.g_idx = take(N * k * 4);
+    L.g_wts = take(N * k * 4);
+    L.g_info = take(sizeof(moe::GroupInfo));
+    L.g_ptok = take(g.mcap * 4);
+    L.g_pslot = take(g.mcap * 4);
+    L.g_inv = take(N * k * 4);
+    L.g_aperm = take(g.mcap * I * 2);
+    if (Is) L.g_ashared = take(N * Is * 2);
+    if (atomic) {
+      L.g_acc = take(N * H * 4);
+    } else {
+      L.g_dperm = take(g.mcap * H * 4);
+      if (Is) L.g_dshared = take(N * H * 4);
+    }
+    L.g_zpart = take((size_t)g.ksplit * N * E * 4);
+  }
   L.total = off;
   return L;
+}
+
+// Bytes a call with n tokens needs (0 if such a call is refused).
+size_t need_bytes(const moe_cfg* c, int32_t n) {
+  int path;
+  if (resolve_path(c, n, &path)) return 0;
+  return layout(c, n, path).total;
 }
 
 // Gate+up geometry: a workgroup stages x once (tokens * H BF16 into LDS) and
@@ -236,6 +313,75 @@ moe::DevProj to_dev(const moe_weight& w) {
   return p;
 }
 
+moe_status forward_grouped(const moe_cfg* cfg, const moe_router* router,
+                           const moe_experts* experts, const moe_experts* shared, const void* x,
+                           int32_t n, void* out, const moe_topk_out* topk, void* workspace,
+                           hipStream_t hs, hipEvent_t* ev) {
+  moe::GroupedArgs a{};
+  a.N = n;
+  a.H = cfg->hidden;
+  a.I = cfg->inter;
+  a.E = cfg->num_experts;
+  a.k = cfg->top_k;
+  a.I_s = cfg->shared_inter;
+  a.scoring = cfg->scoring;
+  a.renorm = cfg->norm_topk_prob;
+  a.atomic = cfg->accum_mode == MOE_ACCUM_ATOMIC_F32;
+  a.rsf = cfg->routed_scaling_factor;
+  a.x = static_cast<const uint16_t*>(x);
+  a.out = static_cast<uint16_t*>(out);
+  a.router_w = static_cast<const uint16_t*>(router->weight);
+  a.router_bias = router->bias;
+  a.gate = to_dev(experts->gate);
+  a.up = to_dev(experts->up);
+  a.down = to_dev(experts->down);
+  const int fr = experts->gate.format;
+  int fs = moe::FMT_NONE_HOST;
+  if (a.I_s > 0) {
+    a.sgate = to_dev(shared->gate);
+    a.sup = to_dev(shared->up);
+    a.sdown = to_dev(shared->down);
+    fs = shared->gate.format;
+  }
+  const GPlan g = gplan(cfg, n);
+  a.nt = g.nt;
+  a.W = g.W;
+  a.maxu = g.maxu;
+  a.ksplit = g.ksplit;
+  a.kcps = g.kcps;
+  a.r_rb = g.r_rb;
+  a.r_tg = g.r_tg;
+  a.s_tg = g.s_tg;
+  a.gu_s = g.gu_s;
+  a.gu_r = g.gu_r;
+  a.dn_s = g.dn_s;
+  a.dn_r = g.dn_r;
+  char* base = static_cast<char*>(workspace);
+  const Layout L = layout(cfg, n, MOE_PATH_GROUPED);
+  a.zpart = reinterpret_cast<float*>(base + L.g_zpart);
+  a.mask = reinterpret_cast<uint32_t*>(base + L.g_mask);
+  a.idx = reinterpret_cast<int*>(base + L.g_idx);
+  a.wts = reinterpret_cast<float*>(base + L.g_wts);
+  a.info = reinterpret_cast<moe::GroupInfo*>(base + L.g_info);
+  a.perm_tok = reinterpret_cast<int*>(base + L.g_ptok);
+  a.perm_slot = reinterpret_cast<int*>(base + L.g_pslot);
+  a.inv = reinterpret_cast<int*>(base + L.g_inv);
+  a.a_perm = reinterpret_cast<uint16_t*>(base + L.g_aperm);
+  a.a_shared = a.I_s ? reinterpret_cast<uint16_t*>(base + L.g_ashared) : nullptr;
+  a.d_perm = a.atomic ? nullptr : reinterpret_cast<float*>(base + L.g_dperm);
+  a.d_shared = (!a.atomic && a.I_s) ? reinterpret_cast<float*>(base + L.g_dshared) : nullptr;
+  a.acc = a.atomic ? reinterpret_cast<float*>(base + L.g_acc) : nullptr;
+  if (topk) {
+    a.out_idx = topk->idx;
+    a.out_w = topk->weights;
+    a.out_logits = topk->logits;
+  }
+  hipError_t err = moe::launch_grouped(a, fr, fs, hs, ev);
+  if (err != hipSuccess)
+    return fail(MOE_ERR_HIP, "launch failed: %s", hipGetErrorString(err));
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -259,7 +405,15 @@ size_t moe_workspace_bytes(const moe_cfg* cfg, int32_t max_tokens) {
   if (check_cfg(cfg)) return 0;
   int path;
   if (resolve_path(cfg, max_tokens, &path)) return 0;
-  return layout(cfg, max_tokens).total;
+  // the most any call with 1..max_tokens tokens needs (the router's K split
+  // makes the grouped size not quite monotone in N)
+  size_t most = 0;
+  for (int32_t n = 1; n <= max_tokens; ++n) {
+    const size_t b = need_bytes(cfg, n);
+    most = b > most ? b : most;
+  }
+  g_err[0] = 0;
+  return most;
 }
 
 moe_status moe_validate(const moe_cfg* cfg, const moe_router* router, const moe_experts* experts,
@@ -292,10 +446,29 @@ moe_status moe_validate(const moe_cfg* cfg, const moe_router* router, const moe_
   } else if (shared) {
     return fail(MOE_ERR_INVALID_ARG, "shared is given but shared_inter == 0");
   }
-  const size_t need = layout(cfg, n_tokens).total;
+  const size_t need = layout(cfg, n_tokens, path).total;
   if (workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace too small: need %zu bytes, have %zu", need,
                 workspace_bytes);
+  return MOE_OK;
+}
+
+moe_status moe_group_layout(const moe_cfg* cfg, int32_t n_tokens, moe_group_view* view) {
+  g_err[0] = 0;
+  moe_status st = check_cfg(cfg);
+  if (st) return st;
+  if (!view) return fail(MOE_ERR_INVALID_ARG, "null view");
+  int path;
+  st = resolve_path(cfg, n_tokens, &path);
+  if (st) return st;
+  if (path != MOE_PATH_GROUPED)
+    return fail(MOE_ERR_UNSUPPORTED, "a call with n_tokens=%d takes the decode path", n_tokens);
+  const Layout L = layout(cfg, n_tokens, path);
+  view->info = L.g_info;
+  view->perm_tok = L.g_ptok;
+  view->perm_slot = L.g_pslot;
+  view->inv = L.g_inv;
+  view->rows = (int32_t)gplan(cfg, n_tokens).mcap;
   return MOE_OK;
 }
 
@@ -303,7 +476,7 @@ int32_t moe_num_launches(const moe_cfg* cfg, int32_t n_tokens) {
   if (check_cfg(cfg)) return -1;
   int path;
   if (resolve_path(cfg, n_tokens, &path)) return -1;
-  return 1;
+  return path == MOE_PATH_DECODE ? 1 : moe::kGLaunches;
 }
 
 moe_status moe_forward(const moe_cfg* cfg, const moe_router* router, const moe_experts* experts,
@@ -322,8 +495,16 @@ moe_status moe_forward(const moe_cfg* cfg, const moe_router* router, const moe_e
         (topk->logits && !aligned(topk->logits, 4)))
       return fail(MOE_ERR_INVALID_ARG, "top-k outputs must be 4-byte aligned");
   }
-  if (trace && (!trace->events || trace->count < 2))
-    return fail(MOE_ERR_INVALID_ARG, "trace needs 2 events");
+  int path;
+  resolve_path(cfg, n_tokens, &path);
+  const int launches = path == MOE_PATH_DECODE ? 1 : moe::kGLaunches;
+  if (trace && (!trace->events || trace->count < 2 * launches))
+    return fail(MOE_ERR_INVALID_ARG, "trace needs %d events (start and stop of each launch), got %d",
+                2 * launches, trace ? trace->count : 0);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipEvent_t* ev = trace ? reinterpret_cast<hipEvent_t*>(trace->events) : nullptr;
+  if (path == MOE_PATH_GROUPED) return forward_grouped(cfg, router, experts, shared, x, n_tokens,
+                                                       out, topk, workspace, hs, ev);
 
   moe::DecodeArgs a{};
   a.N = n_tokens;
@@ -372,7 +553,7 @@ moe_status moe_forward(const moe_cfg* cfg, const moe_router* router, const moe_e
   a.spin_limit = 1u << 22;
 
   char* base = static_cast<char*>(workspace);
-  const Layout L = layout(cfg, n_tokens);
+  const Layout L = layout(cfg, n_tokens, MOE_PATH_DECODE);
   a.ctl = reinterpret_cast<moe::Ctl*>(base);
   a.unit_done = reinterpret_cast<unsigned*>(base + L.unit_done);
   a.blend_ctr = reinterpret_cast<unsigned*>(base + L.blend_ctr);
@@ -386,11 +567,8 @@ moe_status moe_forward(const moe_cfg* cfg, const moe_router* router, const moe_e
     a.out_logits = topk->logits;
   }
   const size_t lds = moe::decode_lds_bytes(a.H, a.I, a.I_s);
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  hipEvent_t* ev = trace ? reinterpret_cast<hipEvent_t*>(trace->events) : nullptr;
-  if (ev) hipEventRecord(ev[0], hs);
-  hipError_t err = moe::launch_decode(a, fr, fs, rpl, lds, hs);
-  if (ev) hipEventRecord(ev[1], hs);
+  hipError_t err = moe::launch_decode(a, fr, fs, rpl, lds, hs, ev ? ev[0] : nullptr,
+                                      ev ? ev[1] : nullptr);
   if (err != hipSuccess)
     return fail(MOE_ERR_HIP, "launch failed: %s", hipGetErrorString(err));
   return MOE_OK;

@@ -1,0 +1,320 @@
+// gfx950 kernels of the routed MoE layer forward, grouped path (any N).
+//
+// The batch is sorted by expert so that each selected expert's weights are
+// streamed once for all of the rows routed to it ("forward_batched.rs",
+// MoeLayer::forward_batched: one router GEMM over the batch, then per-expert
+// grouped work). Six stream-ordered launches:
+//
+//   router   z = x Wr^T as an MFMA GEMM, H split into ranges whose partial
+//            logits are summed in a fixed order by the next kernel; also
+//            clears the token masks
+//   top-k    one wave per token: logits, top-k (shared with the decode path),
+//            routing weights; sets bit t of mask[e] for each chosen e
+//   group    one workgroup: tokens per expert from the masks, counts padded
+//            to 16 rows, exclusive scan, and the stable permutation of the
+//            N*k slots by (expert, token); each slot's rank is the number of
+//            earlier tokens of the same expert (a token picks an expert at
+//            most once), read off the mask words with popcounts
+//   gate+up  one workgroup per (unit, 64 output features): g and u for the
+//            unit's rows as two 16x16 tiles per wave, a = silu(g) * u in BF16
+//            into the permuted activation buffer; the shared expert is one
+//            more unit holding every token
+//   down     one workgroup per (unit, 128 output rows): d = Wd a; slot mode
+//            stores d per permuted row, atomic mode adds w * d into an FP32
+//            [N,H] accumulator
+//   combine  y[t] = sum_j w[t,j] d[row(t,j)] + shared[t] in slot order, BF16
+//            round to nearest even
+//
+// The MFMA streaming GEMM and the expert kernels are in moe_grouped.h; the
+// expert kernels are instantiated per routed format in moe_grouped_*.hip.
+#include "moe_grouped.h"
+#include "moe_topk.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Router: z partials. Workgroup = (row block of 128 experts, token group,
+// K range); wave w owns expert rows rb*128 + 32w + [0, 32).
+// ---------------------------------------------------------------------------
+template <int NT>
+__global__ __launch_bounds__(kGThreads) void k_g_router(GroupedArgs a) {
+  extern __shared__ uint4 g_lds[];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // clear the token masks (the top-k kernel, launched next, sets them)
+  for (int i = blockIdx.x * kGThreads + tid; i < a.E * a.W; i += gridDim.x * kGThreads)
+    a.mask[i] = 0u;
+  const int s = blockIdx.x % a.ksplit;
+  const int tg = (blockIdx.x / a.ksplit) % a.r_tg;
+  const int rb = blockIdx.x / (a.ksplit * a.r_tg);
+  const int c0 = s * a.kcps;
+  const int nch = min(a.kcps, a.H / kGKC - c0);
+  const int t0 = tg * 16 * NT;
+  const int m = min(a.N - t0, 16 * NT);
+  ARow rows[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int e = min(rb * kGRowsPerWG + 32 * wave + 16 * t + (lane & 15), a.E - 1);
+    rows[t].data = reinterpret_cast<const uint8_t*>(a.router_w + (int64_t)e * a.H + c0 * kGKC);
+    rows[t].scales = nullptr;
+  }
+  const XRows x{a.x + (int64_t)t0 * a.H + c0 * kGKC, a.H, nullptr, m};
+  with_tiles<NT>((m + 15) >> 4, [&](auto ntc) {
+    constexpr int V = decltype(ntc)::value;
+    f32x4 acc[2][V];
+    stream_gemm<FMT_BF16, 2, V>(acc, rows, x, nch, g_lds);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int n = 0; n < V; ++n) {
+        const int j = n * 16 + (lane & 15);
+        if (j < m) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int e = rb * kGRowsPerWG + 32 * wave + 16 * t + 4 * (lane >> 4) + r;
+            if (e < a.E) a.zpart[((int64_t)s * a.N + t0 + j) * a.E + e] = acc[t][n][r];
+          }
+        }
+      }
+  });
+}
+
+// ---------------------------------------------------------------------------
+// Top-k: one wave per token.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kGThreads) void k_g_topk(GroupedArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kGThreads / 64) + (threadIdx.x >> 6);
+  if (t >= a.N) return;
+  float zv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    float z = -INFINITY;
+    if (e < a.E) {
+      z = 0.f;
+      for (int s = 0; s < a.ksplit; ++s) z += a.zpart[((int64_t)s * a.N + t) * a.E + e];
+      if (a.out_logits) a.out_logits[(int64_t)t * a.E + e] = z;
+    }
+    zv[i] = z;
+  }
+  int my_e;
+  float w;
+  topk_wave(zv, a.E, a.k, a.scoring, a.router_bias, a.renorm, a.rsf, lane, my_e, w);
+  if (lane < a.k) {
+    const int sl = t * a.k + lane;
+    a.idx[sl] = my_e;
+    a.wts[sl] = w;
+    if (a.out_idx) a.out_idx[sl] = (uint32_t)my_e;
+    if (a.out_w) a.out_w[sl] = w;
+    atomicOr(a.mask + (int64_t)my_e * a.W + (t >> 5), 1u << (t & 31));
+  }
+  if (a.atomic) {
+    float4* row = reinterpret_cast<float4*>(a.acc + (int64_t)t * a.H);
+    for (int i = lane; i < a.H / 4; i += 64) row[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Grouping: one workgroup of 1024 threads.
+// ---------------------------------------------------------------------------
+constexpr int kGroupThreads = 1024;
+
+constexpr int kPreBytes = 49152;  // LDS for word prefixes of one batch of experts
+
+size_t grouped_group_lds(int E, int W) {
+  (void)E;
+  (void)W;
+  return (256 + 257) * 4 + kPreBytes;
+}
+
+__global__ __launch_bounds__(kGroupThreads) void k_g_group(GroupedArgs a) {
+  extern __shared__ uint4 g_lds[];
+  int* cnt = reinterpret_cast<int*>(g_lds);  // [256]
+  int* base = cnt + 256;                     // [257]
+  uint16_t* pre = reinterpret_cast<uint16_t*>(base + 257);  // [EB * W] word prefixes
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nw = kGroupThreads / 64;
+  const int E = a.E, W = a.W;
+  // tokens per expert
+  for (int e = wave; e < E; e += nw) {
+    const uint32_t* mk = a.mask + (int64_t)e * W;
+    int c = 0;
+    for (int i = lane; i < W; i += 64) c += __popc(mk[i]);
+    c = (int)wave_sum_dpp((float)c);
+    if (lane == 0) cnt[e] = c;
+  }
+  __syncthreads();
+  // padded exclusive scan and the unit list (wave 0, four experts per lane)
+  if (wave == 0) {
+    int pc[4], fl[4], ps = 0, fs = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane * 4 + q;
+      const int c = e < E ? cnt[e] : 0;
+      pc[q] = (c + 15) & ~15;
+      fl[q] = c > 0;
+      ps += pc[q];
+      fs += fl[q];
+    }
+    int ip = ps, ifl = fs;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o1 = __shfl_up(ip, d, 64);
+      const int o2 = __shfl_up(ifl, d, 64);
+      if (lane >= d) {
+        ip += o1;
+        ifl += o2;
+      }
+    }
+    int b = ip - ps, u = ifl - fs;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane * 4 + q;
+      if (e < E) {
+        base[e] = b;
+        if (fl[q]) {
+          a.info->uexp[u] = e;
+          a.info->ubase[u] = b;
+          a.info->ucount[u] = cnt[e];
+        }
+      }
+      b += pc[q];
+      u += fl[q];
+    }
+    if (lane == 63) {
+      a.info->U = ifl;
+      a.info->M = ip;
+      base[E] = ip;
+    }
+  }
+  __syncthreads();
+  // padding rows
+  for (int e = tid; e < E; e += kGroupThreads) {
+    for (int r = base[e] + cnt[e]; r < base[e + 1]; ++r) {
+      a.perm_tok[r] = -1;
+      a.perm_slot[r] = -1;
+    }
+  }
+  // ranks, in batches of experts whose word prefixes fit in LDS
+  const int eb_max = kPreBytes / (2 * W);
+  const int nslots = a.N * a.k;
+  for (int e0 = 0; e0 < E; e0 += eb_max) {
+    const int e1 = min(E, e0 + eb_max);
+    for (int e = e0 + wave; e < e1; e += nw) {
+      const uint32_t* mk = a.mask + (int64_t)e * W;
+      int carry = 0;
+      for (int i0 = 0; i0 < W; i0 += 64) {
+        const int i = i0 + lane;
+        const int c = i < W ? __popc(mk[i]) : 0;
+        int incl = c;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int o = __shfl_up(incl, d, 64);
+          if (lane >= d) incl += o;
+        }
+        if (i < W) pre[(e - e0) * W + i] = (uint16_t)(carry + incl - c);
+        carry += __shfl(incl, 63, 64);
+      }
+    }
+    __syncthreads();
+    for (int s = tid; s < nslots; s += kGroupThreads) {
+      const int e = a.idx[s];
+      if (e < e0 || e >= e1) continue;
+      const int t = s / a.k;
+      const uint32_t wd = a.mask[(int64_t)e * W + (t >> 5)];
+      const int rank = pre[(e - e0) * W + (t >> 5)] + __popc(wd & ((1u << (t & 31)) - 1u));
+      const int pos = base[e] + rank;
+      a.perm_tok[pos] = t;
+      a.perm_slot[pos] = s;
+      a.inv[s] = pos;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine: four output columns per thread.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kGThreads) void k_g_combine(GroupedArgs a) {
+  const int64_t q = (int64_t)blockIdx.x * kGThreads + threadIdx.x;
+  const int qpr = a.H / 4;
+  if (q >= (int64_t)a.N * qpr) return;
+  const int t = (int)(q / qpr);
+  const int h = (int)(q - (int64_t)t * qpr) * 4;
+  float4 y;
+  if (a.atomic) {
+    y = *reinterpret_cast<const float4*>(a.acc + (int64_t)t * a.H + h);
+  } else {
+    y = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < a.k; ++j) {
+      const int s = t * a.k + j;
+      const float w = a.wts[s];
+      const float4 d = *reinterpret_cast<const float4*>(a.d_perm + (int64_t)a.inv[s] * a.H + h);
+      y.x += w * d.x;
+      y.y += w * d.y;
+      y.z += w * d.z;
+      y.w += w * d.w;
+    }
+    if (a.I_s > 0) {
+      const float4 d = *reinterpret_cast<const float4*>(a.d_shared + (int64_t)t * a.H + h);
+      y.x += d.x;
+      y.y += d.y;
+      y.z += d.z;
+      y.w += d.w;
+    }
+  }
+  *reinterpret_cast<uint2*>(a.out + (int64_t)t * a.H + h) =
+      make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+hipError_t launch_one(const void* fn, int blocks, int threads, size_t lds, hipStream_t st,
+                      const GroupedArgs& a, hipEvent_t* ev, int i) {
+  GroupedArgs copy = a;
+  void* args[] = {&copy};
+  if (blocks <= 0) {
+    if (!ev) return hipSuccess;
+    hipError_t e = hipEventRecord(ev[2 * i], st);
+    return e != hipSuccess ? e : hipEventRecord(ev[2 * i + 1], st);
+  }
+  if (ev) return hipExtLaunchKernel(fn, dim3(blocks), dim3(threads), args, lds, st, ev[2 * i],
+                                    ev[2 * i + 1], 0);
+  return hipLaunchKernel(fn, dim3(blocks), dim3(threads), args, lds, st);
+}
+
+static const void* router_fn(int nt) {
+  switch (nt) {
+    case 1: return reinterpret_cast<const void*>(&k_g_router<1>);
+    case 2: return reinterpret_cast<const void*>(&k_g_router<2>);
+    case 4: return reinterpret_cast<const void*>(&k_g_router<4>);
+    default: return reinterpret_cast<const void*>(&k_g_router<8>);
+  }
+}
+
+hipError_t launch_grouped(const GroupedArgs& a, int fr, int fs, hipStream_t st, hipEvent_t* ev) {
+  if (a.nt != 1 && a.nt != 2 && a.nt != 4 && a.nt != 8) return hipErrorInvalidValue;
+  hipError_t err = launch_one(router_fn(a.nt), a.r_rb * a.r_tg * a.ksplit, kGThreads,
+                              gemm_lds(a.nt), st, a, ev, 0);
+  if (err != hipSuccess) return err;
+  err = launch_one(reinterpret_cast<const void*>(&k_g_topk), (a.N + 3) / 4, kGThreads, 0, st, a,
+                   ev, 1);
+  if (err != hipSuccess) return err;
+  err = launch_one(reinterpret_cast<const void*>(&k_g_group), 1, kGroupThreads,
+                   grouped_group_lds(a.E, a.W), st, a, ev, 2);
+  if (err != hipSuccess) return err;
+  switch (fr) {
+    case FMT_BF16: err = launch_experts<FMT_BF16>(a, fs, st, ev); break;
+    case FMT_FP8: err = launch_experts<FMT_FP8>(a, fs, st, ev); break;
+    case FMT_MXFP4: err = launch_experts<FMT_MXFP4>(a, fs, st, ev); break;
+    case FMT_NVFP4: err = launch_experts<FMT_NVFP4>(a, fs, st, ev); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (err != hipSuccess) return err;
+  const int64_t quads = (int64_t)a.N * (a.H / 4);
+  return launch_one(reinterpret_cast<const void*>(&k_g_combine),
+                    (int)((quads + kGThreads - 1) / kGThreads), kGThreads, 0, st, a, ev, 5);
+}
+
+}  // namespace moe

@@ -1,0 +1,12 @@
+// Grouped-path expert kernels (gate+up, down) for routed BF16 weights.
+// One translation unit per routed format keeps the builds parallel.
+#include "moe_grouped.h"
+
+namespace moe {
+
+template <>
+hipError_t launch_experts<FMT_BF16>(const GroupedArgs& a, int fs, hipStream_t st, hipEvent_t* ev) {
+  return launch_experts_fs<FMT_BF16>(a, fs, st, ev);
+}
+
+}  // namespace moe

@@ -91,12 +91,74 @@ struct DecodeArgs {
   float* out_logits;
 };
 
+// ---------------------------------------------------------------------------
+// Grouped path (any N up to MOE_MAX_TOKENS): router GEMM, per-token top-k,
+// grouping of the N*k slots by expert, gate+up and down as grouped BF16 MFMA
+// GEMMs over the permuted rows, and a combine pass.
+// ---------------------------------------------------------------------------
+constexpr int kGKC = 128;         // K columns per staged activation chunk
+constexpr int kGRowsPerWG = 128;  // weight rows per workgroup (4 waves x 2 tiles x 16)
+constexpr int kGLaunches = 6;     // router, top-k, group, gate+up, down, combine
+
+// Result of the grouping step, read by the expert kernels.
+struct GroupInfo {
+  int U;         // distinct routed experts in the batch ("units")
+  int M;         // rows of the permuted buffers in use (per-unit counts padded to 16)
+  int pad[30];
+  int uexp[256];    // expert of unit u, ascending
+  int ubase[256];   // first permuted row of unit u (a multiple of 16)
+  int ucount[256];  // tokens routed to unit u
+};
+
+struct GroupedArgs {
+  const uint16_t* x;
+  const uint16_t* router_w;
+  const float* router_bias;
+  DevProj gate, up, down, sgate, sup, sdown;
+  int N, H, I, E, k, I_s, scoring, renorm, atomic;
+  float rsf;
+  int nt;      // 16-token MFMA tiles per pass (1, 2, 4 or 8)
+  int W;       // token-mask words per expert, ceil(N / 32)
+  int maxu;    // min(E, N * k)
+  int ksplit;  // router: H split into ksplit ranges of kcps 128-column chunks
+  int kcps;
+  // grids
+  int r_rb, r_tg;   // router row blocks, token groups
+  int s_tg;         // token groups of the shared expert
+  int gu_s, gu_r;   // gate+up: shared workgroups, workgroups per routed unit
+  int dn_s, dn_r;   // down: same
+  // workspace
+  float* zpart;      // [ksplit, N, E] partial router logits
+  uint32_t* mask;    // [E, W] bit t of word t/32: token t routes to expert e
+  int* idx;          // [N*k]
+  float* wts;        // [N*k]
+  GroupInfo* info;
+  int* perm_tok;     // [Mcap] token of each permuted row, -1 on padding
+  int* perm_slot;    // [Mcap] slot t*k+j of each permuted row, -1 on padding
+  int* inv;          // [N*k] permuted row of each slot
+  uint16_t* a_perm;  // [Mcap, I] BF16 silu(g)*u
+  uint16_t* a_shared;  // [N, I_s] BF16
+  float* d_perm;     // slot mode [Mcap, H] FP32 down outputs
+  float* d_shared;   // slot mode [N, H] FP32
+  float* acc;        // atomic mode [N, H] FP32
+  // outputs
+  uint16_t* out;
+  uint32_t* out_idx;
+  float* out_w;
+  float* out_logits;
+};
+
+// Enqueue the grouped path. ev: null, or 2 events per launch (start, stop).
+hipError_t launch_grouped(const GroupedArgs& a, int fr, int fs, hipStream_t stream,
+                          hipEvent_t* ev);
+size_t grouped_group_lds(int E, int W);
+
 int lanes_per_row(int fmt, int cols);
 StageGeom stage_geom(int fmt, int cols, int rows, int rpl, int sub);
 size_t decode_lds_bytes(int H, int I, int I_s);
 
 // Enqueue the fused decode kernel (formats: routed fr, shared fs or FMT_NONE).
 hipError_t launch_decode(const DecodeArgs& a, int fr, int fs, int rpl, size_t lds,
-                         hipStream_t stream);
+                         hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 
 }  // namespace moe

@@ -42,11 +42,13 @@
 // converts, then into v_dot2_f32_bf16 against BF16 activations; block scales
 // multiply per-chunk partial sums, row and tensor scales the row result; FP32
 // accumulation throughout.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "moe_topk.h"
 
 namespace moe {
 
@@ -122,54 +124,6 @@ __device__ __forceinline__ void wg_signal_noret(unsigned* p) {
   __syncthreads();
   if (threadIdx.x == 0)
     (void)__hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// ---------------------------------------------------------------------------
-// DPP reductions.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_f32(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
-                                                               ROW_MASK, 0xf, false));
-}
-
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  v += dpp_f32<0x111, 0xf>(v);
-  v += dpp_f32<0x112, 0xf>(v);
-  v += dpp_f32<0x114, 0xf>(v);
-  v += dpp_f32<0x118, 0xf>(v);
-  v += dpp_f32<0x142, 0xa>(v);
-  v += dpp_f32<0x143, 0xc>(v);
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-}
-
-// Sum over aligned groups of `width` lanes (8..64); the sum lands in the last
-// lane of each group.
-__device__ __forceinline__ float group_sum_last(float v, int width) {
-  v += dpp_f32<0x111, 0xf>(v);
-  v += dpp_f32<0x112, 0xf>(v);
-  v += dpp_f32<0x114, 0xf>(v);
-  if (width >= 16) v += dpp_f32<0x118, 0xf>(v);
-  if (width >= 32) v += dpp_f32<0x142, 0xa>(v);
-  if (width >= 64) v += dpp_f32<0x143, 0xc>(v);
-  return v;
-}
-
-// max over finite-or--inf floats via their ordered integer images
-__device__ __forceinline__ float wave_max_dpp(float v) {
-  const uint32_t m = wave_max_u32(ordered_bits(v));
-  const uint32_t b = (m & 0x80000000u) ? (m & 0x7fffffffu) : ~m;
-  return __builtin_bit_cast(float, b);
 }
 
 template <typename T>
@@ -403,81 +357,15 @@ __device__ __forceinline__ void topk_and_plan(const DecodeArgs& a, TopkScratch* 
         if ((unsigned)zw[i] != tag) zw[i] = ld_coh64(zrow + lane + 64 * i);
     }
     float zv[4];
-    uint32_t khi[4], klo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
-      if (e < a.E) {
-        const float zz = tag_value(zw[i]);
-        float sc = zz;
-        if (a.scoring == 1) {
-          sc = 1.0f / (1.0f + expf(-zz));
-          if (a.router_bias) sc += a.router_bias[e];
-        }
-        zv[i] = zz;
-        khi[i] = ordered_bits(sc);
-        klo[i] = 0xffffffffu - (uint32_t)e;
-        if (a.out_logits) a.out_logits[(size_t)t * a.E + e] = zz;
-      } else {
-        zv[i] = -INFINITY;
-        khi[i] = 0u;
-        klo[i] = 0u;
-      }
+      zv[i] = e < a.E ? tag_value(zw[i]) : -INFINITY;
+      if (a.out_logits && e < a.E) a.out_logits[(size_t)t * a.E + e] = zv[i];
     }
-    float zmax = 0.f, zsum = 1.f;
-    if (a.scoring == 0) {
-      zmax = wave_max_dpp(fmaxf(fmaxf(zv[0], zv[1]), fmaxf(zv[2], zv[3])));
-      float p = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (lane + 64 * i < a.E) p += expf(zv[i] - zmax);
-      zsum = wave_sum_dpp(p);
-    }
-    int my_e = 0;
-    float my_z = 0.f;
-    for (int j = 0; j < a.k; ++j) {
-      uint32_t bh = khi[0], bl = klo[0];
-#pragma unroll
-      for (int i = 1; i < 4; ++i) {
-        if (khi[i] > bh || (khi[i] == bh && klo[i] > bl)) {
-          bh = khi[i];
-          bl = klo[i];
-        }
-      }
-      // the largest score; its lane's key when it is unique, else the
-      // largest key among the tied lanes
-      const uint32_t mh = wave_max_u32(bh);
-      const unsigned long long tied = __ballot(bh == mh);
-      uint32_t ml;
-      if (__popcll(tied) == 1)
-        ml = (uint32_t)__builtin_amdgcn_readlane((int)bl, __ffsll((long long)tied) - 1);
-      else
-        ml = wave_max_u32(bh == mh ? bl : 0u);
-      const int e = (int)(0xffffffffu - ml);
-      const int slot = e >> 6;
-      float zloc = zv[0];
-#pragma unroll
-      for (int i = 1; i < 4; ++i)
-        if (slot == i) zloc = zv[i];
-      const float zsel = __builtin_bit_cast(
-          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, zloc), e & 63));
-      if (lane == (e & 63)) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (slot == i) {
-            khi[i] = 0u;
-            klo[i] = 0u;
-          }
-      }
-      if (lane == j) {
-        my_e = e;
-        my_z = zsel;
-      }
-    }
-    float w = 0.f;
-    if (lane < a.k) w = (a.scoring == 0) ? expf(my_z - zmax) / zsum : 1.0f / (1.0f + expf(-my_z));
-    if (a.renorm) w = w / wave_sum_dpp(w);
-    w *= a.rsf;
+    int my_e;
+    float w;
+    topk_wave(zv, a.E, a.k, a.scoring, a.router_bias, a.renorm, a.rsf, lane, my_e, w);
     if (lane < a.k) {
       const int sl = t * a.k + lane;
       if (a.out_idx) a.out_idx[sl] = (uint32_t)my_e;
@@ -922,32 +810,38 @@ size_t decode_lds_bytes(int H, int I, int I_s) {
   return (b + 15) / 16 * 16;
 }
 
+// With trace events, the launch goes through hipExtLaunchKernel, which
+// stamps the events at the kernel's own start and end (the same interval a
+// kernel trace reports) rather than around the enqueue.
 template <int FR, int FS>
-static hipError_t launch(const DecodeArgs& a, int rpl, size_t lds, hipStream_t st) {
+static hipError_t launch(const DecodeArgs& a, int rpl, size_t lds, hipStream_t st, hipEvent_t e0,
+                         hipEvent_t e1) {
   const int blocks = a.nR + a.nGs + a.nGr + a.nDs + a.nDr;
-  if (rpl == 2)
-    hipLaunchKernelGGL((k_moe_decode<FR, FS, 2>), dim3(blocks), dim3(kThreads), lds, st, a);
-  else
-    hipLaunchKernelGGL((k_moe_decode<FR, FS, 1>), dim3(blocks), dim3(kThreads), lds, st, a);
-  return hipGetLastError();
+  const void* fn = rpl == 2 ? reinterpret_cast<const void*>(&k_moe_decode<FR, FS, 2>)
+                            : reinterpret_cast<const void*>(&k_moe_decode<FR, FS, 1>);
+  DecodeArgs copy = a;
+  void* args[] = {&copy};
+  if (e0 || e1)
+    return hipExtLaunchKernel(fn, dim3(blocks), dim3(kThreads), args, lds, st, e0, e1, 0);
+  return hipLaunchKernel(fn, dim3(blocks), dim3(kThreads), args, lds, st);
 }
 
 template <int FR>
 static hipError_t dispatch_shared(const DecodeArgs& a, int fs, int rpl, size_t lds,
-                                  hipStream_t st) {
-  if (fs == FMT_NONE) return launch<FR, FMT_NONE>(a, rpl, lds, st);
-  if (fs == FMT_BF16) return launch<FR, FMT_BF16>(a, rpl, lds, st);
-  if (fs == FR) return launch<FR, FR>(a, rpl, lds, st);
+                                  hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  if (fs == FMT_NONE) return launch<FR, FMT_NONE>(a, rpl, lds, st, e0, e1);
+  if (fs == FMT_BF16) return launch<FR, FMT_BF16>(a, rpl, lds, st, e0, e1);
+  if (fs == FR) return launch<FR, FR>(a, rpl, lds, st, e0, e1);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int fr, int fs, int rpl, size_t lds,
-                         hipStream_t st) {
+                         hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   switch (fr) {
-    case FMT_BF16: return dispatch_shared<FMT_BF16>(a, fs, rpl, lds, st);
-    case FMT_FP8: return dispatch_shared<FMT_FP8>(a, fs, rpl, lds, st);
-    case FMT_MXFP4: return dispatch_shared<FMT_MXFP4>(a, fs, rpl, lds, st);
-    case FMT_NVFP4: return dispatch_shared<FMT_NVFP4>(a, fs, rpl, lds, st);
+    case FMT_BF16: return dispatch_shared<FMT_BF16>(a, fs, rpl, lds, st, e0, e1);
+    case FMT_FP8: return dispatch_shared<FMT_FP8>(a, fs, rpl, lds, st, e0, e1);
+    case FMT_MXFP4: return dispatch_shared<FMT_MXFP4>(a, fs, rpl, lds, st, e0, e1);
+    case FMT_NVFP4: return dispatch_shared<FMT_NVFP4>(a, fs, rpl, lds, st, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }

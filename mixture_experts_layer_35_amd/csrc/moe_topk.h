@@ -1,0 +1,145 @@
+// Wave-level reductions and the per-token top-k selection shared by the
+// decode and grouped kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "moe_device.h"
+
+namespace moe {
+
+// DPP reductions over the 64 lanes of a wave (row shifts, then the row
+// broadcasts 15 and 31); the full result is read from lane 63.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               ROW_MASK, 0xf, false));
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f32<0x111, 0xf>(v);
+  v += dpp_f32<0x112, 0xf>(v);
+  v += dpp_f32<0x114, 0xf>(v);
+  v += dpp_f32<0x118, 0xf>(v);
+  v += dpp_f32<0x142, 0xa>(v);
+  v += dpp_f32<0x143, 0xc>(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Sum over aligned groups of `width` lanes (8..64); the sum lands in the last
+// lane of each group.
+__device__ __forceinline__ float group_sum_last(float v, int width) {
+  v += dpp_f32<0x111, 0xf>(v);
+  v += dpp_f32<0x112, 0xf>(v);
+  v += dpp_f32<0x114, 0xf>(v);
+  if (width >= 16) v += dpp_f32<0x118, 0xf>(v);
+  if (width >= 32) v += dpp_f32<0x142, 0xa>(v);
+  if (width >= 64) v += dpp_f32<0x143, 0xc>(v);
+  return v;
+}
+
+// max over finite-or--inf floats via their ordered integer images
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  const uint32_t m = wave_max_u32(ordered_bits(v));
+  const uint32_t b = (m & 0x80000000u) ? (m & 0x7fffffffu) : ~m;
+  return __builtin_bit_cast(float, b);
+}
+
+// Top-k routing of one token by one wave ("forward_k3.rs",
+// MoeLayer::forward_k3, step 2; "forward_batched.rs", the routing step). The
+// router logits sit four per lane: expert lane + 64 i in zv[i] (-inf past E).
+// Selection score: the logit (softmax) or sigmoid(logit) + correction bias
+// (sigmoid). k rounds of a wave argmax over (score, -expert) keys, so equal
+// scores go to the lower expert index. Weights: softmax over all E logits or
+// the plain sigmoid of the chosen logits (no bias), optionally divided by
+// their sum, then times the routed scaling factor. Lane j < k returns the
+// j-th choice and its weight.
+__device__ __forceinline__ void topk_wave(const float zv[4], int E, int k, int scoring,
+                                          const float* bias, int renorm, float rsf, int lane,
+                                          int& my_e, float& my_w) {
+  uint32_t khi[4], klo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) {
+      float sc = zv[i];
+      if (scoring == 1) {
+        sc = 1.0f / (1.0f + expf(-zv[i]));
+        if (bias) sc += bias[e];
+      }
+      khi[i] = ordered_bits(sc);
+      klo[i] = 0xffffffffu - (uint32_t)e;
+    } else {
+      khi[i] = 0u;
+      klo[i] = 0u;
+    }
+  }
+  float zmax = 0.f, zsum = 1.f;
+  if (scoring == 0) {
+    zmax = wave_max_dpp(fmaxf(fmaxf(zv[0], zv[1]), fmaxf(zv[2], zv[3])));
+    float p = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i < E) p += expf(zv[i] - zmax);
+    zsum = wave_sum_dpp(p);
+  }
+  my_e = 0;
+  float my_z = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint32_t bh = khi[0], bl = klo[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+      if (khi[i] > bh || (khi[i] == bh && klo[i] > bl)) {
+        bh = khi[i];
+        bl = klo[i];
+      }
+    }
+    // the largest score; its lane's key when it is unique, else the largest
+    // key among the tied lanes
+    const uint32_t mh = wave_max_u32(bh);
+    const unsigned long long tied = __ballot(bh == mh);
+    uint32_t ml;
+    if (__popcll(tied) == 1)
+      ml = (uint32_t)__builtin_amdgcn_readlane((int)bl, __ffsll((long long)tied) - 1);
+    else
+      ml = wave_max_u32(bh == mh ? bl : 0u);
+    const int e = (int)(0xffffffffu - ml);
+    const int slot = e >> 6;
+    float zloc = zv[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i)
+      if (slot == i) zloc = zv[i];
+    const float zsel = __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, zloc), e & 63));
+    if (lane == (e & 63)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (slot == i) {
+          khi[i] = 0u;
+          klo[i] = 0u;
+        }
+    }
+    if (lane == j) {
+      my_e = e;
+      my_z = zsel;
+    }
+  }
+  float w = 0.f;
+  if (lane < k) w = (scoring == 0) ? expf(my_z - zmax) / zsum : 1.0f / (1.0f + expf(-my_z));
+  if (renorm) w = w / wave_sum_dpp(w);
+  my_w = w * rsf;
+}
+
+}  // namespace moe

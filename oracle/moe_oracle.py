@@ -55,7 +55,7 @@ import numpy as np
 __all__ = [
     "e2m1_to_f64", "e8m0_to_f64", "e4m3fn_to_f64", "bf16_to_f64",
     "unpack_fp4", "dequant", "router_logits", "selection_scores", "route",
-    "silu", "swiglu_expert", "moe_forward", "FORMATS",
+    "silu", "swiglu_expert", "moe_forward", "group_slots", "FORMATS",
 ]
 
 FORMATS = ("bf16", "fp8_rowscale", "mxfp4", "nvfp4")
@@ -245,13 +245,14 @@ def silu(v):
 
 
 def swiglu_expert(wg: np.ndarray, wu: np.ndarray, wd: np.ndarray, xt: np.ndarray):
-    """One expert on one token: g = Wg x, u = Wu x, a = silu(g) * u,
-    d = Wd a (the gate+up then silu+down kernel pair named on every page).
-    Returns (g, u, a, d)."""
-    g = wg @ xt
-    u = wu @ xt
+    """One expert on one token x (a vector) or on several (rows of a
+    matrix): g = Wg x, u = Wu x, a = silu(g) * u, d = Wd a (the gate+up then
+    silu+down kernel pair named on every page). Returns (g, u, a, d), one row
+    per token when xt is a matrix."""
+    g = xt @ wg.T
+    u = xt @ wu.T
     a = silu(g) * u
-    d = wd @ a
+    d = a @ wd.T
     return g, u, a, d
 
 
@@ -277,30 +278,71 @@ def moe_forward(cfg: dict, layer: dict, x_bits, rows=None) -> dict:
     idx, w = route(z, cfg["k"], cfg["scoring"], bias, cfg["renorm"], cfg["rsf"])
 
     out_rows = np.arange(h) if rows is None else np.asarray(rows)
-    y = np.zeros((n, out_rows.size), dtype=np.float64)
+    k = cfg["k"]
     ex = layer["experts"]
-    cache = {}
-    a_slots = np.zeros((n, cfg["k"], cfg["I"]), dtype=np.float64)
-    for t in range(n):
-        for j in range(cfg["k"]):
-            e = int(idx[t, j])
-            if e not in cache:
-                cache[e] = (dequant(ex["gate"], e), dequant(ex["up"], e),
-                            dequant(ex["down"], e, rows=out_rows))
-            wg, wu, wd = cache[e]
-            _, _, a, d = swiglu_expert(wg, wu, wd, x[t])
-            a_slots[t, j] = a
-            y[t] += w[t, j] * d
+    a_slots = np.zeros((n, k, cfg["I"]), dtype=np.float64)
+    d_slots = np.zeros((n, k, out_rows.size), dtype=np.float64)
+    # one expert's weights at a time (dequantised once for all of its slots)
+    for e in np.unique(idx):
+        wg, wu = dequant(ex["gate"], int(e)), dequant(ex["up"], int(e))
+        wd = dequant(ex["down"], int(e), rows=out_rows)
+        ts, js = np.nonzero(idx == e)
+        _, _, a, d = swiglu_expert(wg, wu, wd, x[ts])
+        a_slots[ts, js] = a
+        d_slots[ts, js] = d
+    y = np.zeros((n, out_rows.size), dtype=np.float64)
+    for j in range(k):
+        y += w[:, j:j + 1] * d_slots[:, j]
     s_out = None
     if layer.get("shared") is not None and cfg.get("I_s", 0) > 0:
         sh = layer["shared"]
         wg = dequant(sh["gate"], 0)
         wu = dequant(sh["up"], 0)
         wd = dequant(sh["down"], 0, rows=out_rows)
-        s_out = np.zeros_like(y)
-        for t in range(n):
-            _, _, _, d = swiglu_expert(wg, wu, wd, x[t])
-            s_out[t] = d
+        _, _, _, s_out = swiglu_expert(wg, wu, wd, x)
         y = y + s_out
     return {"y": y, "z": z, "idx": idx, "w": w, "a": a_slots,
             "shared": s_out, "rows": out_rows}
+
+
+# --------------------------------------------------------------------------
+# Grouping by expert.
+# --------------------------------------------------------------------------
+
+def group_slots(idx, num_experts: int, pad: int = 16) -> dict:
+    """Order of the N*k routing slots when the batch is grouped by expert
+    ("forward_batched.rs", ``MoeLayer::forward_batched``: the grouped FP8
+    decode comment, each expert streamed once for all of its rows; the
+    prefill workload sorts tokens per expert and pads each expert to 16-row
+    tiles).
+
+    Slot s = t*k + j is token t's j-th choice. Experts are laid out in
+    ascending order, each starting at a multiple of ``pad`` rows; within an
+    expert the slots keep ascending slot order (a stable sort by expert).
+    Rows past an expert's count up to its padded size are padding (-1).
+
+    Returns counts [E], offsets [E+1] (padded starts), perm_slot and
+    perm_tok [offsets[E]] (-1 on padding), inv [N*k] (row of each slot) and
+    units (experts with at least one slot, ascending).
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    n, k = idx.shape
+    counts = np.zeros(num_experts, dtype=np.int64)
+    for e in idx.reshape(-1):
+        counts[e] += 1
+    padded = (counts + pad - 1) // pad * pad
+    offsets = np.zeros(num_experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(padded)
+    perm_slot = np.full(offsets[-1], -1, dtype=np.int64)
+    perm_tok = np.full(offsets[-1], -1, dtype=np.int64)
+    inv = np.empty(n * k, dtype=np.int64)
+    fill = offsets[:-1].copy()
+    for s in range(n * k):  # ascending slot order: a stable counting sort
+        e = idx.reshape(-1)[s]
+        perm_slot[fill[e]] = s
+        perm_tok[fill[e]] = s // k
+        inv[s] = fill[e]
+        fill[e] += 1
+    units = np.nonzero(counts)[0]
+    return {"counts": counts, "offsets": offsets, "perm_slot": perm_slot,
+            "perm_tok": perm_tok, "inv": inv, "units": units}

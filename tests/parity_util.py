@@ -5,7 +5,8 @@ import numpy as np
 import torch
 
 import synth
-from oracle import moe_forward, router_logits, selection_scores, bf16_to_f64
+from oracle import (bf16_to_f64, group_slots, moe_forward, route, router_logits,
+                    selection_scores)
 
 # consecutive gap among the top k+1 selection scores; about 100x the FP32
 # error of a router logit at H = 7168
@@ -37,11 +38,11 @@ def bits(t):
     return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-def run_hip(layer, x, accum=None, out=None):
+def run_hip(layer, x, accum=None, out=None, path="auto"):
     from mixture_experts_layer_35_amd import Layer
     n = x.shape[0]
     cfg = layer["cfg"]
-    L = Layer(layer, n, accum=accum)
+    L = Layer(layer, n, accum=accum, path=path)
     dev = x.device
     idx = torch.full((n, cfg["k"]), 0xFFFF, dtype=torch.int32, device=dev)
     w = torch.full((n, cfg["k"]), float("nan"), dtype=torch.float32, device=dev)
@@ -67,25 +68,56 @@ def rel_l2_per_token(got, want):
     return num / den
 
 
-def check_against_oracle(layer, x, accum=None, rows=None, label=""):
+def check_grouping(L, n, ref_idx, num_experts):
+    """The grouped path's permutation against the oracle's, bit for bit."""
+    g = L.grouping(n)
+    ref = group_slots(ref_idx, num_experts, pad=16)
+    units = ref["units"]
+    U = len(units)
+    assert g["U"] == U, (g["U"], U)
+    assert g["M"] == ref["offsets"][-1]
+    assert np.array_equal(g["uexp"][:U], units)
+    assert np.array_equal(g["ubase"][:U], ref["offsets"][units])
+    assert np.array_equal(g["ucount"][:U], ref["counts"][units])
+    M = g["M"]
+    assert np.array_equal(g["perm_slot"][:M], ref["perm_slot"])
+    assert np.array_equal(g["perm_tok"][:M], ref["perm_tok"])
+    assert np.array_equal(g["inv"], ref["inv"])
+
+
+def check_against_oracle(layer, x, accum=None, rows=None, label="", path="auto", tokens=None):
     """Run the HIP path and the oracle on the same inputs and assert the
     bar: indices bit-exact, weights within W_RTOL, logits within 1e-5 (abs,
     relative to their scale), per-token relative L2 of the output within
-    OUT_RTOL. Returns the measured errors."""
+    OUT_RTOL; on the grouped path also the grouping, bit for bit.
+
+    ``rows`` restricts the output check to those hidden rows and ``tokens``
+    to those tokens (the oracle's expert work then covers only them; routing
+    is still checked for every token). Returns the measured errors."""
     npl = synth.as_numpy(layer)
+    cfg = npl["cfg"]
     xb = bits(x)
-    ref = moe_forward(npl["cfg"], npl, xb, rows=rows)
-    out, idx, w, logits, _ = run_hip(layer, x, accum=accum)
+    n = xb.shape[0]
+    out, idx, w, logits, L = run_hip(layer, x, accum=accum, path=path)
+    # routing of every token
+    z = router_logits(bf16_to_f64(xb), bf16_to_f64(npl["router"]["weight"]))
+    ref_idx, ref_w = route(z, cfg["k"], cfg["scoring"], npl["router"]["bias"], cfg["renorm"],
+                           cfg["rsf"])
     got_idx = idx.cpu().numpy().astype(np.int64)
-    assert np.array_equal(got_idx, ref["idx"]), f"{label}: indices differ\n{got_idx}\n{ref['idx']}"
+    assert np.array_equal(got_idx, ref_idx), f"{label}: indices differ\n{got_idx}\n{ref_idx}"
     got_w = w.cpu().numpy().astype(np.float64)
-    np.testing.assert_allclose(got_w, ref["w"], rtol=W_RTOL, atol=0, err_msg=label)
+    np.testing.assert_allclose(got_w, ref_w, rtol=W_RTOL, atol=0, err_msg=label)
     got_z = logits.cpu().numpy().astype(np.float64)
-    zscale = np.abs(ref["z"]).max()
-    assert np.abs(got_z - ref["z"]).max() <= 1e-5 * max(1.0, zscale), label
+    zscale = np.abs(z).max()
+    assert np.abs(got_z - z).max() <= 1e-5 * max(1.0, zscale), label
+    grouped = L.num_launches(n) > 1
+    if grouped:
+        check_grouping(L, n, ref_idx, cfg["E"])
     o = bf16_to_f64(bits(out))
     assert np.isfinite(o).all(), f"{label}: non-finite output (unwritten rows?)"
+    tok = np.arange(n) if tokens is None else np.asarray(tokens)
+    ref = moe_forward(cfg, npl, xb[tok], rows=rows)
     sel = ref["rows"]
-    err = rel_l2_per_token(o[:, sel], ref["y"])
+    err = rel_l2_per_token(o[tok][:, sel], ref["y"])
     assert err.max() <= OUT_RTOL, f"{label}: rel L2 {err}"
-    return {"rel_l2": float(err.max()), "out": out}
+    return {"rel_l2": float(err.max()), "out": out, "grouped": grouped}

@@ -159,12 +159,36 @@ def test_token_count_range(n):
     assert B.validate(c, r, ex, sh, n, 1 << 40) != B.MOE_OK
 
 
-def test_decode_token_limit_and_grouped_not_built():
+def test_decode_token_limit_and_path_choice():
     c, r, ex, sh = _c3()
     c.path = B.PATH["decode"]
     assert B.validate(c, r, ex, sh, 5, 1 << 40) == B.MOE_ERR_UNSUPPORTED
     c.path = B.PATH["auto"]
-    assert B.validate(c, r, ex, sh, 16, 1 << 40) == B.MOE_ERR_UNSUPPORTED
+    assert B.validate(c, r, ex, sh, 16, 1 << 40) == B.MOE_OK
+    assert B.num_launches(c, 4) == 1      # decode: one fused kernel
+    assert B.num_launches(c, 16) == 6     # grouped: router, top-k, group, gate+up, down, combine
+    c.path = B.PATH["grouped"]
+    assert B.num_launches(c, 1) == 6
+    assert B.validate(c, r, ex, sh, 1, 1 << 40) == B.MOE_OK
+
+
+def test_grouped_shape_limits():
+    # the grouped path steps K in 128-column chunks
+    c, r, ex, sh = _c3()
+    c.path = B.PATH["grouped"]
+    c.hidden, c.inter, c.shared_inter = 544, 192, 0
+    ex = _fake_set("mxfp4", 544, 192, 256, FAKE)
+    assert B.validate(c, r, ex, None, 16, 1 << 40) == B.MOE_ERR_UNSUPPORTED
+    assert "multiples of 128" in B.last_error()
+    c.path = B.PATH["auto"]
+    assert B.validate(c, r, ex, None, 4, 1 << 40) == B.MOE_OK   # decode takes it
+
+
+def test_workspace_covers_every_smaller_call():
+    c, r, ex, sh = _c3()
+    ws = B.workspace_bytes(c, 300)
+    for n in (1, 4, 5, 16, 64, 129, 255, 300):
+        assert B.validate(c, r, ex, sh, n, ws) == B.MOE_OK, n
 
 
 def test_shared_presence_must_match_cfg():
