@@ -1,18 +1,27 @@
 """Benchmark of the routed MoE layer forward on one MI355X.
 
-python bench.py [--steps K] [--warmup W] [--config NAME] [--n N]
+python bench.py [--steps K] [--warmup W] [--config NAME] [--n N] [--accum slot|atomic]
 
-A step is one moe_forward call (router, top-k, expert gate+up, down, blend)
-on one batch of N synthetic tokens with the inputs already in HBM. Batches
-rotate through a pool and the weights through enough copies that a call does
-not find its experts in the 256 MB Infinity Cache left by earlier calls.
-Prints one JSON line (µs per call, expert-weight GB/s, roofline of the
-dominant kernel from HIP events recorded inside the call, and the FP64 oracle
-timed on the host cores as a reference point).
+A step is one moe_forward call (router, top-k, experts, weighted sum and
+shared-expert blend) on one batch of N synthetic tokens with the inputs
+already in HBM. Token batches rotate through a pool and the weights through
+enough copies that a call does not find its experts in the 256 MB Infinity
+Cache left by earlier calls. Prints one JSON line: us per call (the metric),
+expert-weight GB/s, per-kernel times from HIP events that bracket each kernel
+(hipExtLaunchKernel start/stop events, the interval a kernel trace reports),
+the roofline of the dominant kernel, and the FP64 oracle timed on the host
+cores as a reference point.
+
+Default workload: the Qwen3-30B-A3B-shaped MXFP4 layer at N = 1 token (decode
+path, one fused kernel). --config grouped_fp8_h4096 / prefill_bf16_h4096 run
+the grouped path (six launches: router, top-k, grouping, gate+up, down,
+combine).
 """
 
 import argparse
 import ctypes
+import glob
+import hashlib
 import json
 import math
 import os
@@ -22,9 +31,12 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
 MALL_BYTES = 256 << 20
-KERNELS = ["moe_decode"]
+KERNELS = {1: ["k_moe_decode"],
+           6: ["k_g_router", "k_g_topk", "k_g_group", "k_g_gate_up", "k_g_down", "k_g_combine"]}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
 def hip():
@@ -45,6 +57,7 @@ def parse():
     p.add_argument("--config", default="qwen3_30b_a3b_mxfp4")
     p.add_argument("--n", type=int, default=None, help="tokens per call")
     p.add_argument("--accum", default=None, choices=[None, "slot", "atomic"])
+    p.add_argument("--path", default="auto", choices=["auto", "decode", "grouped"])
     p.add_argument("--pool", type=int, default=64, help="distinct token batches")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="budget of the oracle baseline (0 = skip)")
@@ -69,6 +82,33 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_per_dispatch": nbytes, "dispatches": 3}), flush=True)
 
 
+def kernel_sources_sha256() -> str:
+    """Hash of the kernel sources: counter readings taken on other sources are
+    not reported."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "mixture_experts_layer_35_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_for(key: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none for this kernel and workload or the sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    ent = rec.get("entries", {}).get(key)
+    if not ent:
+        return None
+    return (ent["fetch_kib"] * rec["fetch_scale"] + ent["write_kib"] * rec["write_scale"]) * 1024.0
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -90,6 +130,7 @@ def main():
     torch.cuda.set_device(0)
     cfg = dict(synth.CONFIGS[args.config])
     n = args.n or cfg["n_list"][0]
+    accum = args.accum or cfg["accum"]
     layer = synth.make_layer(args.config, device=dev)
     by = synth.layer_bytes(layer)
 
@@ -98,7 +139,7 @@ def main():
     per_call_guess = min(cfg["E"], n * cfg["k"]) * by["expert"] + by["shared"]
     copies = max(1, min(32, math.ceil(2 * MALL_BYTES / max(1, per_call_guess)) + 1))
     layers = [layer] + [synth.clone_weights(layer) for _ in range(copies - 1)]
-    bound = [Layer(l, n, accum=args.accum) for l in layers]
+    bound = [Layer(l, n, accum=accum, path=args.path) for l in layers]
     xs = [synth.make_tokens(layer, n, 1000 + i) for i in range(args.pool)]
     out = torch.empty_like(xs[0])
     k = cfg["k"]
@@ -106,6 +147,7 @@ def main():
 
     H = hip()
     nl = num_launches(bound[0].cfg, n)
+    names = KERNELS[nl]
     stream = torch.cuda.current_stream().cuda_stream
 
     def mk_events(count):
@@ -116,7 +158,7 @@ def main():
             evs.append(e.value)
         return evs
 
-    ev = None if args.no_trace else [mk_events(nl + 1) for _ in range(args.steps)]
+    ev = None if args.no_trace else [mk_events(2 * nl) for _ in range(args.steps)]
 
     calls = [bound[(args.warmup + i) % copies].prepare(
         xs[i % args.pool], out, idx=idx_all[i], stream=stream,
@@ -133,9 +175,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     us_per_call = wall / args.steps * 1e6
-    err = int(bound[0].workspace[128:132].view(torch.int32).item())
-    if err:
-        raise RuntimeError(f"device error word {err}: a workgroup wait expired")
+    if nl == 1:
+        err = int(bound[0].workspace[128:132].view(torch.int32).item())
+        if err:
+            raise RuntimeError(f"device error word {err}: a workgroup wait expired")
 
     # distinct experts per call -> algorithmic bytes
     idx_np = idx_all.cpu().numpy()
@@ -149,26 +192,46 @@ def main():
     bytes_dn = U * by["expert_down"] + sdn
     expert_bytes = bytes_gu + bytes_dn
     total_bytes = expert_bytes + by["router"]
+    Hd, I, Is = cfg["H"], cfg["I"], cfg["I_s"]
+    flops_gu = 2.0 * n * k * 2 * Hd * I + 2.0 * n * 2 * Hd * Is
+    flops_dn = 2.0 * n * k * Hd * I + 2.0 * n * Hd * Is
 
     per_kernel = {}
     roof = None
+    kernels_us = None
     if ev is not None:
         durs = np.zeros((args.steps, nl), np.float64)
         f = ctypes.c_float()
         for i in range(args.steps):
             for j in range(nl):
-                H.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(ev[i][j]),
-                                      ctypes.c_void_p(ev[i][j + 1]))
+                H.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(ev[i][2 * j]),
+                                      ctypes.c_void_p(ev[i][2 * j + 1]))
                 durs[i, j] = f.value * 1e3  # us
-        per_kernel = {KERNELS[j]: round(float(durs[:, j].mean()), 3) for j in range(nl)}
-        # one fused launch: its algorithmic bytes are the whole call's
-        d_us = durs.sum(axis=1)
-        achieved = float(total_bytes.sum() / (d_us.sum() * 1e-6) / 1e9)
-        roof = {"bound": "hbm", "kernel": "k_moe_decode", "achieved": round(achieved, 1),
+        per_kernel = {names[j]: round(float(durs[:, j].mean()), 3) for j in range(nl)}
+        kernels_us = float(durs.sum(axis=1).mean())
+        if nl == 1:
+            # one fused launch: its algorithmic bytes are the whole call's
+            dom, dom_bytes, dom_us = "k_moe_decode", total_bytes, durs[:, 0]
+        else:
+            dom, dom_bytes, dom_us = "k_g_gate_up", bytes_gu, durs[:, 3]
+        achieved = float(dom_bytes.sum() / (dom_us.sum() * 1e-6) / 1e9)
+        key = f"{dom}:{args.config}:N={n}:{accum}"
+        traffic = traffic_for(key)
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None,
-                "bytes_per_launch": float(total_bytes.mean()), "avg_launch_us": float(d_us.mean())}
-        experts_gbs = float(expert_bytes.sum() / (d_us.sum() * 1e-6) / 1e9)
+                "traffic": None if traffic is None else round(traffic),
+                "bytes_per_launch": float(dom_bytes.mean()), "avg_launch_us": float(dom_us.mean())}
+        if nl > 1:
+            gu_tf = flops_gu / (durs[:, 3].mean() * 1e-6) / 1e12
+            dn_tf = flops_dn / (durs[:, 4].mean() * 1e-6) / 1e12
+            dn_gbs = float(bytes_dn.sum() / (durs[:, 4].sum() * 1e-6) / 1e9)
+            roof["mfma"] = {"gate_up_tflops": round(gu_tf, 1), "down_tflops": round(dn_tf, 1),
+                            "peak_bf16_tflops": MFMA_BF16_PEAK_TFLOPS,
+                            "gate_up_util": round(gu_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                            "down_util": round(dn_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                            "flops_per_call": flops_gu + flops_dn}
+            roof["down_gbps"] = round(dn_gbs, 1)
+        experts_gbs = float(expert_bytes.sum() / (durs.sum() * 1e-6) / 1e9)
         for row in ev:
             for e in row:
                 H.hipEventDestroy(ctypes.c_void_p(e))
@@ -179,6 +242,7 @@ def main():
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(layer, xs, n, args.cpu_seconds)
 
+    path = "decode" if nl == 1 else "grouped"
     rec = {
         "metric": "MoE layer us/call + expert-weight HBM GB/s (% peak) at N=1,3,4 tokens",
         "value": round(us_per_call, 3),
@@ -194,12 +258,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.config} H={cfg['H']} I={cfg['I']} E={cfg['E']} "
                                f"k={k} I_s={cfg['I_s']} {cfg['routed_fmt']} N={n}",
-                   "n_tokens": n, "routed_format": cfg["routed_fmt"],
-                   "accum": args.accum or cfg["accum"], "weight_copies": copies,
-                   "token_batches": args.pool, "launch": "eager stream, one fused kernel per call"},
+                   "n_tokens": n, "routed_format": cfg["routed_fmt"], "path": path,
+                   "accum": accum, "weight_copies": copies, "token_batches": args.pool,
+                   "launch": f"eager stream, {nl} launch(es) per call"},
         "expert_weight_gbps_call": round(float(expert_bytes.mean() / (us_per_call * 1e-6) / 1e9), 1),
         "expert_weight_gbps_kernels": None if experts_gbs is None else round(experts_gbs, 1),
         "pct_hbm_peak_kernels": None if experts_gbs is None else round(100 * experts_gbs / HBM_PEAK_GBS, 2),
+        "kernels_us_per_call": None if kernels_us is None else round(kernels_us, 3),
         "distinct_experts_mean": float(U.mean()),
         "bytes_per_call_mean": float(total_bytes.mean()),
         "per_kernel_us": per_kernel,

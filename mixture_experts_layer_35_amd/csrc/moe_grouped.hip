@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kGThreads) void k_g_router(GroupedArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int e = rb * kGRowsPerWG + 32 * wave + 16 * t + 4 * (lane >> 4) + r;
-            if (e < a.E) a.zpart[((int64_t)s * a.N + t0 + j) * a.E + e] = acc[t][n][r];
+            if (e < a.E) a.zpart[((int64_t)(t0 + j) * a.E + e) * a.ksplit + s] = acc[t][n][r];
           }
         }
       }
@@ -85,17 +85,32 @@ __global__ __launch_bounds__(kGThreads) void k_g_topk(GroupedArgs a) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kGThreads / 64) + (threadIdx.x >> 6);
   if (t >= a.N) return;
-  float zv[4];
+  // sum the K-range partials of the lane's four logits in ascending range
+  // order, 16 ranges at a time so that 64 loads are in flight per lane
+  const int ks = a.ksplit;
+  float zv[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < ks; s0 += 16) {
+    float v[4][16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      const float* p = a.zpart + ((int64_t)t * a.E + e) * ks + s0;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[i][q] = (e < a.E && s0 + q < ks) ? p[q] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) zv[i] += v[i][q];
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    float z = -INFINITY;
     if (e < a.E) {
-      z = 0.f;
-      for (int s = 0; s < a.ksplit; ++s) z += a.zpart[((int64_t)s * a.N + t) * a.E + e];
-      if (a.out_logits) a.out_logits[(int64_t)t * a.E + e] = z;
+      if (a.out_logits) a.out_logits[(int64_t)t * a.E + e] = zv[i];
+    } else {
+      zv[i] = -INFINITY;
     }
-    zv[i] = z;
   }
   int my_e;
   float w;
@@ -118,13 +133,13 @@ __global__ __launch_bounds__(kGThreads) void k_g_topk(GroupedArgs a) {
 // Grouping: one workgroup of 1024 threads.
 // ---------------------------------------------------------------------------
 constexpr int kGroupThreads = 1024;
-
-constexpr int kPreBytes = 49152;  // LDS for word prefixes of one batch of experts
+constexpr int kMaskLdsWords = 8192;  // masks of up to 8192 words are copied to LDS
+constexpr int kPreBytes = 16384;     // LDS for word prefixes (one batch of experts)
 
 size_t grouped_group_lds(int E, int W) {
   (void)E;
   (void)W;
-  return (256 + 257) * 4 + kPreBytes;
+  return (256 + 257) * 4 + kPreBytes + kMaskLdsWords * 4;
 }
 
 __global__ __launch_bounds__(kGroupThreads) void k_g_group(GroupedArgs a) {
@@ -132,14 +147,20 @@ __global__ __launch_bounds__(kGroupThreads) void k_g_group(GroupedArgs a) {
   int* cnt = reinterpret_cast<int*>(g_lds);  // [256]
   int* base = cnt + 256;                     // [257]
   uint16_t* pre = reinterpret_cast<uint16_t*>(base + 257);  // [EB * W] word prefixes
+  uint32_t* mlds = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(pre) + kPreBytes);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nw = kGroupThreads / 64;
   const int E = a.E, W = a.W;
+  // the token masks, from LDS when they fit (one coalesced copy)
+  const bool staged = E * W <= kMaskLdsWords;
+  if (staged)
+    for (int i = tid; i < E * W; i += kGroupThreads) mlds[i] = a.mask[i];
+  const uint32_t* mk = staged ? mlds : a.mask;
+  __syncthreads();
   // tokens per expert
   for (int e = wave; e < E; e += nw) {
-    const uint32_t* mk = a.mask + (int64_t)e * W;
     int c = 0;
-    for (int i = lane; i < W; i += 64) c += __popc(mk[i]);
+    for (int i = lane; i < W; i += 64) c += __popc(mk[e * W + i]);
     c = (int)wave_sum_dpp((float)c);
     if (lane == 0) cnt[e] = c;
   }
@@ -201,11 +222,10 @@ __global__ __launch_bounds__(kGroupThreads) void k_g_group(GroupedArgs a) {
   for (int e0 = 0; e0 < E; e0 += eb_max) {
     const int e1 = min(E, e0 + eb_max);
     for (int e = e0 + wave; e < e1; e += nw) {
-      const uint32_t* mk = a.mask + (int64_t)e * W;
       int carry = 0;
       for (int i0 = 0; i0 < W; i0 += 64) {
         const int i = i0 + lane;
-        const int c = i < W ? __popc(mk[i]) : 0;
+        const int c = i < W ? __popc(mk[e * W + i]) : 0;
         int incl = c;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
@@ -221,7 +241,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_g_group(GroupedArgs a) {
       const int e = a.idx[s];
       if (e < e0 || e >= e1) continue;
       const int t = s / a.k;
-      const uint32_t wd = a.mask[(int64_t)e * W + (t >> 5)];
+      const uint32_t wd = mk[e * W + (t >> 5)];
       const int rank = pre[(e - e0) * W + (t >> 5)] + __popc(wd & ((1u << (t & 31)) - 1u));
       const int pos = base[e] + rank;
       a.perm_tok[pos] = t;

@@ -128,7 +128,7 @@ struct GroupedArgs {
   int gu_s, gu_r;   // gate+up: shared workgroups, workgroups per routed unit
   int dn_s, dn_r;   // down: same
   // workspace
-  float* zpart;      // [ksplit, N, E] partial router logits
+  float* zpart;      // [N, E, ksplit] partial router logits
   uint32_t* mask;    // [E, W] bit t of word t/32: token t routes to expert e
   int* idx;          // [N*k]
   float* wts;        // [N*k]
