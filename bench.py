@@ -59,6 +59,9 @@ def parse():
     p.add_argument("--accum", default=None, choices=[None, "slot", "atomic"])
     p.add_argument("--path", default="auto", choices=["auto", "decode", "grouped"])
     p.add_argument("--pool", type=int, default=64, help="distinct token batches")
+    p.add_argument("--copies", type=int, default=None,
+                   help="weight copies to rotate through (default: enough that a copy's "
+                        "bytes have left the 256 MB Infinity Cache before it is used again)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="budget of the oracle baseline (0 = skip)")
     p.add_argument("--no-trace", action="store_true", help="time without per-kernel events")
@@ -138,6 +141,8 @@ def main():
     # more than twice the Infinity Cache
     per_call_guess = min(cfg["E"], n * cfg["k"]) * by["expert"] + by["shared"]
     copies = max(1, min(32, math.ceil(2 * MALL_BYTES / max(1, per_call_guess)) + 1))
+    if args.copies:
+        copies = args.copies
     layers = [layer] + [synth.clone_weights(layer) for _ in range(copies - 1)]
     bound = [Layer(l, n, accum=accum, path=args.path) for l in layers]
     xs = [synth.make_tokens(layer, n, 1000 + i) for i in range(args.pool)]

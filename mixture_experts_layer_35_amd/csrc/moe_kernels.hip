@@ -118,10 +118,11 @@ __device__ __forceinline__ unsigned wg_signal(unsigned* p, unsigned* s_tmp, bool
   return *s_tmp;
 }
 
-// Add 1 to *p once every wave of the workgroup got here, without waiting for
-// the atomic to return.
-__device__ __forceinline__ void wg_signal_noret(unsigned* p) {
-  __syncthreads();
+// Add 1 to *p once every wave of the workgroup has issued its stores, without
+// waiting for them (or the add) to complete. The count is only a hint to
+// start reading: the readers check the tags of the words they read.
+__device__ __forceinline__ void wg_hint(unsigned* p) {
+  __builtin_amdgcn_s_barrier();
   if (threadIdx.x == 0)
     (void)__hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -260,10 +261,13 @@ __device__ __forceinline__ void stage_x(uint4* lds, const uint16_t* x, uint32_t 
   const uint4 z = make_uint4(0u, 0u, 0u, 0u);
   for (int i0 = threadIdx.x; i0 < total; i0 += kThreads * SB) {
     const int i1 = i0 + kThreads, i2 = i0 + 2 * kThreads, i3 = i0 + 3 * kThreads;
+    // explicit branches: a select of the two sources would become a
+    // generic-pointer load of a private copy of z
     const uint4 v0 = *src(i0);
-    const uint4 v1 = i1 < total ? *src(i1) : z;
-    const uint4 v2 = i2 < total ? *src(i2) : z;
-    const uint4 v3 = i3 < total ? *src(i3) : z;
+    uint4 v1 = z, v2 = z, v3 = z;
+    if (i1 < total) v1 = *src(i1);
+    if (i2 < total) v2 = *src(i2);
+    if (i3 < total) v3 = *src(i3);
     *dst(i0) = v0;
     if (i1 < total) *dst(i1) = v1;
     if (i2 < total) *dst(i2) = v2;
@@ -576,7 +580,7 @@ __device__ __forceinline__ void gate_up_phase(const DecodeArgs& a, int wg, uint4
       for (int t = 0; t < kNmax; ++t) slots[t] = t;
       gate_up_tile<FS, RPL>(a, a.sgate, a.sup, 0, wg, a.gs, a.I_s, smem, all, slots, a.a_shared,
                             tag);
-      wg_signal_noret(&a.unit_done[a.maxu * kLineWords]);
+      wg_hint(&a.unit_done[a.maxu * kLineWords]);
     }
     return;
   }
@@ -587,7 +591,7 @@ __device__ __forceinline__ void gate_up_phase(const DecodeArgs& a, int wg, uint4
   float wt[kNmax];
   if (!read_plan(a, unit, tag, e, slots, wt, mask, s_words)) return;
   gate_up_tile<FR, RPL>(a, a.gate, a.up, e, tile, a.gr, a.I, smem, mask, slots, a.a_routed, tag);
-  wg_signal_noret(&a.unit_done[unit * kLineWords]);
+  wg_hint(&a.unit_done[unit * kLineWords]);
 }
 
 // ---------------------------------------------------------------------------

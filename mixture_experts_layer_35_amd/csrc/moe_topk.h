@@ -61,30 +61,32 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
 // MoeLayer::forward_k3, step 2; "forward_batched.rs", the routing step). The
 // router logits sit four per lane: expert lane + 64 i in zv[i] (-inf past E).
 // Selection score: the logit (softmax) or sigmoid(logit) + correction bias
-// (sigmoid). k rounds of a wave argmax over (score, -expert) keys, so equal
-// scores go to the lower expert index. Weights: softmax over all E logits or
-// the plain sigmoid of the chosen logits (no bias), optionally divided by
-// their sum, then times the routed scaling factor. Lane j < k returns the
-// j-th choice and its weight.
+// (sigmoid). Keys order by (score, -expert), so equal scores go to the lower
+// expert index. Each lane sorts its four keys once (a five-exchange network);
+// each of the k rounds then takes the wave maximum of the lanes' head keys
+// and pops the winner's head. Weights: softmax over all E logits or the plain
+// sigmoid of the chosen logits (no bias), optionally divided by their sum,
+// then times the routed scaling factor. Lane j < k returns the j-th choice
+// and its weight.
 __device__ __forceinline__ void topk_wave(const float zv[4], int E, int k, int scoring,
                                           const float* bias, int renorm, float rsf, int lane,
                                           int& my_e, float& my_w) {
-  uint32_t khi[4], klo[4];
+  // key: hi = ordered score bits, lo = ~expert (larger lo = lower expert);
+  // an absent expert has hi = lo = 0, below every real key
+  uint32_t hi[4], lo[4];
+  float zz[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    if (e < E) {
-      float sc = zv[i];
-      if (scoring == 1) {
-        sc = 1.0f / (1.0f + expf(-zv[i]));
-        if (bias) sc += bias[e];
-      }
-      khi[i] = ordered_bits(sc);
-      klo[i] = 0xffffffffu - (uint32_t)e;
-    } else {
-      khi[i] = 0u;
-      klo[i] = 0u;
+    const bool in = e < E;
+    float sc = zv[i];
+    if (scoring == 1) {
+      sc = 1.0f / (1.0f + expf(-zv[i]));
+      if (bias && in) sc += bias[e];
     }
+    hi[i] = in ? ordered_bits(sc) : 0u;
+    lo[i] = in ? 0xffffffffu - (uint32_t)e : 0u;
+    zz[i] = zv[i];
   }
   float zmax = 0.f, zsum = 1.f;
   if (scoring == 0) {
@@ -95,44 +97,56 @@ __device__ __forceinline__ void topk_wave(const float zv[4], int E, int k, int s
       if (lane + 64 * i < E) p += expf(zv[i] - zmax);
     zsum = wave_sum_dpp(p);
   }
+  // sort the lane's four keys, largest first (branch-free exchanges)
+  auto cx = [&](int x, int y) {
+    const bool sw = hi[y] > hi[x] || (hi[y] == hi[x] && lo[y] > lo[x]);
+    const uint32_t h0 = hi[x], l0 = lo[x];
+    const float z0 = zz[x];
+    hi[x] = sw ? hi[y] : hi[x];
+    lo[x] = sw ? lo[y] : lo[x];
+    zz[x] = sw ? zz[y] : zz[x];
+    hi[y] = sw ? h0 : hi[y];
+    lo[y] = sw ? l0 : lo[y];
+    zz[y] = sw ? z0 : zz[y];
+  };
+  cx(0, 1);
+  cx(2, 3);
+  cx(0, 2);
+  cx(1, 3);
+  cx(1, 2);
   my_e = 0;
   float my_z = 0.f;
   for (int j = 0; j < k; ++j) {
-    uint32_t bh = khi[0], bl = klo[0];
-#pragma unroll
-    for (int i = 1; i < 4; ++i) {
-      if (khi[i] > bh || (khi[i] == bh && klo[i] > bl)) {
-        bh = khi[i];
-        bl = klo[i];
-      }
-    }
-    // the largest score; its lane's key when it is unique, else the largest
-    // key among the tied lanes
-    const uint32_t mh = wave_max_u32(bh);
-    const unsigned long long tied = __ballot(bh == mh);
+    // the largest head score; its lane when unique, else the largest key
+    // among the tied heads
+    const uint32_t mh = wave_max_u32(hi[0]);
+    const unsigned long long tied = __ballot(hi[0] == mh);
+    int wl;
     uint32_t ml;
-    if (__popcll(tied) == 1)
-      ml = (uint32_t)__builtin_amdgcn_readlane((int)bl, __ffsll((long long)tied) - 1);
-    else
-      ml = wave_max_u32(bh == mh ? bl : 0u);
-    const int e = (int)(0xffffffffu - ml);
-    const int slot = e >> 6;
-    float zloc = zv[0];
-#pragma unroll
-    for (int i = 1; i < 4; ++i)
-      if (slot == i) zloc = zv[i];
-    const float zsel = __builtin_bit_cast(
-        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, zloc), e & 63));
-    if (lane == (e & 63)) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (slot == i) {
-          khi[i] = 0u;
-          klo[i] = 0u;
-        }
+    if (__popcll(tied) == 1) {
+      wl = __ffsll((long long)tied) - 1;
+      ml = (uint32_t)__builtin_amdgcn_readlane((int)lo[0], wl);
+    } else {
+      ml = wave_max_u32(hi[0] == mh ? lo[0] : 0u);
+      wl = __ffsll((long long)__ballot(hi[0] == mh && lo[0] == ml)) - 1;
+    }
+    const float zsel =
+        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, zz[0]), wl));
+    if (lane == wl) {  // pop the winner's head
+      hi[0] = hi[1];
+      lo[0] = lo[1];
+      zz[0] = zz[1];
+      hi[1] = hi[2];
+      lo[1] = lo[2];
+      zz[1] = zz[2];
+      hi[2] = hi[3];
+      lo[2] = lo[3];
+      zz[2] = zz[3];
+      hi[3] = 0u;
+      lo[3] = 0u;
     }
     if (lane == j) {
-      my_e = e;
+      my_e = (int)(0xffffffffu - ml);
       my_z = zsel;
     }
   }
