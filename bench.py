@@ -14,8 +14,8 @@ cores as a reference point.
 
 Default workload: the Qwen3-30B-A3B-shaped MXFP4 layer at N = 1 token (decode
 path, one fused kernel). --config grouped_fp8_h4096 / prefill_bf16_h4096 run
-the grouped path (six launches: router, top-k, grouping, gate+up, down,
-combine).
+the grouped path (five launches: router, top-k with the grouping, gate+up,
+down, combine).
 """
 
 import argparse
@@ -35,7 +35,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
 MALL_BYTES = 256 << 20
 KERNELS = {1: ["k_moe_decode"],
-           6: ["k_g_router", "k_g_topk", "k_g_group", "k_g_gate_up", "k_g_down", "k_g_combine"]}
+           5: ["k_g_router", "k_g_topk", "k_g_gate_up", "k_g_down", "k_g_combine"]}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
@@ -218,7 +218,7 @@ def main():
             # one fused launch: its algorithmic bytes are the whole call's
             dom, dom_bytes, dom_us = "k_moe_decode", total_bytes, durs[:, 0]
         else:
-            dom, dom_bytes, dom_us = "k_g_gate_up", bytes_gu, durs[:, 3]
+            dom, dom_bytes, dom_us = "k_g_gate_up", bytes_gu, durs[:, 2]
         achieved = float(dom_bytes.sum() / (dom_us.sum() * 1e-6) / 1e9)
         key = f"{dom}:{args.config}:N={n}:{accum}"
         traffic = traffic_for(key)
@@ -227,9 +227,9 @@ def main():
                 "traffic": None if traffic is None else round(traffic),
                 "bytes_per_launch": float(dom_bytes.mean()), "avg_launch_us": float(dom_us.mean())}
         if nl > 1:
-            gu_tf = flops_gu / (durs[:, 3].mean() * 1e-6) / 1e12
-            dn_tf = flops_dn / (durs[:, 4].mean() * 1e-6) / 1e12
-            dn_gbs = float(bytes_dn.sum() / (durs[:, 4].sum() * 1e-6) / 1e9)
+            gu_tf = flops_gu / (durs[:, 2].mean() * 1e-6) / 1e12
+            dn_tf = flops_dn / (durs[:, 3].mean() * 1e-6) / 1e12
+            dn_gbs = float(bytes_dn.sum() / (durs[:, 3].sum() * 1e-6) / 1e9)
             roof["mfma"] = {"gate_up_tflops": round(gu_tf, 1), "down_tflops": round(dn_tf, 1),
                             "peak_bf16_tflops": MFMA_BF16_PEAK_TFLOPS,
                             "gate_up_util": round(gu_tf / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -160,9 +160,9 @@ moe_status moe_validate(const moe_cfg* cfg, const moe_router* router,
                         int32_t n_tokens, size_t workspace_bytes);
 
 /* Number of kernel launches moe_forward makes for this call (for moe_trace):
- * 1 on the decode path (one fused kernel); 6 on the grouped path (router,
- * top-k, grouping, gate+up, down, combine). Returns -1 if the call is
- * invalid. */
+ * 1 on the decode path (one fused kernel); 5 on the grouped path (router,
+ * top-k with the grouping, gate+up, down, combine). Returns -1 if the call
+ * is invalid. */
 int32_t moe_num_launches(const moe_cfg* cfg, int32_t n_tokens);
 
 /* Where a grouped-path call keeps the result of its grouping step

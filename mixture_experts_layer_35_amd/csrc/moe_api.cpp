@@ -221,7 +221,7 @@ struct Layout {
   size_t unit_done = 0, blend_ctr = 0, acc = 0;
   size_t a_routed = 0, a_shared = 0, dbuf = 0;
   // grouped
-  size_t g_zpart = 0, g_mask = 0, g_idx = 0, g_wts = 0, g_info = 0, g_ptok = 0, g_pslot = 0,
+  size_t g_zpart = 0, g_ticket = 0, g_mask = 0, g_idx = 0, g_wts = 0, g_info = 0, g_ptok = 0, g_pslot = 0,
          g_inv = 0, g_aperm = 0, g_ashared = 0, g_dperm = 0, g_dshared = 0, g_acc = 0;
 };
 
@@ -247,6 +247,7 @@ Layout layout(const moe_cfg* c, int32_t n, int path) {
   } else {
     const GPlan g = gplan(c, n);
     L.g_mask = take(E * g.W * 4);
+    L.g_ticket = take(4);
     L.g_idx = take(N * k * 4);
     L.g_wts = take(N * k * 4);
     L.g_info = take(sizeof(moe::GroupInfo));
@@ -360,6 +361,7 @@ moe_status forward_grouped(const moe_cfg* cfg, const moe_router* router,
   const Layout L = layout(cfg, n, MOE_PATH_GROUPED);
   a.zpart = reinterpret_cast<float*>(base + L.g_zpart);
   a.mask = reinterpret_cast<uint32_t*>(base + L.g_mask);
+  a.ticket = reinterpret_cast<unsigned*>(base + L.g_ticket);
   a.idx = reinterpret_cast<int*>(base + L.g_idx);
   a.wts = reinterpret_cast<float*>(base + L.g_wts);
   a.info = reinterpret_cast<moe::GroupInfo*>(base + L.g_info);

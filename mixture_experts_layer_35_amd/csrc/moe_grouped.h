@@ -449,7 +449,7 @@ inline size_t gemm_lds(int nt) { return (size_t)2 * 16 * nt * 256; }
 hipError_t launch_one(const void* fn, int blocks, int threads, size_t lds, hipStream_t st,
                       const GroupedArgs& a, hipEvent_t* ev, int i);
 
-// Gate+up and down launches (launches 3 and 4 of the call) for routed
+// Gate+up and down launches (launches 2 and 3 of the call) for routed
 // format FR; defined in one translation unit per format.
 template <int FR>
 hipError_t launch_experts(const GroupedArgs& a, int fs, hipStream_t st, hipEvent_t* ev);
@@ -465,10 +465,10 @@ hipError_t launch_experts<FMT_NVFP4>(const GroupedArgs&, int, hipStream_t, hipEv
 template <int FR, int FS, int NT>
 hipError_t launch_experts_t(const GroupedArgs& a, hipStream_t st, hipEvent_t* ev) {
   hipError_t err = launch_one(reinterpret_cast<const void*>(&k_g_gate_up<FR, FS, NT>),
-                              a.gu_s + a.maxu * a.gu_r, kGThreads, gemm_lds(NT), st, a, ev, 3);
+                              a.gu_s + a.maxu * a.gu_r, kGThreads, gemm_lds(NT), st, a, ev, 2);
   if (err != hipSuccess) return err;
   return launch_one(reinterpret_cast<const void*>(&k_g_down<FR, FS, NT>),
-                    a.dn_s + a.maxu * a.dn_r, kGThreads, gemm_lds(NT), st, a, ev, 4);
+                    a.dn_s + a.maxu * a.dn_r, kGThreads, gemm_lds(NT), st, a, ev, 3);
 }
 
 template <int FR, int FS>

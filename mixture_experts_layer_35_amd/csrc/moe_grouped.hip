@@ -3,18 +3,19 @@
 // The batch is sorted by expert so that each selected expert's weights are
 // streamed once for all of the rows routed to it ("forward_batched.rs",
 // MoeLayer::forward_batched: one router GEMM over the batch, then per-expert
-// grouped work). Six stream-ordered launches:
+// grouped work). Five stream-ordered launches:
 //
 //   router   z = x Wr^T as an MFMA GEMM, H split into ranges whose partial
 //            logits are summed in a fixed order by the next kernel; also
 //            clears the token masks
 //   top-k    one wave per token: logits, top-k (shared with the decode path),
-//            routing weights; sets bit t of mask[e] for each chosen e
-//   group    one workgroup: tokens per expert from the masks, counts padded
-//            to 16 rows, exclusive scan, and the stable permutation of the
-//            N*k slots by (expert, token); each slot's rank is the number of
-//            earlier tokens of the same expert (a token picks an expert at
-//            most once), read off the mask words with popcounts
+//            routing weights; sets bit t of mask[e] for each chosen e. The
+//            last workgroup to finish then groups: tokens per expert from
+//            the masks, counts padded to 16 rows, exclusive scan, and the
+//            stable permutation of the N*k slots by (expert, token); each
+//            slot's rank is the number of earlier tokens of the same expert
+//            (a token picks an expert at most once), read off the mask words
+//            with popcounts
 //   gate+up  one workgroup per (unit, 64 output features): g and u for the
 //            unit's rows as two 16x16 tiles per wave, a = silu(g) * u in BF16
 //            into the permuted activation buffer; the shared expert is one
@@ -43,6 +44,7 @@ __global__ __launch_bounds__(kGThreads) void k_g_router(GroupedArgs a) {
   // clear the token masks (the top-k kernel, launched next, sets them)
   for (int i = blockIdx.x * kGThreads + tid; i < a.E * a.W; i += gridDim.x * kGThreads)
     a.mask[i] = 0u;
+  if (blockIdx.x == 0 && tid == 0) *a.ticket = 0u;
   const int s = blockIdx.x % a.ksplit;
   const int tg = (blockIdx.x / a.ksplit) % a.r_tg;
   const int rb = blockIdx.x / (a.ksplit * a.r_tg);
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(kGThreads) void k_g_router(GroupedArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int e = rb * kGRowsPerWG + 32 * wave + 16 * t + 4 * (lane >> 4) + r;
-            if (e < a.E) a.zpart[((int64_t)(t0 + j) * a.E + e) * a.ksplit + s] = acc[t][n][r];
+            if (e < a.E) a.zpart[((int64_t)(t0 + j) * a.ksplit + s) * a.E + e] = acc[t][n][r];
           }
         }
       }
@@ -79,60 +81,89 @@ __global__ __launch_bounds__(kGThreads) void k_g_router(GroupedArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Top-k: one wave per token.
+// Top-k: one wave per token; the last workgroup to finish then groups the
+// slots by expert (group_slots below).
 // ---------------------------------------------------------------------------
+__device__ void group_slots(const GroupedArgs& a, uint4* lds);
+
+// Device-coherent (agent-scope, relaxed) accesses for what the grouping
+// workgroup reads from the other top-k workgroups of the same launch.
+__device__ __forceinline__ int ld_dev(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __global__ __launch_bounds__(kGThreads) void k_g_topk(GroupedArgs a) {
+  extern __shared__ uint4 g_lds[];
+  __shared__ int s_last;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kGThreads / 64) + (threadIdx.x >> 6);
-  if (t >= a.N) return;
-  // sum the K-range partials of the lane's four logits in ascending range
-  // order, 16 ranges at a time so that 64 loads are in flight per lane
-  const int ks = a.ksplit;
-  float zv[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < ks; s0 += 16) {
-    float v[4][16];
+  if (t < a.N) {
+    // sum the K-range partials of the lane's four logits in ascending range
+    // order; lanes read consecutive experts, 16 ranges at a time
+    const int ks = a.ksplit;
+    float zv[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < ks; s0 += 16) {
+      float v[4][16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const float* p = a.zpart + ((int64_t)t * ks + s0 + q) * a.E;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = lane + 64 * i;
+          v[i][q] = (e < a.E && s0 + q < ks) ? p[e] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) zv[i] += v[i][q];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
-      const float* p = a.zpart + ((int64_t)t * a.E + e) * ks + s0;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) v[i][q] = (e < a.E && s0 + q < ks) ? p[q] : 0.f;
+      if (e < a.E) {
+        if (a.out_logits) a.out_logits[(int64_t)t * a.E + e] = zv[i];
+      } else {
+        zv[i] = -INFINITY;
+      }
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) zv[i] += v[i][q];
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    if (e < a.E) {
-      if (a.out_logits) a.out_logits[(int64_t)t * a.E + e] = zv[i];
-    } else {
-      zv[i] = -INFINITY;
+    int my_e;
+    float w;
+    topk_wave(zv, a.E, a.k, a.scoring, a.router_bias, a.renorm, a.rsf, lane, my_e, w);
+    if (lane < a.k) {
+      const int sl = t * a.k + lane;
+      st_dev(a.idx + sl, my_e);
+      a.wts[sl] = w;
+      if (a.out_idx) a.out_idx[sl] = (uint32_t)my_e;
+      if (a.out_w) a.out_w[sl] = w;
+      atomicOr(a.mask + (int64_t)my_e * a.W + (t >> 5), 1u << (t & 31));
+    }
+    if (a.atomic) {
+      float4* row = reinterpret_cast<float4*>(a.acc + (int64_t)t * a.H);
+      for (int i = lane; i < a.H / 4; i += 64) row[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
-  int my_e;
-  float w;
-  topk_wave(zv, a.E, a.k, a.scoring, a.router_bias, a.renorm, a.rsf, lane, my_e, w);
-  if (lane < a.k) {
-    const int sl = t * a.k + lane;
-    a.idx[sl] = my_e;
-    a.wts[sl] = w;
-    if (a.out_idx) a.out_idx[sl] = (uint32_t)my_e;
-    if (a.out_w) a.out_w[sl] = w;
-    atomicOr(a.mask + (int64_t)my_e * a.W + (t >> 5), 1u << (t & 31));
-  }
-  if (a.atomic) {
-    float4* row = reinterpret_cast<float4*>(a.acc + (int64_t)t * a.H);
-    for (int i = lane; i < a.H / 4; i += 64) row[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  // the last workgroup to arrive groups the slots. idx is written with
+  // device-coherent stores and mask with device atomics; each workgroup waits
+  // for its own to complete before taking its ticket, and the last one reads
+  // them with device-coherent loads (no cache-wide fence either way)
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(a.ticket, 1u) == gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;
+  group_slots(a, g_lds);
 }
 
 // ---------------------------------------------------------------------------
-// Grouping: one workgroup of 1024 threads.
+// Grouping, by one workgroup (the last top-k workgroup).
 // ---------------------------------------------------------------------------
-constexpr int kGroupThreads = 1024;
 constexpr int kMaskLdsWords = 8192;  // masks of up to 8192 words are copied to LDS
 constexpr int kPreBytes = 16384;     // LDS for word prefixes (one batch of experts)
 
@@ -142,27 +173,25 @@ size_t grouped_group_lds(int E, int W) {
   return (256 + 257) * 4 + kPreBytes + kMaskLdsWords * 4;
 }
 
-__global__ __launch_bounds__(kGroupThreads) void k_g_group(GroupedArgs a) {
-  extern __shared__ uint4 g_lds[];
+__device__ void group_slots(const GroupedArgs& a, uint4* g_lds) {
+  constexpr int kT = kGThreads;  // one thread per expert (E <= 256)
   int* cnt = reinterpret_cast<int*>(g_lds);  // [256]
   int* base = cnt + 256;                     // [257]
   uint16_t* pre = reinterpret_cast<uint16_t*>(base + 257);  // [EB * W] word prefixes
   uint32_t* mlds = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(pre) + kPreBytes);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int nw = kGroupThreads / 64;
   const int E = a.E, W = a.W;
   // the token masks, from LDS when they fit (one coalesced copy)
   const bool staged = E * W <= kMaskLdsWords;
   if (staged)
-    for (int i = tid; i < E * W; i += kGroupThreads) mlds[i] = a.mask[i];
-  const uint32_t* mk = staged ? mlds : a.mask;
+    for (int i = tid; i < E * W; i += kT) mlds[i] = ld_dev(a.mask + i);
   __syncthreads();
-  // tokens per expert
-  for (int e = wave; e < E; e += nw) {
+  auto mword = [&](int i) { return staged ? mlds[i] : ld_dev(a.mask + i); };
+  // tokens per expert: thread e sums its mask words
+  if (tid < E) {
     int c = 0;
-    for (int i = lane; i < W; i += 64) c += __popc(mk[e * W + i]);
-    c = (int)wave_sum_dpp((float)c);
-    if (lane == 0) cnt[e] = c;
+    for (int i = 0; i < W; ++i) c += __popc(mword(tid * W + i));
+    cnt[tid] = c;
   }
   __syncthreads();
   // padded exclusive scan and the unit list (wave 0, four experts per lane)
@@ -210,43 +239,47 @@ __global__ __launch_bounds__(kGroupThreads) void k_g_group(GroupedArgs a) {
   }
   __syncthreads();
   // padding rows
-  for (int e = tid; e < E; e += kGroupThreads) {
-    for (int r = base[e] + cnt[e]; r < base[e + 1]; ++r) {
+  if (tid < E) {
+    for (int r = base[tid] + cnt[tid]; r < base[tid + 1]; ++r) {
       a.perm_tok[r] = -1;
       a.perm_slot[r] = -1;
     }
   }
-  // ranks, in batches of experts whose word prefixes fit in LDS
+  // ranks, in batches of experts whose word prefixes fit in LDS: thread e
+  // writes the running popcount before each of its words
   const int eb_max = kPreBytes / (2 * W);
   const int nslots = a.N * a.k;
   for (int e0 = 0; e0 < E; e0 += eb_max) {
     const int e1 = min(E, e0 + eb_max);
-    for (int e = e0 + wave; e < e1; e += nw) {
-      int carry = 0;
-      for (int i0 = 0; i0 < W; i0 += 64) {
-        const int i = i0 + lane;
-        const int c = i < W ? __popc(mk[e * W + i]) : 0;
-        int incl = c;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const int o = __shfl_up(incl, d, 64);
-          if (lane >= d) incl += o;
-        }
-        if (i < W) pre[(e - e0) * W + i] = (uint16_t)(carry + incl - c);
-        carry += __shfl(incl, 63, 64);
+    if (tid >= e0 && tid < e1) {
+      int run = 0;
+      for (int i = 0; i < W; ++i) {
+        pre[(tid - e0) * W + i] = (uint16_t)run;
+        run += __popc(mword(tid * W + i));
       }
     }
     __syncthreads();
-    for (int s = tid; s < nslots; s += kGroupThreads) {
-      const int e = a.idx[s];
-      if (e < e0 || e >= e1) continue;
-      const int t = s / a.k;
-      const uint32_t wd = mk[e * W + (t >> 5)];
-      const int rank = pre[(e - e0) * W + (t >> 5)] + __popc(wd & ((1u << (t & 31)) - 1u));
-      const int pos = base[e] + rank;
-      a.perm_tok[pos] = t;
-      a.perm_slot[pos] = s;
-      a.inv[s] = pos;
+    // eight slots per thread per pass, their loads issued together
+    for (int s0 = 0; s0 < nslots; s0 += 8 * kT) {
+      int ev[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int sl = s0 + q * kT + tid;
+        ev[q] = sl < nslots ? ld_dev(a.idx + sl) : -1;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int sl = s0 + q * kT + tid;
+        const int e = ev[q];
+        if (e < e0 || e >= e1) continue;
+        const int t = sl / a.k;
+        const uint32_t wd = mword(e * W + (t >> 5));
+        const int rank = pre[(e - e0) * W + (t >> 5)] + __popc(wd & ((1u << (t & 31)) - 1u));
+        const int pos = base[e] + rank;
+        a.perm_tok[pos] = t;
+        a.perm_slot[pos] = sl;
+        a.inv[sl] = pos;
+      }
     }
     __syncthreads();
   }
@@ -318,11 +351,8 @@ hipError_t launch_grouped(const GroupedArgs& a, int fr, int fs, hipStream_t st, 
   hipError_t err = launch_one(router_fn(a.nt), a.r_rb * a.r_tg * a.ksplit, kGThreads,
                               gemm_lds(a.nt), st, a, ev, 0);
   if (err != hipSuccess) return err;
-  err = launch_one(reinterpret_cast<const void*>(&k_g_topk), (a.N + 3) / 4, kGThreads, 0, st, a,
-                   ev, 1);
-  if (err != hipSuccess) return err;
-  err = launch_one(reinterpret_cast<const void*>(&k_g_group), 1, kGroupThreads,
-                   grouped_group_lds(a.E, a.W), st, a, ev, 2);
+  err = launch_one(reinterpret_cast<const void*>(&k_g_topk), (a.N + 3) / 4, kGThreads,
+                   grouped_group_lds(a.E, a.W), st, a, ev, 1);
   if (err != hipSuccess) return err;
   switch (fr) {
     case FMT_BF16: err = launch_experts<FMT_BF16>(a, fs, st, ev); break;
@@ -334,7 +364,7 @@ hipError_t launch_grouped(const GroupedArgs& a, int fr, int fs, hipStream_t st, 
   if (err != hipSuccess) return err;
   const int64_t quads = (int64_t)a.N * (a.H / 4);
   return launch_one(reinterpret_cast<const void*>(&k_g_combine),
-                    (int)((quads + kGThreads - 1) / kGThreads), kGThreads, 0, st, a, ev, 5);
+                    (int)((quads + kGThreads - 1) / kGThreads), kGThreads, 0, st, a, ev, 4);
 }
 
 }  // namespace moe

@@ -98,7 +98,7 @@ struct DecodeArgs {
 // ---------------------------------------------------------------------------
 constexpr int kGKC = 128;         // K columns per staged activation chunk
 constexpr int kGRowsPerWG = 128;  // weight rows per workgroup (4 waves x 2 tiles x 16)
-constexpr int kGLaunches = 6;     // router, top-k, group, gate+up, down, combine
+constexpr int kGLaunches = 5;     // router, top-k (+ grouping), gate+up, down, combine
 
 // Result of the grouping step, read by the expert kernels.
 struct GroupInfo {
@@ -128,7 +128,8 @@ struct GroupedArgs {
   int gu_s, gu_r;   // gate+up: shared workgroups, workgroups per routed unit
   int dn_s, dn_r;   // down: same
   // workspace
-  float* zpart;      // [N, E, ksplit] partial router logits
+  float* zpart;      // [N, ksplit, E] partial router logits
+  unsigned* ticket;  // top-k workgroups finished (zeroed by the router kernel)
   uint32_t* mask;    // [E, W] bit t of word t/32: token t routes to expert e
   int* idx;          // [N*k]
   float* wts;        // [N*k]

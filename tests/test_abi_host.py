@@ -166,9 +166,9 @@ def test_decode_token_limit_and_path_choice():
     c.path = B.PATH["auto"]
     assert B.validate(c, r, ex, sh, 16, 1 << 40) == B.MOE_OK
     assert B.num_launches(c, 4) == 1      # decode: one fused kernel
-    assert B.num_launches(c, 16) == 6     # grouped: router, top-k, group, gate+up, down, combine
+    assert B.num_launches(c, 16) == 5     # grouped: router, top-k + grouping, gate+up, down, combine
     c.path = B.PATH["grouped"]
-    assert B.num_launches(c, 1) == 6
+    assert B.num_launches(c, 1) == 5
     assert B.validate(c, r, ex, sh, 1, 1 << 40) == B.MOE_OK
 
 
