@@ -45,7 +45,13 @@ Readings where the pages are silent (each also listed in the design notes):
   R9  E4M3 is OCP E4M3FN (no infinities, S.1111.111 is NaN, max 448);
   R10 NVFP4 carries one FP32 tensor scale per expert per projection;
   R11 FP8 weights carry one FP32 scale per output row;
-  R12 the shared expert is added with gate 1 (no shared-expert gate).
+  R12 the shared expert is added with gate 1 when the layer has no
+      shared-expert gate; with a gate vector w_sg it is added with weight
+      sigmoid(x . w_sg) per token (the gated blend);
+  R13 an expert-parallel share holds the experts of one index range; routing
+      stays global, slots whose expert is outside the range add nothing, and
+      the shared expert is left to the caller, who adds it once after summing
+      the shares.
 """
 
 from __future__ import annotations
@@ -55,7 +61,7 @@ import numpy as np
 __all__ = [
     "e2m1_to_f64", "e8m0_to_f64", "e4m3fn_to_f64", "bf16_to_f64",
     "unpack_fp4", "dequant", "router_logits", "selection_scores", "route",
-    "silu", "swiglu_expert", "moe_forward", "group_slots", "FORMATS",
+    "silu", "swiglu_expert", "moe_forward", "group_slots", "shared_gate_weight", "FORMATS",
 ]
 
 FORMATS = ("bf16", "fp8_rowscale", "mxfp4", "nvfp4")
@@ -256,7 +262,20 @@ def swiglu_expert(wg: np.ndarray, wu: np.ndarray, wd: np.ndarray, xt: np.ndarray
     return g, u, a, d
 
 
-def moe_forward(cfg: dict, layer: dict, x_bits, rows=None) -> dict:
+def shared_gate_weight(x: np.ndarray, w_sg) -> np.ndarray:
+    """Per-token weight of the shared expert ("forward_k3.rs", the EP
+    all-reduce block: without a shared-expert gate weight the shared output is
+    added by a residual add, with one it goes through the batched blend with
+    a sigmoid gate): gamma[t] = sigmoid(x[t] . w_sg), or 1 without a gate
+    (reading R12)."""
+    x = np.asarray(x, np.float64)
+    if w_sg is None:
+        return np.ones(x.shape[0])
+    g = x @ np.asarray(w_sg, np.float64)
+    return 1.0 / (1.0 + np.exp(-g))
+
+
+def moe_forward(cfg: dict, layer: dict, x_bits, rows=None, expert_range=None) -> dict:
     """The whole layer for N tokens, in float64.
 
     ``cfg`` keys: H, I, E, k, I_s, scoring ('softmax' | 'sigmoid'), renorm,
@@ -265,8 +284,11 @@ def moe_forward(cfg: dict, layer: dict, x_bits, rows=None) -> dict:
     each projection a dict as taken by :func:`dequant`. ``x_bits`` is the BF16
     bit pattern of the [N, H] input. ``rows`` optionally restricts the output
     to those hidden rows (the down projections then use only those rows).
+    ``expert_range`` = (lo, hi) computes one expert-parallel share instead
+    (reading R13): only slots with lo <= idx < hi contribute, the layer's
+    ``experts`` hold experts lo..hi-1 only, and there is no shared term.
 
-    y[t] = sum_j w[t, j] * d_{idx[t, j]}(x_t) + s(x_t)   (reading R12)
+    y[t] = sum_j w[t, j] * d_{idx[t, j]}(x_t) + gamma[t] * s(x_t)   (R12)
     """
     x = bf16_to_f64(np.asarray(x_bits))
     n, h = x.shape
@@ -283,9 +305,12 @@ def moe_forward(cfg: dict, layer: dict, x_bits, rows=None) -> dict:
     a_slots = np.zeros((n, k, cfg["I"]), dtype=np.float64)
     d_slots = np.zeros((n, k, out_rows.size), dtype=np.float64)
     # one expert's weights at a time (dequantised once for all of its slots)
+    lo, hi = (0, cfg["E"]) if expert_range is None else expert_range
     for e in np.unique(idx):
-        wg, wu = dequant(ex["gate"], int(e)), dequant(ex["up"], int(e))
-        wd = dequant(ex["down"], int(e), rows=out_rows)
+        if not lo <= e < hi:
+            continue  # another share's expert: this share adds nothing for it
+        wg, wu = dequant(ex["gate"], int(e) - lo), dequant(ex["up"], int(e) - lo)
+        wd = dequant(ex["down"], int(e) - lo, rows=out_rows)
         ts, js = np.nonzero(idx == e)
         _, _, a, d = swiglu_expert(wg, wu, wd, x[ts])
         a_slots[ts, js] = a
@@ -294,15 +319,18 @@ def moe_forward(cfg: dict, layer: dict, x_bits, rows=None) -> dict:
     for j in range(k):
         y += w[:, j:j + 1] * d_slots[:, j]
     s_out = None
-    if layer.get("shared") is not None and cfg.get("I_s", 0) > 0:
+    gamma = None
+    if expert_range is None and layer.get("shared") is not None and cfg.get("I_s", 0) > 0:
         sh = layer["shared"]
         wg = dequant(sh["gate"], 0)
         wu = dequant(sh["up"], 0)
         wd = dequant(sh["down"], 0, rows=out_rows)
         _, _, _, s_out = swiglu_expert(wg, wu, wd, x)
-        y = y + s_out
+        gamma = shared_gate_weight(x, None if layer["router"].get("shared_gate") is None
+                                   else bf16_to_f64(layer["router"]["shared_gate"]))
+        y = y + gamma[:, None] * s_out
     return {"y": y, "z": z, "idx": idx, "w": w, "a": a_slots,
-            "shared": s_out, "rows": out_rows}
+            "shared": s_out, "gamma": gamma, "rows": out_rows}
 
 
 # --------------------------------------------------------------------------

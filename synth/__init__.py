@@ -63,7 +63,7 @@ CONFIGS = {
                                accum="slot"),
 }
 
-_TENSOR_IDS = {"router": 1, "bias": 2, "gate": 3, "up": 4, "down": 5,
+_TENSOR_IDS = {"router": 1, "bias": 2, "gate": 3, "up": 4, "down": 5, "shared_gate": 11,
                "sgate": 6, "sup": 7, "sdown": 8, "x": 9, "zipf": 10}
 
 
@@ -195,7 +195,12 @@ def make_layer(name_or_cfg, device="cpu") -> dict:
         gz = _gen("cpu", cfg["cfg_id"], _TENSOR_IDS["zipf"])
         ranks = torch.randperm(E, generator=gz).to(torch.float64) + 1.0
         wr[:, H - 1] = (-cfg["zipf"] * torch.log(ranks)).to(wr.dtype).to(device)
-    router = {"weight": wr.to(torch.bfloat16).contiguous(), "bias": None}
+    router = {"weight": wr.to(torch.bfloat16).contiguous(), "bias": None, "shared_gate": None}
+    if cfg.get("shared_gate") and I_s > 0:
+        # the shared-expert gate vector, N(0, 1/sqrt(H)) like a router row
+        gg = _gen(device, cfg["cfg_id"], _TENSOR_IDS["shared_gate"])
+        router["shared_gate"] = (torch.randn((H,), generator=gg, device=device)
+                                 / math.sqrt(H)).to(torch.bfloat16).contiguous()
     if cfg.get("bias_std"):
         gb = _gen(device, cfg["cfg_id"], _TENSOR_IDS["bias"])
         router["bias"] = (torch.randn((E,), generator=gb, device=device)
@@ -268,7 +273,8 @@ def as_numpy(layer: dict) -> dict:
         return {k: (_np(v) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
     out = {"cfg": dict(layer["cfg"]),
            "router": {"weight": _np(layer["router"]["weight"]),
-                      "bias": _np(layer["router"]["bias"])},
+                      "bias": _np(layer["router"]["bias"]),
+                      "shared_gate": _np(layer["router"].get("shared_gate"))},
            "experts": {k: proj(v) for k, v in layer["experts"].items()},
            "shared": None}
     if layer["shared"] is not None:
@@ -310,6 +316,8 @@ def layer_bytes(layer: dict) -> dict:
         b_s = sum(projection_bytes(layer["shared"][k]) for k in ("gate", "up", "down"))
     r = layer["router"]
     b_r = r["weight"].numel() * 2 + (0 if r["bias"] is None else r["bias"].numel() * 4)
+    if r.get("shared_gate") is not None:
+        b_r += r["shared_gate"].numel() * 2
     b_e_gu = sum(projection_bytes(ex[k]) for k in ("gate", "up"))
     return {"expert": b_e, "expert_gate_up": b_e_gu, "expert_down": b_e - b_e_gu,
             "shared": b_s, "router": b_r}

@@ -234,3 +234,89 @@ def test_layer_matches_pure_python_brute_force(fmt, shared_fmt, scoring):
     got = moe_forward(npl["cfg"], npl, _bf16_bits(x))["y"]
     want = _brute_layer(layer, x)
     np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-13)
+
+
+# ---- shared-expert gate and expert-parallel shares ----------------------
+
+def test_shared_gate_weight_closed_form():
+    from oracle import shared_gate_weight
+    x = np.array([[0.5, -1.0, 2.0], [0.0, 0.0, 0.0]])
+    w = np.array([1.0, 0.25, -0.125])
+    g = shared_gate_weight(x, w)
+    dots = [0.5 * 1.0 + (-1.0) * 0.25 + 2.0 * (-0.125), 0.0]
+    for t in range(2):
+        assert math.isclose(g[t], 1.0 / (1.0 + math.exp(-dots[t])), rel_tol=1e-15)
+    assert np.array_equal(shared_gate_weight(x, None), np.ones(2))
+
+
+def _gated_layer(cfg_over):
+    cfg = synth.reduced("tiny_bf16", shared_gate=True, **cfg_over)
+    layer = synth.make_layer(cfg)
+    assert layer["router"]["shared_gate"] is not None
+    return layer, synth.as_numpy(layer)
+
+
+def test_zero_gate_vector_halves_the_shared_expert():
+    # sigmoid(0) = 1/2 exactly: y = routed + s / 2
+    layer, npl = _gated_layer(dict(H=64, I=32, E=6, k=2, I_s=16))
+    x = _bf16_bits(synth.make_tokens(layer, 3, 8))
+    npl["router"]["shared_gate"] = np.zeros_like(npl["router"]["shared_gate"])
+    gated = moe_forward(npl["cfg"], npl, x)
+    plain = dict(npl, router=dict(npl["router"], shared_gate=None))
+    ref = moe_forward(npl["cfg"], plain, x)
+    assert np.array_equal(gated["gamma"], np.full(3, 0.5))
+    np.testing.assert_allclose(gated["y"], ref["y"] - 0.5 * ref["shared"], rtol=1e-12, atol=1e-15)
+
+
+def test_gate_brute_force_per_token():
+    layer, npl = _gated_layer(dict(H=32, I=16, E=4, k=2, I_s=8))
+    xt = synth.make_tokens(layer, 2, 9)
+    x = _bf16_bits(xt)
+    out = moe_forward(npl["cfg"], npl, x)
+    wsg = layer["router"]["shared_gate"].double().tolist()
+    for t, row in enumerate(xt.double().tolist()):
+        dot = sum(a * b for a, b in zip(row, wsg))
+        assert math.isclose(out["gamma"][t], 1.0 / (1.0 + math.exp(-dot)), rel_tol=1e-13)
+
+
+def _share(npl, lo, hi):
+    """The layer as an expert-parallel share holding experts lo..hi-1."""
+    ex = {}
+    for name, p in npl["experts"].items():
+        q = dict(p, data=p["data"][lo:hi], count=hi - lo)
+        if p.get("scales") is not None:
+            q["scales"] = p["scales"][lo:hi]
+        if p.get("tensor_scale") is not None:
+            q["tensor_scale"] = p["tensor_scale"][lo:hi]
+        ex[name] = q
+    return dict(npl, experts=ex)
+
+
+@pytest.mark.parametrize("bounds", [(0, 3, 6), (0, 1, 4, 6), (0, 6)])
+def test_expert_shares_sum_to_the_layer(bounds):
+    # the shares' routed partials plus the gated shared expert, added once,
+    # give the whole layer
+    for gated in (False, True):
+        layer, npl = _gated_layer(dict(H=64, I=32, E=6, k=3, I_s=16, routed_fmt="mxfp4"))
+        if not gated:
+            npl["router"]["shared_gate"] = None
+        x = _bf16_bits(synth.make_tokens(layer, 4, 10))
+        full = moe_forward(npl["cfg"], npl, x)
+        parts = [moe_forward(npl["cfg"], _share(npl, lo, hi), x, expert_range=(lo, hi))
+                 for lo, hi in zip(bounds[:-1], bounds[1:])]
+        for p in parts:
+            assert p["shared"] is None and np.array_equal(p["idx"], full["idx"])
+        total = sum(p["y"] for p in parts) + full["gamma"][:, None] * full["shared"]
+        np.testing.assert_allclose(total, full["y"], rtol=1e-12, atol=1e-15)
+
+
+def test_share_without_selected_experts_is_zero():
+    layer, npl = _gated_layer(dict(H=64, I=32, E=6, k=1, I_s=16))
+    x = _bf16_bits(synth.make_tokens(layer, 2, 11))
+    full = moe_forward(npl["cfg"], npl, x)
+    used = set(full["idx"].reshape(-1).tolist())
+    free = [e for e in range(6) if e not in used]
+    if free:
+        e = free[0]
+        part = moe_forward(npl["cfg"], _share(npl, e, e + 1), x, expert_range=(e, e + 1))
+        assert not part["y"].any()
