@@ -7,7 +7,8 @@
  *   idx, w = top-k of z (softmax) or of sigmoid(z)+bias (sigmoid),
  *            optional renormalisation, times the routed scaling factor
  *   a      = silu(Wg[e] x) * (Wu[e] x)  per routed (token, expert) pair
- *   y[t]   = sum_j w[t,j] * Wd[idx[t,j]] a  +  shared expert(x[t])
+ *   y[t]   = sum_j w[t,j] * Wd[idx[t,j]] a  +  g[t] * shared expert(x[t]),
+ *            g[t] = sigmoid(x[t] . w_sg) with a shared-expert gate, else 1
  *   out    = BF16(y) (round to nearest even)
  *
  * The stages and their arguments follow the reference pages:
@@ -51,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -115,6 +116,12 @@ typedef struct {
 typedef struct {
   const void* weight;  /* device, BF16 [E, H], 16-byte aligned */
   const float* bias;   /* device, FP32 [E] correction bias for sigmoid scoring, or NULL */
+  /* device, BF16 [H], 16-byte aligned, or NULL: the shared-expert gate. With
+   * it, token t's shared-expert output is added with weight
+   * sigmoid(x[t] . shared_gate); without it, with weight 1 ("forward_k3.rs",
+   * the EP all-reduce block: the batched blend with a sigmoid gate, or a
+   * plain residual add when the layer has no gate). Needs shared_inter > 0. */
+  const void* shared_gate;
 } moe_router;
 
 typedef struct {

@@ -32,7 +32,8 @@ class MoeCfg(ctypes.Structure):
 
 
 class MoeRouter(ctypes.Structure):
-    _fields_ = [("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
+    _fields_ = [("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("shared_gate", ctypes.c_void_p)]
 
 
 class MoeWeight(ctypes.Structure):
@@ -171,6 +172,7 @@ def make_router(r: dict) -> MoeRouter:
     m = MoeRouter()
     m.weight = _ptr(r["weight"])
     m.bias = _ptr(r.get("bias"))
+    m.shared_gate = _ptr(r.get("shared_gate"))
     return m
 
 

@@ -185,8 +185,9 @@ struct GPlan {
   size_t mcap;  // rows of the permuted buffers
 };
 
-GPlan gplan(const moe_cfg* c, int n) {
+GPlan gplan(const moe_cfg* c, int n, bool gated) {
   GPlan g;
+  const int ER = c->num_experts + (gated ? 1 : 0);  // router rows (+ the shared gate)
   const int mmax = n < 128 ? n : 128;  // tokens of one expert per pass
   g.nt = mmax <= 16 ? 1 : (mmax <= 32 ? 2 : (mmax <= 64 ? 4 : 8));
   const int T = 16 * g.nt;
@@ -194,7 +195,7 @@ GPlan gplan(const moe_cfg* c, int n) {
   const int64_t slots = (int64_t)n * c->top_k;
   g.maxu = (int)(slots < c->num_experts ? slots : c->num_experts);
   const int chunks = c->hidden / moe::kGKC;
-  g.r_rb = (c->num_experts + moe::kGRowsPerWG - 1) / moe::kGRowsPerWG;
+  g.r_rb = (ER + moe::kGRowsPerWG - 1) / moe::kGRowsPerWG;
   g.r_tg = (n + T - 1) / T;
   // split H so that the router has about 256 workgroups
   int want = (256 + g.r_rb * g.r_tg - 1) / (g.r_rb * g.r_tg);
@@ -221,11 +222,11 @@ struct Layout {
   size_t unit_done = 0, blend_ctr = 0, acc = 0;
   size_t a_routed = 0, a_shared = 0, dbuf = 0;
   // grouped
-  size_t g_zpart = 0, g_ticket = 0, g_mask = 0, g_idx = 0, g_wts = 0, g_info = 0, g_ptok = 0, g_pslot = 0,
+  size_t g_zpart = 0, g_gamma = 0, g_ticket = 0, g_mask = 0, g_idx = 0, g_wts = 0, g_info = 0, g_ptok = 0, g_pslot = 0,
          g_inv = 0, g_aperm = 0, g_ashared = 0, g_dperm = 0, g_dshared = 0, g_acc = 0;
 };
 
-Layout layout(const moe_cfg* c, int32_t n, int path) {
+Layout layout(const moe_cfg* c, int32_t n, int path, bool gated) {
   Layout L;
   const size_t N = n, k = c->top_k, H = c->hidden, I = c->inter, Is = c->shared_inter,
                E = c->num_experts;
@@ -245,7 +246,7 @@ Layout layout(const moe_cfg* c, int32_t n, int path) {
     L.a_shared = take(N * (Is ? Is : 1) * 8);
     if (!atomic) L.dbuf = take((N * k + N) * H * 8);
   } else {
-    const GPlan g = gplan(c, n);
+    const GPlan g = gplan(c, n, gated);
     L.g_mask = take(E * g.W * 4);
     L.g_ticket = take(4);
     L.g_idx = take(N * k * 4);
@@ -262,7 +263,8 @@ Layout layout(const moe_cfg* c, int32_t n, int path) {
       L.g_dperm = take(g.mcap * H * 4);
       if (Is) L.g_dshared = take(N * H * 4);
     }
-    L.g_zpart = take((size_t)g.ksplit * N * E * 4);
+    L.g_zpart = take((size_t)g.ksplit * N * (E + (gated ? 1 : 0)) * 4);
+    L.g_gamma = take(N * 4);
   }
   L.total = off;
   return L;
@@ -272,7 +274,10 @@ Layout layout(const moe_cfg* c, int32_t n, int path) {
 size_t need_bytes(const moe_cfg* c, int32_t n) {
   int path;
   if (resolve_path(c, n, &path)) return 0;
-  return layout(c, n, path).total;
+  // a call may or may not bring a shared-expert gate: size for the larger
+  const size_t plain = layout(c, n, path, false).total;
+  const size_t gated = c->shared_inter > 0 ? layout(c, n, path, true).total : 0;
+  return plain > gated ? plain : gated;
 }
 
 // Gate+up geometry: a workgroup stages x once (tokens * H BF16 into LDS) and
@@ -333,6 +338,9 @@ moe_status forward_grouped(const moe_cfg* cfg, const moe_router* router,
   a.out = static_cast<uint16_t*>(out);
   a.router_w = static_cast<const uint16_t*>(router->weight);
   a.router_bias = router->bias;
+  a.shared_gate = static_cast<const uint16_t*>(router->shared_gate);
+  const bool gated = a.shared_gate != nullptr;
+  a.ER = a.E + (gated ? 1 : 0);
   a.gate = to_dev(experts->gate);
   a.up = to_dev(experts->up);
   a.down = to_dev(experts->down);
@@ -344,7 +352,7 @@ moe_status forward_grouped(const moe_cfg* cfg, const moe_router* router,
     a.sdown = to_dev(shared->down);
     fs = shared->gate.format;
   }
-  const GPlan g = gplan(cfg, n);
+  const GPlan g = gplan(cfg, n, gated);
   a.nt = g.nt;
   a.W = g.W;
   a.maxu = g.maxu;
@@ -358,8 +366,9 @@ moe_status forward_grouped(const moe_cfg* cfg, const moe_router* router,
   a.dn_s = g.dn_s;
   a.dn_r = g.dn_r;
   char* base = static_cast<char*>(workspace);
-  const Layout L = layout(cfg, n, MOE_PATH_GROUPED);
+  const Layout L = layout(cfg, n, MOE_PATH_GROUPED, gated);
   a.zpart = reinterpret_cast<float*>(base + L.g_zpart);
+  a.gamma = reinterpret_cast<float*>(base + L.g_gamma);
   a.mask = reinterpret_cast<uint32_t*>(base + L.g_mask);
   a.ticket = reinterpret_cast<unsigned*>(base + L.g_ticket);
   a.idx = reinterpret_cast<int*>(base + L.g_idx);
@@ -433,6 +442,12 @@ moe_status moe_validate(const moe_cfg* cfg, const moe_router* router, const moe_
     return fail(MOE_ERR_UNSUPPORTED, "a correction bias with softmax scoring is not supported");
   if (router->bias && !aligned(router->bias, 4))
     return fail(MOE_ERR_INVALID_ARG, "router bias not 4-byte aligned");
+  if (router->shared_gate) {
+    if (cfg->shared_inter <= 0)
+      return fail(MOE_ERR_INVALID_ARG, "a shared-expert gate needs a shared expert (shared_inter=0)");
+    if (!aligned(router->shared_gate, 16))
+      return fail(MOE_ERR_INVALID_ARG, "shared_gate not 16-byte aligned");
+  }
   if (!experts) return fail(MOE_ERR_INVALID_ARG, "null experts");
   st = check_set(experts, "experts", cfg->hidden, cfg->inter, cfg->num_experts);
   if (st) return st;
@@ -448,7 +463,7 @@ moe_status moe_validate(const moe_cfg* cfg, const moe_router* router, const moe_
   } else if (shared) {
     return fail(MOE_ERR_INVALID_ARG, "shared is given but shared_inter == 0");
   }
-  const size_t need = layout(cfg, n_tokens, path).total;
+  const size_t need = layout(cfg, n_tokens, path, router->shared_gate != nullptr).total;
   if (workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace too small: need %zu bytes, have %zu", need,
                 workspace_bytes);
@@ -465,12 +480,12 @@ moe_status moe_group_layout(const moe_cfg* cfg, int32_t n_tokens, moe_group_view
   if (st) return st;
   if (path != MOE_PATH_GROUPED)
     return fail(MOE_ERR_UNSUPPORTED, "a call with n_tokens=%d takes the decode path", n_tokens);
-  const Layout L = layout(cfg, n_tokens, path);
+  const Layout L = layout(cfg, n_tokens, path, false);
   view->info = L.g_info;
   view->perm_tok = L.g_ptok;
   view->perm_slot = L.g_pslot;
   view->inv = L.g_inv;
-  view->rows = (int32_t)gplan(cfg, n_tokens).mcap;
+  view->rows = (int32_t)gplan(cfg, n_tokens, false).mcap;
   return MOE_OK;
 }
 
@@ -524,6 +539,7 @@ moe_status moe_forward(const moe_cfg* cfg, const moe_router* router, const moe_e
   a.out = static_cast<uint16_t*>(out);
   a.router_w = static_cast<const uint16_t*>(router->weight);
   a.router_bias = router->bias;
+  a.shared_gate = static_cast<const uint16_t*>(router->shared_gate);
   a.gate = to_dev(experts->gate);
   a.up = to_dev(experts->up);
   a.down = to_dev(experts->down);
@@ -545,7 +561,7 @@ moe_status moe_forward(const moe_cfg* cfg, const moe_router* router, const moe_e
     a.gs = gate_up_geom(fs, a.H, a.I_s, rpl, a.N, 1);
     a.ds = moe::stage_geom(fs, a.I_s, a.H, rpl, 1);
   }
-  a.nR = (a.E + 3) / 4;
+  a.nR = (a.E + (a.shared_gate ? 1 : 0) + 3) / 4;  // one router row per wave (+ the gate)
   a.nGs = a.I_s > 0 ? a.gs.tiles : 0;
   a.nGr = a.maxu * a.gr.tiles;
   a.nDs = a.I_s > 0 ? a.ds.tiles : 0;
@@ -555,7 +571,7 @@ moe_status moe_forward(const moe_cfg* cfg, const moe_router* router, const moe_e
   a.spin_limit = 1u << 22;
 
   char* base = static_cast<char*>(workspace);
-  const Layout L = layout(cfg, n_tokens, MOE_PATH_DECODE);
+  const Layout L = layout(cfg, n_tokens, MOE_PATH_DECODE, false);
   a.ctl = reinterpret_cast<moe::Ctl*>(base);
   a.unit_done = reinterpret_cast<unsigned*>(base + L.unit_done);
   a.blend_ctr = reinterpret_cast<unsigned*>(base + L.blend_ctr);

@@ -389,7 +389,7 @@ __device__ __forceinline__ void down_pass(const GroupedArgs& a, const MatView& m
           *reinterpret_cast<float4*>(dst + (int64_t)(row0 + j) * a.H + ho) = d;
         } else {
           int tok = row0 + j;
-          float w = 1.0f;
+          float w = a.shared_gate ? a.gamma[tok] : 1.0f;
           if (!shared) {
             tok = a.perm_tok[row0 + j];
             w = tok >= 0 ? a.wts[a.perm_slot[row0 + j]] : 0.f;

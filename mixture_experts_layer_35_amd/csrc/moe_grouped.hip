@@ -55,8 +55,10 @@ __global__ __launch_bounds__(kGThreads) void k_g_router(GroupedArgs a) {
   ARow rows[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int e = min(rb * kGRowsPerWG + 32 * wave + 16 * t + (lane & 15), a.E - 1);
-    rows[t].data = reinterpret_cast<const uint8_t*>(a.router_w + (int64_t)e * a.H + c0 * kGKC);
+    // rows 0..E-1: the router; row E (with a shared-expert gate): w_sg
+    const int e = min(rb * kGRowsPerWG + 32 * wave + 16 * t + (lane & 15), a.ER - 1);
+    const uint16_t* wr = e < a.E ? a.router_w + (int64_t)e * a.H : a.shared_gate;
+    rows[t].data = reinterpret_cast<const uint8_t*>(wr + c0 * kGKC);
     rows[t].scales = nullptr;
   }
   const XRows x{a.x + (int64_t)t0 * a.H + c0 * kGKC, a.H, nullptr, m};
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(kGThreads) void k_g_router(GroupedArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int e = rb * kGRowsPerWG + 32 * wave + 16 * t + 4 * (lane >> 4) + r;
-            if (e < a.E) a.zpart[((int64_t)(t0 + j) * a.ksplit + s) * a.E + e] = acc[t][n][r];
+            if (e < a.ER) a.zpart[((int64_t)(t0 + j) * a.ksplit + s) * a.ER + e] = acc[t][n][r];
           }
         }
       }
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(kGThreads) void k_g_topk(GroupedArgs a) {
       float v[4][16];
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const float* p = a.zpart + ((int64_t)t * ks + s0 + q) * a.E;
+        const float* p = a.zpart + ((int64_t)t * ks + s0 + q) * a.ER;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int e = lane + 64 * i;
@@ -132,6 +134,12 @@ __global__ __launch_bounds__(kGThreads) void k_g_topk(GroupedArgs a) {
       } else {
         zv[i] = -INFINITY;
       }
+    }
+    if (a.shared_gate && lane == 0) {
+      // the shared-expert weight sigmoid(x . w_sg), from router row E
+      float g = 0.f;
+      for (int q = 0; q < ks; ++q) g += a.zpart[((int64_t)t * ks + q) * a.ER + a.E];
+      a.gamma[t] = 1.0f / (1.0f + expf(-g));
     }
     int my_e;
     float w;
@@ -310,10 +318,11 @@ __global__ __launch_bounds__(kGThreads) void k_g_combine(GroupedArgs a) {
     }
     if (a.I_s > 0) {
       const float4 d = *reinterpret_cast<const float4*>(a.d_shared + (int64_t)t * a.H + h);
-      y.x += d.x;
-      y.y += d.y;
-      y.z += d.z;
-      y.w += d.w;
+      const float g = a.shared_gate ? a.gamma[t] : 1.0f;
+      y.x += g * d.x;
+      y.y += g * d.y;
+      y.z += g * d.z;
+      y.w += g * d.w;
     }
   }
   *reinterpret_cast<uint2*>(a.out + (int64_t)t * a.H + h) =

@@ -41,12 +41,15 @@ struct Ctl {
   unsigned group_done[kDoneGroups * kLineWords];  // per done group, one line each
   // router logits, tagged; token t, expert e at t * 256 + e
   unsigned long long zlog[kNmax * 256];
+  // shared-expert gate logits x . w_sg, tagged, one per token
+  unsigned long long glog[kNmax];
   // the plan: unit u, token t: words u * kPlanStride + 2t (info) and + 2t + 1
   // (routing weight), both tagged
   unsigned long long plan[256 * kPlanStride];
 };
 // the error word is bytes 128..131
-static_assert(sizeof(Ctl) == 384 + kDoneGroups * 128 + kNmax * 256 * 8 + 256 * kPlanStride * 8,
+static_assert(sizeof(Ctl) ==
+                  384 + kDoneGroups * 128 + kNmax * 256 * 8 + kNmax * 8 + 256 * kPlanStride * 8,
               "Ctl layout");
 
 // Plan info word (high half of the tagged word):
@@ -67,6 +70,7 @@ struct DecodeArgs {
   const uint16_t* x;
   const uint16_t* router_w;
   const float* router_bias;
+  const uint16_t* shared_gate;  // [H] BF16 or null: shared output weighted by sigmoid(x . w_sg)
   DevProj gate, up, down, sgate, sup, sdown;
   int N, H, I, E, k, I_s, scoring, renorm, atomic, maxu;
   float rsf;
@@ -114,8 +118,10 @@ struct GroupedArgs {
   const uint16_t* x;
   const uint16_t* router_w;
   const float* router_bias;
+  const uint16_t* shared_gate;  // [H] BF16 or null: shared output weighted by sigmoid(x . w_sg)
   DevProj gate, up, down, sgate, sup, sdown;
   int N, H, I, E, k, I_s, scoring, renorm, atomic;
+  int ER;  // router rows: E, plus the shared gate's row
   float rsf;
   int nt;      // 16-token MFMA tiles per pass (1, 2, 4 or 8)
   int W;       // token-mask words per expert, ceil(N / 32)
@@ -128,7 +134,8 @@ struct GroupedArgs {
   int gu_s, gu_r;   // gate+up: shared workgroups, workgroups per routed unit
   int dn_s, dn_r;   // down: same
   // workspace
-  float* zpart;      // [N, ksplit, E] partial router logits
+  float* zpart;      // [N, ksplit, ER] partial router logits (row E: the shared gate)
+  float* gamma;      // [N] shared-expert weights sigmoid(x . w_sg) (with a gate)
   unsigned* ticket;  // top-k workgroups finished (zeroed by the router kernel)
   uint32_t* mask;    // [E, W] bit t of word t/32: token t routes to expert e
   int* idx;          // [N*k]

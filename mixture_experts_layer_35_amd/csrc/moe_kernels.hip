@@ -439,9 +439,12 @@ __device__ __forceinline__ void router_phase(const DecodeArgs& a, int wg, uint4*
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int e = wg * (kThreads / 64) + wave;
-  if (e < a.E) {
+  // rows 0..E-1: the router; row E (with a shared-expert gate): w_sg
+  if (e < a.E + (a.shared_gate ? 1 : 0)) {
     const int cpr = a.H / 8;
-    const uint8_t* wrow = reinterpret_cast<const uint8_t*>(a.router_w) + (size_t)e * a.H * 2;
+    const uint8_t* wrow = e < a.E
+                              ? reinterpret_cast<const uint8_t*>(a.router_w) + (size_t)e * a.H * 2
+                              : reinterpret_cast<const uint8_t*>(a.shared_gate);
     const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.x);
     float acc[kNmax] = {0.f, 0.f, 0.f, 0.f};
     for (int c0 = 0; c0 < cpr; c0 += 64 * IT) {
@@ -469,7 +472,8 @@ __device__ __forceinline__ void router_phase(const DecodeArgs& a, int wg, uint4*
 #pragma unroll
     for (int t = 0; t < kNmax; ++t) {
       const float s = wave_sum_dpp(acc[t]);
-      if (lane == 0 && t < a.N) st_coh64(a.ctl->zlog + t * 256 + e, tagged(s, tag));
+      if (lane == 0 && t < a.N)
+        st_coh64(e < a.E ? a.ctl->zlog + t * 256 + e : a.ctl->glog + t, tagged(s, tag));
     }
   }
   // the last router workgroup (it waits only on lower ids) routes
@@ -699,6 +703,28 @@ __device__ __forceinline__ void down_phase(const DecodeArgs& a, int wg, uint4* s
         slots[t] = t;
         wt[t] = 1.0f;
         if (t < a.N) mask |= 1u << t;
+      }
+      if (a.shared_gate) {
+        // the shared output's weight sigmoid(x . w_sg): the gate logits come
+        // from the router phase (tagged)
+        if (threadIdx.x < a.N) {
+          const u64* p = a.ctl->glog + threadIdx.x;
+          u64 v = ld_coh64(p);
+          unsigned spins = 0;
+          while ((unsigned)v != tag) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++spins > a.spin_limit) {
+              set_error(a, 4u);
+              break;
+            }
+            v = ld_coh64(p);
+          }
+          s_words[threadIdx.x] = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < kNmax; ++t)
+          if (t < a.N) wt[t] = 1.0f / (1.0f + expf(-tag_value(s_words[t])));
       }
       row0 = wg * a.ds.rows_per_wg;
       down_tile<FS, RPL>(a, a.sdown, 0, wg, a.ds, a.I_s, smem, mask, slots, wt, a.a_shared, true,

@@ -31,7 +31,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version():
-    assert moe.abi_version() == 1
+    assert moe.abi_version() == 2
 
 
 def _fake_weight(fmt, rows, cols, count, base):
@@ -219,3 +219,15 @@ def test_softmax_with_bias_refused():
 def test_status_strings():
     assert moe.status_str(0) == "MOE_OK"
     assert moe.status_str(3) == "MOE_ERR_WORKSPACE"
+
+
+def test_shared_gate_needs_shared_expert_and_alignment():
+    c, r, ex, sh = _c3()
+    r.shared_gate = FAKE
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_OK
+    r.shared_gate = FAKE + 2
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
+    r.shared_gate = FAKE
+    c.shared_inter = 0
+    assert B.validate(c, r, ex, None, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
+    assert "shared expert" in B.last_error()

@@ -120,3 +120,18 @@ def test_prefill_bf16_h4096_full_sampled():
     rows = np.sort(g.choice(4096, size=128, replace=False))
     tokens = np.sort(g.choice(512, size=24, replace=False))
     _case("prefill_bf16_h4096", 512, seed=500, rows=rows, tokens=tokens)
+
+
+# ---- shared-expert sigmoid gate ---------------------------------------------
+
+@pytest.mark.parametrize("accum", ["slot", "atomic"])
+def test_shared_gate_grouped(accum):
+    cfg = synth.reduced("tiny_bf16", shared_gate=True, name="tiny_gated_g")
+    _case(cfg, 17, seed=350, accum=accum)
+
+
+def test_shared_gate_fp8_e256_grouped():
+    # 257 router rows: the gate row opens a third 128-row router block
+    cfg = synth.reduced("grouped_fp8_h4096", H=512, I=256, E=256, k=8, I_s=256,
+                        shared_gate=True, zipf=None, name="fp8_e256_gated_g")
+    _case(cfg, 40, seed=351)

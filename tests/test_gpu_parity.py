@@ -180,3 +180,19 @@ def test_repeated_calls_reuse_workspace(accum):
     head = L.workspace[:HEAD_BYTES].view(torch.int32).cpu().numpy()
     assert head[0] == 0 and head[32] == 0 and head[64] == 5, head[[0, 32, 64]]
     assert not head[96:96 + 64 * 32].any()
+
+
+# ---- shared-expert sigmoid gate ---------------------------------------------
+
+@pytest.mark.parametrize("accum", ["slot", "atomic"])
+@pytest.mark.parametrize("n", [1, 4])
+def test_shared_gate_decode(n, accum):
+    cfg = synth.reduced("tiny_bf16", shared_gate=True, name="tiny_gated")
+    _case(cfg, n, seed=80 + n, accum=accum)
+
+
+def test_shared_gate_nvfp4_e256_decode():
+    # 256 experts: the gate is router row 256, past the logit rows
+    cfg = synth.reduced("deepseek_v3_nvfp4", H=512, I=128, E=256, k=8, I_s=256,
+                        shared_gate=True, name="nvfp4_e256_gated")
+    _case(cfg, 3, seed=85, accum="atomic")
