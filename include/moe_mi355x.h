@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -212,6 +212,41 @@ moe_status moe_forward(const moe_cfg* cfg, const moe_router* router,
                        const moe_topk_out* topk, void* workspace,
                        size_t workspace_bytes, void* stream,
                        const moe_trace* trace);
+
+/* One expert-parallel share of the layer forward, with no collective: the
+ * experts are split over G devices, device g holding experts
+ * [expert_begin, expert_end), and the layer output is the sum of the G
+ * partials plus the shared expert's term, added once ("forward_k3.rs", the
+ * EP all-reduce block: each device sums its own experts' weighted down
+ * projections, the results are all-reduced, and the shared expert is blended
+ * in once afterwards; "forward_atomic_c4.rs", the finalize call that leaves
+ * the shared term out on an EP device; "forward_ep.rs", the local expert
+ * range [local_start, local_end) of an EP rank).
+ *
+ * Every token is routed over all E experts as in moe_forward (the router
+ * weight is the full [E, H] one, and topk reports the full routing); only
+ * the (token, expert) pairs whose expert lies in [expert_begin, expert_end)
+ * are computed. local_experts holds those experts' weights only: count =
+ * expert_end - expert_begin, local index e - expert_begin. shared: the
+ * shared expert when this share is to add its term (weighted by the
+ * shared-expert gate when router->shared_gate is set), or NULL to leave it
+ * out (router->shared_gate is then ignored); at most one share of a layer
+ * should carry it. partial: device FP32 [n_tokens, H], 16-byte aligned,
+ * every element written (zero for a token none of whose experts is local).
+ * The decode path always accumulates in ATOMIC_F32 mode here (a share's
+ * slots outside its range are never produced, which the slot-ordered blend
+ * would wait for); cfg->accum_mode applies on the grouped path. The
+ * workspace and the other arguments are as for moe_forward, and one
+ * workspace sized by moe_workspace_bytes serves both entry points. Errors:
+ * MOE_ERR_INVALID_ARG for an empty range or one outside [0, E), and for
+ * local_experts whose count is not the range's size. */
+moe_status moe_forward_ep_partial(const moe_cfg* cfg, const moe_router* router,
+                                  const moe_experts* local_experts, int32_t expert_begin,
+                                  int32_t expert_end, const moe_experts* shared,
+                                  const void* x, int32_t n_tokens, float* partial,
+                                  const moe_topk_out* topk, void* workspace,
+                                  size_t workspace_bytes, void* stream,
+                                  const moe_trace* trace);
 
 const char* moe_status_str(moe_status status);
 const char* moe_last_error(void);

@@ -20,7 +20,8 @@ PATH = {"auto": 0, "decode": 1, "grouped": 2}
 FORMAT = {"bf16": 0, "fp8_rowscale": 1, "mxfp4": 2, "nvfp4": 3}
 
 EXPORTED = ("moe_abi_version", "moe_last_error", "moe_status_str", "moe_workspace_bytes",
-            "moe_validate", "moe_num_launches", "moe_group_layout", "moe_forward")
+            "moe_validate", "moe_num_launches", "moe_group_layout", "moe_forward",
+            "moe_forward_ep_partial")
 
 
 class MoeCfg(ctypes.Structure):
@@ -105,6 +106,12 @@ def lib() -> ctypes.CDLL:
                                   ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                   ctypes.POINTER(MoeTopkOut), ctypes.c_void_p, ctypes.c_size_t,
                                   ctypes.c_void_p, ctypes.POINTER(MoeTrace)]
+        L.moe_forward_ep_partial.restype = ctypes.c_int
+        L.moe_forward_ep_partial.argtypes = [
+            ctypes.POINTER(MoeCfg), ctypes.POINTER(MoeRouter), ctypes.POINTER(MoeExperts),
+            ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(MoeExperts), ctypes.c_void_p,
+            ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(MoeTopkOut), ctypes.c_void_p,
+            ctypes.c_size_t, ctypes.c_void_p, ctypes.POINTER(MoeTrace)]
         _lib = L
     return _lib
 
@@ -168,6 +175,20 @@ def make_experts(s: dict | None) -> MoeExperts | None:
     return e
 
 
+def slice_experts(s: dict, lo: int, hi: int) -> dict:
+    """Experts lo..hi-1 of a packed set: views of the same device tensors
+    (the expert index is the leading dimension of every array)."""
+    out = {}
+    for name in ("gate", "up", "down"):
+        p = dict(s[name])
+        for key in ("data", "scales", "tensor_scale"):
+            if p.get(key) is not None:
+                p[key] = p[key][lo:hi]
+        p["count"] = hi - lo
+        out[name] = p
+    return out
+
+
 def make_router(r: dict) -> MoeRouter:
     m = MoeRouter()
     m.weight = _ptr(r["weight"])
@@ -225,9 +246,14 @@ class Layer:
         # zero-filled once: the counter head must start at zero (calls keep it so)
         self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
 
-    def prepare(self, x, out, idx=None, weights=None, logits=None, stream=None, events=None):
+    def prepare(self, x, out, idx=None, weights=None, logits=None, stream=None, events=None,
+                share=None, with_shared=False):
         """Marshal one call's arguments once; returns a no-argument callable
-        that enqueues the call (raises MoeError on a refused call)."""
+        that enqueues the call (raises MoeError on a refused call).
+
+        share=(lo, hi) makes it an expert-parallel share (moe_forward_ep_partial):
+        only experts lo..hi-1 are computed, out is FP32 [N, H], and the shared
+        expert's term is added only if with_shared."""
         import torch
         n = x.shape[0]
         topk = None
@@ -241,12 +267,22 @@ class Layer:
             trace = MoeTrace(ctypes.cast(arr, ctypes.c_void_p), len(events))
         if stream is None:
             stream = torch.cuda.current_stream(x.device).cuda_stream
-        args = (ctypes.byref(self.cfg), ctypes.byref(self.router), _ref(self.experts),
-                _ref(self.shared), ctypes.c_void_p(x.data_ptr()), ctypes.c_int32(n),
+        tail = (ctypes.c_void_p(x.data_ptr()), ctypes.c_int32(n),
                 ctypes.c_void_p(out.data_ptr()), _ref(topk),
                 ctypes.c_void_p(self.workspace.data_ptr()),
                 ctypes.c_size_t(self.workspace.numel()), ctypes.c_void_p(stream), _ref(trace))
-        fn = lib().moe_forward
+        if share is None:
+            fn = lib().moe_forward
+            args = (ctypes.byref(self.cfg), ctypes.byref(self.router), _ref(self.experts),
+                    _ref(self.shared)) + tail
+        else:
+            lo, hi = int(share[0]), int(share[1])
+            local = make_experts(slice_experts(self.layer["experts"], lo, hi))
+            keep.append(local)
+            fn = lib().moe_forward_ep_partial
+            args = (ctypes.byref(self.cfg), ctypes.byref(self.router), _ref(local),
+                    ctypes.c_int32(lo), ctypes.c_int32(hi),
+                    _ref(self.shared if with_shared else None)) + tail
         keep += [topk, trace, x, out, idx, weights, logits]
 
         def call():
@@ -280,4 +316,15 @@ class Layer:
         if out is None:
             out = torch.empty_like(x)
         self.prepare(x, out, idx, weights, logits, stream, events)()
+        return out
+
+    def forward_share(self, x, lo: int, hi: int, with_shared=False, out=None, idx=None,
+                      weights=None, logits=None, stream=None, events=None):
+        """One expert-parallel share: FP32 [N, H] partial output of experts
+        lo..hi-1 (plus the shared expert's term if with_shared)."""
+        import torch
+        if out is None:
+            out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+        self.prepare(x, out, idx, weights, logits, stream, events, share=(lo, hi),
+                     with_shared=with_shared)()
         return out

@@ -239,7 +239,9 @@ Layout layout(const moe_cfg* c, int32_t n, int path, bool gated) {
   };
   L.unit_done = take((MOE_MAX_EXPERTS + 1) * moe::kLineWords * 4);
   L.blend_ctr = take((H + 3) / 4 * moe::kLineWords * 4);
-  if (atomic) L.acc = take((size_t)moe::kNmax * H * 4);
+  // the decode accumulator is part of the head in both modes, so that calls
+  // of either mode can share a workspace (it is zero at rest)
+  L.acc = take((size_t)moe::kNmax * H * 4);
   L.head_bytes = off;
   if (path == MOE_PATH_DECODE) {
     L.a_routed = take(N * k * I * 8);
@@ -274,11 +276,28 @@ Layout layout(const moe_cfg* c, int32_t n, int path, bool gated) {
 size_t need_bytes(const moe_cfg* c, int32_t n) {
   int path;
   if (resolve_path(c, n, &path)) return 0;
-  // a call may or may not bring a shared-expert gate: size for the larger
-  const size_t plain = layout(c, n, path, false).total;
-  const size_t gated = c->shared_inter > 0 ? layout(c, n, path, true).total : 0;
-  return plain > gated ? plain : gated;
+  // a call may bring a shared-expert gate, and an expert-parallel share runs
+  // the decode path in atomic mode: size for the largest of these layouts
+  size_t most = 0;
+  for (int acc = MOE_ACCUM_SLOT; acc <= MOE_ACCUM_ATOMIC_F32; ++acc) {
+    moe_cfg cc = *c;
+    cc.accum_mode = acc;
+    for (int gated = 0; gated <= (c->shared_inter > 0 ? 1 : 0); ++gated) {
+      const size_t b = layout(&cc, n, path, gated != 0).total;
+      most = b > most ? b : most;
+    }
+  }
+  return most;
 }
+
+// What a call computes: the whole layer (experts 0..E-1, BF16 output, the
+// shared expert included) or one expert-parallel share (experts lo..hi-1,
+// whose weights are the only ones given, an FP32 partial output, and the
+// shared expert only if this share carries it).
+struct Share {
+  int lo = 0, hi = 0;
+  bool partial = false;
+};
 
 // Gate+up geometry: a workgroup stages x once (tokens * H BF16 into LDS) and
 // then streams `sub` row blocks, enough that the staged bytes stay under a
@@ -322,23 +341,30 @@ moe::DevProj to_dev(const moe_weight& w) {
 moe_status forward_grouped(const moe_cfg* cfg, const moe_router* router,
                            const moe_experts* experts, const moe_experts* shared, const void* x,
                            int32_t n, void* out, const moe_topk_out* topk, void* workspace,
-                           hipStream_t hs, hipEvent_t* ev) {
+                           hipStream_t hs, hipEvent_t* ev, const Share& sh) {
   moe::GroupedArgs a{};
   a.N = n;
   a.H = cfg->hidden;
   a.I = cfg->inter;
   a.E = cfg->num_experts;
   a.k = cfg->top_k;
-  a.I_s = cfg->shared_inter;
+  a.I_s = shared ? cfg->shared_inter : 0;
+  a.e_lo = sh.lo;
+  a.EL = sh.hi - sh.lo;
   a.scoring = cfg->scoring;
   a.renorm = cfg->norm_topk_prob;
   a.atomic = cfg->accum_mode == MOE_ACCUM_ATOMIC_F32;
   a.rsf = cfg->routed_scaling_factor;
   a.x = static_cast<const uint16_t*>(x);
-  a.out = static_cast<uint16_t*>(out);
+  if (sh.partial)
+    a.out_f32 = static_cast<float*>(out);
+  else
+    a.out = static_cast<uint16_t*>(out);
   a.router_w = static_cast<const uint16_t*>(router->weight);
   a.router_bias = router->bias;
-  a.shared_gate = static_cast<const uint16_t*>(router->shared_gate);
+  // the gate weights the shared expert's output: without it in this call,
+  // its router row is not needed
+  a.shared_gate = a.I_s > 0 ? static_cast<const uint16_t*>(router->shared_gate) : nullptr;
   const bool gated = a.shared_gate != nullptr;
   a.ER = a.E + (gated ? 1 : 0);
   a.gate = to_dev(experts->gate);
@@ -355,7 +381,7 @@ moe_status forward_grouped(const moe_cfg* cfg, const moe_router* router,
   const GPlan g = gplan(cfg, n, gated);
   a.nt = g.nt;
   a.W = g.W;
-  a.maxu = g.maxu;
+  a.maxu = g.maxu < a.EL ? g.maxu : a.EL;
   a.ksplit = g.ksplit;
   a.kcps = g.kcps;
   a.r_rb = g.r_rb;
@@ -365,6 +391,7 @@ moe_status forward_grouped(const moe_cfg* cfg, const moe_router* router,
   a.gu_r = g.gu_r;
   a.dn_s = g.dn_s;
   a.dn_r = g.dn_r;
+  if (a.I_s == 0) a.s_tg = a.gu_s = a.dn_s = 0;  // a share without the shared expert
   char* base = static_cast<char*>(workspace);
   const Layout L = layout(cfg, n, MOE_PATH_GROUPED, gated);
   a.zpart = reinterpret_cast<float*>(base + L.g_zpart);
@@ -388,6 +415,162 @@ moe_status forward_grouped(const moe_cfg* cfg, const moe_router* router,
     a.out_logits = topk->logits;
   }
   hipError_t err = moe::launch_grouped(a, fr, fs, hs, ev);
+  if (err != hipSuccess)
+    return fail(MOE_ERR_HIP, "launch failed: %s", hipGetErrorString(err));
+  return MOE_OK;
+}
+
+moe_status validate_impl(const moe_cfg* cfg, const moe_router* router,
+                         const moe_experts* experts, const moe_experts* shared, int32_t n_tokens,
+                         size_t workspace_bytes, const Share& sh) {
+  g_err[0] = 0;
+  moe_status st = check_cfg(cfg);
+  if (st) return st;
+  int path;
+  st = resolve_path(cfg, n_tokens, &path);
+  if (st) return st;
+  if (!router || !router->weight) return fail(MOE_ERR_INVALID_ARG, "null router weight");
+  if (!aligned(router->weight, 16))
+    return fail(MOE_ERR_INVALID_ARG, "router weight not 16-byte aligned");
+  if (cfg->scoring == MOE_SCORE_SOFTMAX && router->bias)
+    return fail(MOE_ERR_UNSUPPORTED, "a correction bias with softmax scoring is not supported");
+  if (router->bias && !aligned(router->bias, 4))
+    return fail(MOE_ERR_INVALID_ARG, "router bias not 4-byte aligned");
+  const bool with_shared = !sh.partial || shared != nullptr;
+  if (router->shared_gate && with_shared) {
+    if (cfg->shared_inter <= 0)
+      return fail(MOE_ERR_INVALID_ARG, "a shared-expert gate needs a shared expert (shared_inter=0)");
+    if (!aligned(router->shared_gate, 16))
+      return fail(MOE_ERR_INVALID_ARG, "shared_gate not 16-byte aligned");
+  }
+  if (sh.lo < 0 || sh.hi > cfg->num_experts || sh.lo >= sh.hi)
+    return fail(MOE_ERR_INVALID_ARG, "expert range [%d, %d) must be non-empty within [0, %d)",
+                sh.lo, sh.hi, cfg->num_experts);
+  if (!experts) return fail(MOE_ERR_INVALID_ARG, "null experts");
+  st = check_set(experts, "experts", cfg->hidden, cfg->inter, sh.hi - sh.lo);
+  if (st) return st;
+  if (cfg->shared_inter > 0 && with_shared) {
+    if (!shared) return fail(MOE_ERR_INVALID_ARG, "shared_inter=%d but shared is null",
+                             cfg->shared_inter);
+    st = check_set(shared, "shared", cfg->hidden, cfg->shared_inter, 1);
+    if (st) return st;
+    if (shared->gate.format != MOE_FMT_BF16 && shared->gate.format != experts->gate.format)
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "shared expert format must be BF16 or the routed format (%s), got %s",
+                  fmt_name(experts->gate.format), fmt_name(shared->gate.format));
+  } else if (shared) {
+    return fail(MOE_ERR_INVALID_ARG, "shared is given but shared_inter == 0");
+  }
+  moe_cfg cc = *cfg;
+  if (sh.partial && path == MOE_PATH_DECODE) cc.accum_mode = MOE_ACCUM_ATOMIC_F32;
+  const size_t need =
+      layout(&cc, n_tokens, path, router->shared_gate != nullptr && with_shared).total;
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace too small: need %zu bytes, have %zu", need,
+                workspace_bytes);
+  return MOE_OK;
+}
+
+moe_status forward_impl(const moe_cfg* cfg, const moe_router* router, const moe_experts* experts,
+                        const moe_experts* shared, const void* x, int32_t n_tokens, void* out,
+                        const moe_topk_out* topk, void* workspace, size_t workspace_bytes,
+                        void* stream, const moe_trace* trace, const Share& sh) {
+  moe_status st = validate_impl(cfg, router, experts, shared, n_tokens, workspace_bytes, sh);
+  if (st) return st;
+  if (!x || !aligned(x, 16)) return fail(MOE_ERR_INVALID_ARG, "x null or not 16-byte aligned");
+  if (!out || !aligned(out, 16))
+    return fail(MOE_ERR_INVALID_ARG, "out null or not 16-byte aligned");
+  if (!workspace || !aligned(workspace, 256))
+    return fail(MOE_ERR_INVALID_ARG, "workspace null or not 256-byte aligned");
+  if (topk) {
+    if ((topk->idx && !aligned(topk->idx, 4)) || (topk->weights && !aligned(topk->weights, 4)) ||
+        (topk->logits && !aligned(topk->logits, 4)))
+      return fail(MOE_ERR_INVALID_ARG, "top-k outputs must be 4-byte aligned");
+  }
+  int path;
+  resolve_path(cfg, n_tokens, &path);
+  const int launches = path == MOE_PATH_DECODE ? 1 : moe::kGLaunches;
+  if (trace && (!trace->events || trace->count < 2 * launches))
+    return fail(MOE_ERR_INVALID_ARG, "trace needs %d events (start and stop of each launch), got %d",
+                2 * launches, trace ? trace->count : 0);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipEvent_t* ev = trace ? reinterpret_cast<hipEvent_t*>(trace->events) : nullptr;
+  if (path == MOE_PATH_GROUPED) return forward_grouped(cfg, router, experts, shared, x, n_tokens,
+                                                       out, topk, workspace, hs, ev, sh);
+
+  moe::DecodeArgs a{};
+  a.N = n_tokens;
+  a.H = cfg->hidden;
+  a.I = cfg->inter;
+  a.E = cfg->num_experts;
+  a.k = cfg->top_k;
+  a.I_s = shared ? cfg->shared_inter : 0;
+  a.scoring = cfg->scoring;
+  a.renorm = cfg->norm_topk_prob;
+  // a share's slots outside its range are never written, so the slot-order
+  // blend would wait for them: a share always accumulates atomically
+  a.atomic = sh.partial || cfg->accum_mode == MOE_ACCUM_ATOMIC_F32;
+  a.rsf = cfg->routed_scaling_factor;
+  a.e_lo = sh.lo;
+  a.e_hi = sh.hi;
+  a.maxu = (a.N * a.k < sh.hi - sh.lo) ? a.N * a.k : sh.hi - sh.lo;
+  a.x = static_cast<const uint16_t*>(x);
+  if (sh.partial)
+    a.out_f32 = static_cast<float*>(out);
+  else
+    a.out = static_cast<uint16_t*>(out);
+  a.router_w = static_cast<const uint16_t*>(router->weight);
+  a.router_bias = router->bias;
+  a.shared_gate = a.I_s > 0 ? static_cast<const uint16_t*>(router->shared_gate) : nullptr;
+  a.gate = to_dev(experts->gate);
+  a.up = to_dev(experts->up);
+  a.down = to_dev(experts->down);
+  const int fr = experts->gate.format;
+  int fs = moe::FMT_NONE_HOST;
+  if (a.I_s > 0) {
+    a.sgate = to_dev(shared->gate);
+    a.sup = to_dev(shared->up);
+    a.sdown = to_dev(shared->down);
+    fs = shared->gate.format;
+  }
+  // two rows per lane group when the routed gate+up grid still gives at
+  // least two workgroups per compute unit
+  const moe::StageGeom g2 = moe::stage_geom(fr, a.H, a.I, 2, 1);
+  const int rpl = ((long)a.maxu * g2.tiles >= 512) ? 2 : 1;
+  a.gr = gate_up_geom(fr, a.H, a.I, rpl, 1, a.maxu);
+  a.dr = moe::stage_geom(fr, a.I, a.H, rpl, 1);
+  if (a.I_s > 0) {
+    a.gs = gate_up_geom(fs, a.H, a.I_s, rpl, a.N, 1);
+    a.ds = moe::stage_geom(fs, a.I_s, a.H, rpl, 1);
+  }
+  a.nR = (a.E + (a.shared_gate ? 1 : 0) + 3) / 4;  // one router row per wave (+ the gate)
+  a.nGs = a.I_s > 0 ? a.gs.tiles : 0;
+  a.nGr = a.maxu * a.gr.tiles;
+  a.nDs = a.I_s > 0 ? a.ds.tiles : 0;
+  a.nDr = a.maxu * a.dr.tiles;
+  a.blend_rows = a.dr.rows_per_wg;
+  if (a.I_s > 0 && a.ds.rows_per_wg > a.blend_rows) a.blend_rows = a.ds.rows_per_wg;
+  a.spin_limit = 1u << 22;
+
+  char* base = static_cast<char*>(workspace);
+  moe_cfg cc = *cfg;
+  cc.accum_mode = a.atomic ? MOE_ACCUM_ATOMIC_F32 : MOE_ACCUM_SLOT;
+  const Layout L = layout(&cc, n_tokens, MOE_PATH_DECODE, false);
+  a.ctl = reinterpret_cast<moe::Ctl*>(base);
+  a.unit_done = reinterpret_cast<unsigned*>(base + L.unit_done);
+  a.blend_ctr = reinterpret_cast<unsigned*>(base + L.blend_ctr);
+  a.acc = a.atomic ? reinterpret_cast<float*>(base + L.acc) : nullptr;
+  a.a_routed = reinterpret_cast<unsigned long long*>(base + L.a_routed);
+  a.a_shared = reinterpret_cast<unsigned long long*>(base + L.a_shared);
+  a.dbuf = a.atomic ? nullptr : reinterpret_cast<unsigned long long*>(base + L.dbuf);
+  if (topk) {
+    a.out_idx = topk->idx;
+    a.out_w = topk->weights;
+    a.out_logits = topk->logits;
+  }
+  const size_t lds = moe::decode_lds_bytes(a.H, a.I, a.I_s);
+  hipError_t err = moe::launch_decode(a, fr, fs, rpl, lds, hs, ev ? ev[0] : nullptr,
+                                      ev ? ev[1] : nullptr);
   if (err != hipSuccess)
     return fail(MOE_ERR_HIP, "launch failed: %s", hipGetErrorString(err));
   return MOE_OK;
@@ -427,49 +610,6 @@ size_t moe_workspace_bytes(const moe_cfg* cfg, int32_t max_tokens) {
   return most;
 }
 
-moe_status moe_validate(const moe_cfg* cfg, const moe_router* router, const moe_experts* experts,
-                        const moe_experts* shared, int32_t n_tokens, size_t workspace_bytes) {
-  g_err[0] = 0;
-  moe_status st = check_cfg(cfg);
-  if (st) return st;
-  int path;
-  st = resolve_path(cfg, n_tokens, &path);
-  if (st) return st;
-  if (!router || !router->weight) return fail(MOE_ERR_INVALID_ARG, "null router weight");
-  if (!aligned(router->weight, 16))
-    return fail(MOE_ERR_INVALID_ARG, "router weight not 16-byte aligned");
-  if (cfg->scoring == MOE_SCORE_SOFTMAX && router->bias)
-    return fail(MOE_ERR_UNSUPPORTED, "a correction bias with softmax scoring is not supported");
-  if (router->bias && !aligned(router->bias, 4))
-    return fail(MOE_ERR_INVALID_ARG, "router bias not 4-byte aligned");
-  if (router->shared_gate) {
-    if (cfg->shared_inter <= 0)
-      return fail(MOE_ERR_INVALID_ARG, "a shared-expert gate needs a shared expert (shared_inter=0)");
-    if (!aligned(router->shared_gate, 16))
-      return fail(MOE_ERR_INVALID_ARG, "shared_gate not 16-byte aligned");
-  }
-  if (!experts) return fail(MOE_ERR_INVALID_ARG, "null experts");
-  st = check_set(experts, "experts", cfg->hidden, cfg->inter, cfg->num_experts);
-  if (st) return st;
-  if (cfg->shared_inter > 0) {
-    if (!shared) return fail(MOE_ERR_INVALID_ARG, "shared_inter=%d but shared is null",
-                             cfg->shared_inter);
-    st = check_set(shared, "shared", cfg->hidden, cfg->shared_inter, 1);
-    if (st) return st;
-    if (shared->gate.format != MOE_FMT_BF16 && shared->gate.format != experts->gate.format)
-      return fail(MOE_ERR_UNSUPPORTED,
-                  "shared expert format must be BF16 or the routed format (%s), got %s",
-                  fmt_name(experts->gate.format), fmt_name(shared->gate.format));
-  } else if (shared) {
-    return fail(MOE_ERR_INVALID_ARG, "shared is given but shared_inter == 0");
-  }
-  const size_t need = layout(cfg, n_tokens, path, router->shared_gate != nullptr).total;
-  if (workspace_bytes < need)
-    return fail(MOE_ERR_WORKSPACE, "workspace too small: need %zu bytes, have %zu", need,
-                workspace_bytes);
-  return MOE_OK;
-}
-
 moe_status moe_group_layout(const moe_cfg* cfg, int32_t n_tokens, moe_group_view* view) {
   g_err[0] = 0;
   moe_status st = check_cfg(cfg);
@@ -496,100 +636,35 @@ int32_t moe_num_launches(const moe_cfg* cfg, int32_t n_tokens) {
   return path == MOE_PATH_DECODE ? 1 : moe::kGLaunches;
 }
 
+moe_status moe_validate(const moe_cfg* cfg, const moe_router* router, const moe_experts* experts,
+                        const moe_experts* shared, int32_t n_tokens, size_t workspace_bytes) {
+  Share sh;
+  sh.hi = cfg ? cfg->num_experts : 0;
+  return validate_impl(cfg, router, experts, shared, n_tokens, workspace_bytes, sh);
+}
+
 moe_status moe_forward(const moe_cfg* cfg, const moe_router* router, const moe_experts* experts,
                        const moe_experts* shared, const void* x, int32_t n_tokens, void* out,
                        const moe_topk_out* topk, void* workspace, size_t workspace_bytes,
                        void* stream, const moe_trace* trace) {
-  moe_status st = moe_validate(cfg, router, experts, shared, n_tokens, workspace_bytes);
-  if (st) return st;
-  if (!x || !aligned(x, 16)) return fail(MOE_ERR_INVALID_ARG, "x null or not 16-byte aligned");
-  if (!out || !aligned(out, 16))
-    return fail(MOE_ERR_INVALID_ARG, "out null or not 16-byte aligned");
-  if (!workspace || !aligned(workspace, 256))
-    return fail(MOE_ERR_INVALID_ARG, "workspace null or not 256-byte aligned");
-  if (topk) {
-    if ((topk->idx && !aligned(topk->idx, 4)) || (topk->weights && !aligned(topk->weights, 4)) ||
-        (topk->logits && !aligned(topk->logits, 4)))
-      return fail(MOE_ERR_INVALID_ARG, "top-k outputs must be 4-byte aligned");
-  }
-  int path;
-  resolve_path(cfg, n_tokens, &path);
-  const int launches = path == MOE_PATH_DECODE ? 1 : moe::kGLaunches;
-  if (trace && (!trace->events || trace->count < 2 * launches))
-    return fail(MOE_ERR_INVALID_ARG, "trace needs %d events (start and stop of each launch), got %d",
-                2 * launches, trace ? trace->count : 0);
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  hipEvent_t* ev = trace ? reinterpret_cast<hipEvent_t*>(trace->events) : nullptr;
-  if (path == MOE_PATH_GROUPED) return forward_grouped(cfg, router, experts, shared, x, n_tokens,
-                                                       out, topk, workspace, hs, ev);
+  Share sh;
+  sh.hi = cfg ? cfg->num_experts : 0;
+  return forward_impl(cfg, router, experts, shared, x, n_tokens, out, topk, workspace,
+                      workspace_bytes, stream, trace, sh);
+}
 
-  moe::DecodeArgs a{};
-  a.N = n_tokens;
-  a.H = cfg->hidden;
-  a.I = cfg->inter;
-  a.E = cfg->num_experts;
-  a.k = cfg->top_k;
-  a.I_s = cfg->shared_inter;
-  a.scoring = cfg->scoring;
-  a.renorm = cfg->norm_topk_prob;
-  a.atomic = cfg->accum_mode == MOE_ACCUM_ATOMIC_F32;
-  a.rsf = cfg->routed_scaling_factor;
-  a.maxu = (a.N * a.k < a.E) ? a.N * a.k : a.E;
-  a.x = static_cast<const uint16_t*>(x);
-  a.out = static_cast<uint16_t*>(out);
-  a.router_w = static_cast<const uint16_t*>(router->weight);
-  a.router_bias = router->bias;
-  a.shared_gate = static_cast<const uint16_t*>(router->shared_gate);
-  a.gate = to_dev(experts->gate);
-  a.up = to_dev(experts->up);
-  a.down = to_dev(experts->down);
-  const int fr = experts->gate.format;
-  int fs = moe::FMT_NONE_HOST;
-  if (a.I_s > 0) {
-    a.sgate = to_dev(shared->gate);
-    a.sup = to_dev(shared->up);
-    a.sdown = to_dev(shared->down);
-    fs = shared->gate.format;
-  }
-  // two rows per lane group when the routed gate+up grid still gives at
-  // least two workgroups per compute unit
-  const moe::StageGeom g2 = moe::stage_geom(fr, a.H, a.I, 2, 1);
-  const int rpl = ((long)a.maxu * g2.tiles >= 512) ? 2 : 1;
-  a.gr = gate_up_geom(fr, a.H, a.I, rpl, 1, a.maxu);
-  a.dr = moe::stage_geom(fr, a.I, a.H, rpl, 1);
-  if (a.I_s > 0) {
-    a.gs = gate_up_geom(fs, a.H, a.I_s, rpl, a.N, 1);
-    a.ds = moe::stage_geom(fs, a.I_s, a.H, rpl, 1);
-  }
-  a.nR = (a.E + (a.shared_gate ? 1 : 0) + 3) / 4;  // one router row per wave (+ the gate)
-  a.nGs = a.I_s > 0 ? a.gs.tiles : 0;
-  a.nGr = a.maxu * a.gr.tiles;
-  a.nDs = a.I_s > 0 ? a.ds.tiles : 0;
-  a.nDr = a.maxu * a.dr.tiles;
-  a.blend_rows = a.dr.rows_per_wg;
-  if (a.I_s > 0 && a.ds.rows_per_wg > a.blend_rows) a.blend_rows = a.ds.rows_per_wg;
-  a.spin_limit = 1u << 22;
-
-  char* base = static_cast<char*>(workspace);
-  const Layout L = layout(cfg, n_tokens, MOE_PATH_DECODE, false);
-  a.ctl = reinterpret_cast<moe::Ctl*>(base);
-  a.unit_done = reinterpret_cast<unsigned*>(base + L.unit_done);
-  a.blend_ctr = reinterpret_cast<unsigned*>(base + L.blend_ctr);
-  a.acc = a.atomic ? reinterpret_cast<float*>(base + L.acc) : nullptr;
-  a.a_routed = reinterpret_cast<unsigned long long*>(base + L.a_routed);
-  a.a_shared = reinterpret_cast<unsigned long long*>(base + L.a_shared);
-  a.dbuf = a.atomic ? nullptr : reinterpret_cast<unsigned long long*>(base + L.dbuf);
-  if (topk) {
-    a.out_idx = topk->idx;
-    a.out_w = topk->weights;
-    a.out_logits = topk->logits;
-  }
-  const size_t lds = moe::decode_lds_bytes(a.H, a.I, a.I_s);
-  hipError_t err = moe::launch_decode(a, fr, fs, rpl, lds, hs, ev ? ev[0] : nullptr,
-                                      ev ? ev[1] : nullptr);
-  if (err != hipSuccess)
-    return fail(MOE_ERR_HIP, "launch failed: %s", hipGetErrorString(err));
-  return MOE_OK;
+moe_status moe_forward_ep_partial(const moe_cfg* cfg, const moe_router* router,
+                                  const moe_experts* local_experts, int32_t expert_begin,
+                                  int32_t expert_end, const moe_experts* shared, const void* x,
+                                  int32_t n_tokens, float* partial, const moe_topk_out* topk,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  const moe_trace* trace) {
+  Share sh;
+  sh.lo = expert_begin;
+  sh.hi = expert_end;
+  sh.partial = true;
+  return forward_impl(cfg, router, local_experts, shared, x, n_tokens, partial, topk, workspace,
+                      workspace_bytes, stream, trace, sh);
 }
 
 }  // extern "C"

@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kGThreads) void k_g_router(GroupedArgs a) {
   extern __shared__ uint4 g_lds[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // clear the token masks (the top-k kernel, launched next, sets them)
-  for (int i = blockIdx.x * kGThreads + tid; i < a.E * a.W; i += gridDim.x * kGThreads)
+  for (int i = blockIdx.x * kGThreads + tid; i < a.EL * a.W; i += gridDim.x * kGThreads)
     a.mask[i] = 0u;
   if (blockIdx.x == 0 && tid == 0) *a.ticket = 0u;
   const int s = blockIdx.x % a.ksplit;
@@ -150,7 +150,8 @@ __global__ __launch_bounds__(kGThreads) void k_g_topk(GroupedArgs a) {
       a.wts[sl] = w;
       if (a.out_idx) a.out_idx[sl] = (uint32_t)my_e;
       if (a.out_w) a.out_w[sl] = w;
-      atomicOr(a.mask + (int64_t)my_e * a.W + (t >> 5), 1u << (t & 31));
+      const int el = my_e - a.e_lo;  // only this call's experts are grouped
+      if (el >= 0 && el < a.EL) atomicOr(a.mask + (int64_t)el * a.W + (t >> 5), 1u << (t & 31));
     }
     if (a.atomic) {
       float4* row = reinterpret_cast<float4*>(a.acc + (int64_t)t * a.H);
@@ -188,7 +189,7 @@ __device__ void group_slots(const GroupedArgs& a, uint4* g_lds) {
   uint16_t* pre = reinterpret_cast<uint16_t*>(base + 257);  // [EB * W] word prefixes
   uint32_t* mlds = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(pre) + kPreBytes);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int E = a.E, W = a.W;
+  const int E = a.EL, W = a.W;  // the experts this call computes
   // the token masks, from LDS when they fit (one coalesced copy)
   const bool staged = E * W <= kMaskLdsWords;
   if (staged)
@@ -278,7 +279,11 @@ __device__ void group_slots(const GroupedArgs& a, uint4* g_lds) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int sl = s0 + q * kT + tid;
-        const int e = ev[q];
+        const int e = ev[q] - a.e_lo;  // local expert index
+        if (sl < nslots && (e < 0 || e >= E)) {
+          a.inv[sl] = -1;  // another share's expert
+          continue;
+        }
         if (e < e0 || e >= e1) continue;
         const int t = sl / a.k;
         const uint32_t wd = mword(e * W + (t >> 5));
@@ -309,8 +314,10 @@ __global__ __launch_bounds__(kGThreads) void k_g_combine(GroupedArgs a) {
     y = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < a.k; ++j) {
       const int s = t * a.k + j;
+      const int row = a.inv[s];
+      if (row < 0) continue;  // another share's expert
       const float w = a.wts[s];
-      const float4 d = *reinterpret_cast<const float4*>(a.d_perm + (int64_t)a.inv[s] * a.H + h);
+      const float4 d = *reinterpret_cast<const float4*>(a.d_perm + (int64_t)row * a.H + h);
       y.x += w * d.x;
       y.y += w * d.y;
       y.z += w * d.z;
@@ -325,8 +332,11 @@ __global__ __launch_bounds__(kGThreads) void k_g_combine(GroupedArgs a) {
       y.w += g * d.w;
     }
   }
-  *reinterpret_cast<uint2*>(a.out + (int64_t)t * a.H + h) =
-      make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
+  if (a.out_f32)  // an expert-parallel share's FP32 partial
+    *reinterpret_cast<float4*>(a.out_f32 + (int64_t)t * a.H + h) = y;
+  else
+    *reinterpret_cast<uint2*>(a.out + (int64_t)t * a.H + h) =
+        make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
 }
 
 // ---------------------------------------------------------------------------
@@ -361,7 +371,7 @@ hipError_t launch_grouped(const GroupedArgs& a, int fr, int fs, hipStream_t st, 
                               gemm_lds(a.nt), st, a, ev, 0);
   if (err != hipSuccess) return err;
   err = launch_one(reinterpret_cast<const void*>(&k_g_topk), (a.N + 3) / 4, kGThreads,
-                   grouped_group_lds(a.E, a.W), st, a, ev, 1);
+                   grouped_group_lds(a.EL, a.W), st, a, ev, 1);
   if (err != hipSuccess) return err;
   switch (fr) {
     case FMT_BF16: err = launch_experts<FMT_BF16>(a, fs, st, ev); break;

@@ -73,6 +73,7 @@ struct DecodeArgs {
   const uint16_t* shared_gate;  // [H] BF16 or null: shared output weighted by sigmoid(x . w_sg)
   DevProj gate, up, down, sgate, sup, sdown;
   int N, H, I, E, k, I_s, scoring, renorm, atomic, maxu;
+  int e_lo, e_hi;  // experts computed: [e_lo, e_hi); weights hold these only
   float rsf;
   // phases (workgroup id ranges, in this order): router, shared gate+up,
   // routed gate+up, shared down, routed down
@@ -90,6 +91,7 @@ struct DecodeArgs {
   float* acc;                    // atomic mode [N, H], zero at rest
   // outputs
   uint16_t* out;
+  float* out_f32;  // instead of out: an expert-parallel share's FP32 partial
   uint32_t* out_idx;
   float* out_w;
   float* out_logits;
@@ -109,7 +111,7 @@ struct GroupInfo {
   int U;         // distinct routed experts in the batch ("units")
   int M;         // rows of the permuted buffers in use (per-unit counts padded to 16)
   int pad[30];
-  int uexp[256];    // expert of unit u, ascending
+  int uexp[256];    // expert of unit u (local index: expert - e_lo), ascending
   int ubase[256];   // first permuted row of unit u (a multiple of 16)
   int ucount[256];  // tokens routed to unit u
 };
@@ -122,6 +124,7 @@ struct GroupedArgs {
   DevProj gate, up, down, sgate, sup, sdown;
   int N, H, I, E, k, I_s, scoring, renorm, atomic;
   int ER;  // router rows: E, plus the shared gate's row
+  int e_lo, EL;  // experts computed: e_lo .. e_lo + EL - 1; weights hold these only
   float rsf;
   int nt;      // 16-token MFMA tiles per pass (1, 2, 4 or 8)
   int W;       // token-mask words per expert, ceil(N / 32)
@@ -137,13 +140,13 @@ struct GroupedArgs {
   float* zpart;      // [N, ksplit, ER] partial router logits (row E: the shared gate)
   float* gamma;      // [N] shared-expert weights sigmoid(x . w_sg) (with a gate)
   unsigned* ticket;  // top-k workgroups finished (zeroed by the router kernel)
-  uint32_t* mask;    // [E, W] bit t of word t/32: token t routes to expert e
+  uint32_t* mask;    // [EL, W] bit t of word t/32: token t routes to expert e_lo + e
   int* idx;          // [N*k]
   float* wts;        // [N*k]
   GroupInfo* info;
   int* perm_tok;     // [Mcap] token of each permuted row, -1 on padding
   int* perm_slot;    // [Mcap] slot t*k+j of each permuted row, -1 on padding
-  int* inv;          // [N*k] permuted row of each slot
+  int* inv;          // [N*k] permuted row of each slot (-1: expert outside the range)
   uint16_t* a_perm;  // [Mcap, I] BF16 silu(g)*u
   uint16_t* a_shared;  // [N, I_s] BF16
   float* d_perm;     // slot mode [Mcap, H] FP32 down outputs
@@ -151,6 +154,7 @@ struct GroupedArgs {
   float* acc;        // atomic mode [N, H] FP32
   // outputs
   uint16_t* out;
+  float* out_f32;  // instead of out: an expert-parallel share's FP32 partial
   uint32_t* out_idx;
   float* out_w;
   float* out_logits;

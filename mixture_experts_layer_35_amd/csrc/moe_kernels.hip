@@ -380,7 +380,12 @@ __device__ __forceinline__ void topk_and_plan(const DecodeArgs& a, TopkScratch* 
   }
   __syncthreads();
   const int nslots = a.N * a.k;
-  if (tid < nslots) s->present[s->idx[tid]] = 1;
+  // units: the distinct selected experts this call computes (those in
+  // [e_lo, e_hi): all of them, or one expert-parallel share's range)
+  if (tid < nslots) {
+    const int e = s->idx[tid];
+    if (e >= a.e_lo && e < a.e_hi) s->present[e] = 1;
+  }
   __syncthreads();
   if (wave == 0) {
     // units in ascending expert order: exclusive scan of the presence flags
@@ -403,7 +408,7 @@ __device__ __forceinline__ void topk_and_plan(const DecodeArgs& a, TopkScratch* 
     if (lane == 63) s->nunits = incl;
   }
   __syncthreads();
-  if (tid < nslots) {
+  if (tid < nslots && s->idx[tid] >= a.e_lo && s->idx[tid] < a.e_hi) {
     const int e = s->idx[tid];
     const int u = s->unit_of[e];
     const int t = tid / a.k;
@@ -594,7 +599,8 @@ __device__ __forceinline__ void gate_up_phase(const DecodeArgs& a, int wg, uint4
   int e;
   float wt[kNmax];
   if (!read_plan(a, unit, tag, e, slots, wt, mask, s_words)) return;
-  gate_up_tile<FR, RPL>(a, a.gate, a.up, e, tile, a.gr, a.I, smem, mask, slots, a.a_routed, tag);
+  gate_up_tile<FR, RPL>(a, a.gate, a.up, e - a.e_lo, tile, a.gr, a.I, smem, mask, slots,
+                        a.a_routed, tag);
   wg_hint(&a.unit_done[unit * kLineWords]);
 }
 
@@ -632,7 +638,10 @@ __device__ __forceinline__ void blend_block(const DecodeArgs& a, int bt, unsigne
         y += tag_value(v);
       }
     }
-    a.out[(size_t)t * a.H + r] = f32_to_bf16_rne(y);
+    if (a.out_f32)
+      a.out_f32[(size_t)t * a.H + r] = y;  // an expert-parallel share's FP32 partial
+    else
+      a.out[(size_t)t * a.H + r] = f32_to_bf16_rne(y);
   }
 }
 
@@ -737,7 +746,8 @@ __device__ __forceinline__ void down_phase(const DecodeArgs& a, int wg, uint4* s
     row0 = tile * a.dr.rows_per_wg;
     int e;
     if (read_plan(a, unit, tag, e, slots, wt, mask, s_words))
-      down_tile<FR, RPL>(a, a.down, e, tile, a.dr, a.I, smem, mask, slots, wt, a.a_routed, false,
+      down_tile<FR, RPL>(a, a.down, e - a.e_lo, tile, a.dr, a.I, smem, mask, slots, wt, a.a_routed,
+                         false,
                          &a.unit_done[unit * kLineWords], (unsigned)a.gr.tiles, tag);
   }
   const int bt = row0 / a.blend_rows;

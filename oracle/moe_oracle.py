@@ -337,7 +337,7 @@ def moe_forward(cfg: dict, layer: dict, x_bits, rows=None, expert_range=None) ->
 # Grouping by expert.
 # --------------------------------------------------------------------------
 
-def group_slots(idx, num_experts: int, pad: int = 16) -> dict:
+def group_slots(idx, num_experts: int, pad: int = 16, expert_range=None) -> dict:
     """Order of the N*k routing slots when the batch is grouped by expert
     ("forward_batched.rs", ``MoeLayer::forward_batched``: the grouped FP8
     decode comment, each expert streamed once for all of its rows; the
@@ -349,24 +349,33 @@ def group_slots(idx, num_experts: int, pad: int = 16) -> dict:
     expert the slots keep ascending slot order (a stable sort by expert).
     Rows past an expert's count up to its padded size are padding (-1).
 
-    Returns counts [E], offsets [E+1] (padded starts), perm_slot and
-    perm_tok [offsets[E]] (-1 on padding), inv [N*k] (row of each slot) and
-    units (experts with at least one slot, ascending).
+    ``expert_range`` = (lo, hi) groups one expert-parallel share (reading
+    R13): only slots whose expert lies in [lo, hi) are placed, experts are
+    numbered locally (e - lo), and the other slots get inv = -1.
+
+    Returns counts [E_local], offsets [E_local+1] (padded starts), perm_slot
+    and perm_tok [offsets[-1]] (-1 on padding), inv [N*k] (row of each slot)
+    and units (local experts with at least one slot, ascending).
     """
     idx = np.asarray(idx, dtype=np.int64)
     n, k = idx.shape
-    counts = np.zeros(num_experts, dtype=np.int64)
-    for e in idx.reshape(-1):
-        counts[e] += 1
+    lo, hi = (0, num_experts) if expert_range is None else expert_range
+    flat = idx.reshape(-1)
+    counts = np.zeros(hi - lo, dtype=np.int64)
+    for e in flat:
+        if lo <= e < hi:
+            counts[e - lo] += 1
     padded = (counts + pad - 1) // pad * pad
-    offsets = np.zeros(num_experts + 1, dtype=np.int64)
+    offsets = np.zeros(hi - lo + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(padded)
     perm_slot = np.full(offsets[-1], -1, dtype=np.int64)
     perm_tok = np.full(offsets[-1], -1, dtype=np.int64)
-    inv = np.empty(n * k, dtype=np.int64)
+    inv = np.full(n * k, -1, dtype=np.int64)
     fill = offsets[:-1].copy()
     for s in range(n * k):  # ascending slot order: a stable counting sort
-        e = idx.reshape(-1)[s]
+        if not lo <= flat[s] < hi:
+            continue
+        e = flat[s] - lo
         perm_slot[fill[e]] = s
         perm_tok[fill[e]] = s // k
         inv[s] = fill[e]

@@ -68,10 +68,11 @@ def rel_l2_per_token(got, want):
     return num / den
 
 
-def check_grouping(L, n, ref_idx, num_experts):
-    """The grouped path's permutation against the oracle's, bit for bit."""
+def check_grouping(L, n, ref_idx, num_experts, expert_range=None):
+    """The grouped path's permutation against the oracle's, bit for bit
+    (of one expert-parallel share's experts, with ``expert_range``)."""
     g = L.grouping(n)
-    ref = group_slots(ref_idx, num_experts, pad=16)
+    ref = group_slots(ref_idx, num_experts, pad=16, expert_range=expert_range)
     units = ref["units"]
     U = len(units)
     assert g["U"] == U, (g["U"], U)

@@ -31,7 +31,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version():
-    assert moe.abi_version() == 2
+    assert moe.abi_version() == 3
 
 
 def _fake_weight(fmt, rows, cols, count, base):
@@ -81,9 +81,13 @@ def test_valid_call_passes_validation():
 def test_workspace_too_small_names_need_and_have():
     c, r, ex, sh = _c3()
     ws = B.workspace_bytes(c, 4)
-    assert B.validate(c, r, ex, sh, 4, ws - 1) == B.MOE_ERR_WORKSPACE
+    assert B.validate(c, r, ex, sh, 4, 1) == B.MOE_ERR_WORKSPACE
     msg = B.last_error()
-    assert f"need {ws} bytes" in msg and f"have {ws - 1}" in msg
+    need = int(re.search(r"need (\d+) bytes", msg).group(1))
+    assert "have 1" in msg and 0 < need <= ws
+    assert B.validate(c, r, ex, sh, 4, need - 1) == B.MOE_ERR_WORKSPACE
+    assert f"need {need} bytes" in B.last_error() and f"have {need - 1}" in B.last_error()
+    assert B.validate(c, r, ex, sh, 4, need) == B.MOE_OK
 
 
 def test_workspace_grows_with_tokens():
@@ -231,3 +235,67 @@ def test_shared_gate_needs_shared_expert_and_alignment():
     c.shared_inter = 0
     assert B.validate(c, r, ex, None, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
     assert "shared expert" in B.last_error()
+
+
+def _share_call(c, r, local, lo, hi, shared, n=4, ws=1 << 40, partial=FAKE + 4096,
+                workspace=FAKE):
+    # every argument fails validation before anything is enqueued
+    return int(B.lib().moe_forward_ep_partial(
+        ctypes.byref(c), ctypes.byref(r), None if local is None else ctypes.byref(local),
+        lo, hi, None if shared is None else ctypes.byref(shared), ctypes.c_void_p(FAKE), n,
+        ctypes.c_void_p(partial), None, ctypes.c_void_p(workspace), ws, None, None))
+
+
+def test_ep_share_range_checked():
+    c, r, _, sh = _c3()
+    for lo, hi in ((5, 5), (9, 3), (-1, 8), (250, 257)):
+        cnt = max(1, hi - lo)
+        local = _fake_set("nvfp4", 7168, 2048, cnt, FAKE)
+        assert _share_call(c, r, local, lo, hi, None) == B.MOE_ERR_INVALID_ARG, (lo, hi)
+        assert "expert range" in B.last_error()
+
+
+def test_ep_share_local_count_must_match_range():
+    c, r, _, sh = _c3()
+    local = _fake_set("nvfp4", 7168, 2048, 64, FAKE)
+    # 64 local experts for a 32-expert range: refused at the count check; a
+    # workspace of 1 byte would fail later, so the count check comes first
+    assert _share_call(c, r, local, 32, 64, None, ws=1) == B.MOE_ERR_INVALID_ARG
+    assert "expected [32," in B.last_error()
+
+
+def test_ep_share_shared_expert_optional_but_consistent():
+    c, r, _, sh = _c3()
+    local = _fake_set("nvfp4", 7168, 2048, 32, FAKE)
+    # with or without the shared expert, a bad output alignment is what is left
+    for s in (None, sh):
+        assert _share_call(c, r, local, 0, 32, s, partial=FAKE + 4) == B.MOE_ERR_INVALID_ARG
+        assert "out" in B.last_error()
+    c.shared_inter = 0
+    assert _share_call(c, r, local, 0, 32, sh) == B.MOE_ERR_INVALID_ARG
+    assert "shared_inter == 0" in B.last_error()
+
+
+def test_ep_share_workspace_checked_against_the_same_size():
+    c, r, _, sh = _c3()
+    ws = B.workspace_bytes(c, 4)
+    local = _fake_set("nvfp4", 7168, 2048, 16, FAKE)
+    assert _share_call(c, r, local, 16, 32, sh, ws=ws - 1, partial=FAKE + 4) in (
+        B.MOE_ERR_INVALID_ARG, B.MOE_ERR_WORKSPACE)
+    assert _share_call(c, r, local, 16, 32, sh, ws=ws // 4) == B.MOE_ERR_WORKSPACE
+
+
+def test_workspace_covers_a_decode_share_of_a_slot_mode_layer():
+    # a share on the decode path accumulates atomically even when the layer
+    # is configured for slot order: the one workspace size covers both
+    cfg = dict(H=2048, I=768, E=128, k=8, I_s=0, scoring="softmax", renorm=True, rsf=1.0)
+    c = B.make_cfg(cfg, accum="slot")
+    r = B.MoeRouter(FAKE, None)
+    ws = B.workspace_bytes(c, 4)
+    local = _fake_set("mxfp4", 2048, 768, 32, FAKE)
+    for n in (1, 3, 4):
+        assert _share_call(c, r, local, 0, 32, None, n=n, ws=1) == B.MOE_ERR_WORKSPACE
+        need = int(re.search(r"need (\d+) bytes", B.last_error()).group(1))
+        assert need <= ws, n
+        assert _share_call(c, r, local, 0, 32, None, n=n, ws=ws,
+                           partial=FAKE + 4) == B.MOE_ERR_INVALID_ARG

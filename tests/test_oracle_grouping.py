@@ -67,3 +67,28 @@ def test_matches_stable_argsort():
     order = np.argsort(idx.reshape(-1), kind="stable")
     ps = r["perm_slot"]
     assert np.array_equal(ps[ps >= 0], order)
+
+
+@pytest.mark.parametrize("lo,hi", [(0, 1), (3, 11), (8, 16), (0, 16)])
+def test_share_grouping_is_the_full_one_restricted(lo, hi):
+    # a share's grouping keeps, expert by expert, exactly the slots (in the
+    # same order) that the full grouping puts under that expert
+    rng = np.random.default_rng(lo * 100 + hi)
+    n, k, e = 37, 4, 16
+    idx = _random_idx(rng, n, k, e, 0.5)
+    full = group_slots(idx, e, pad=16)
+    part = group_slots(idx, e, pad=16, expert_range=(lo, hi))
+    flat = idx.reshape(-1)
+    local = (flat >= lo) & (flat < hi)
+    assert np.array_equal(part["counts"], full["counts"][lo:hi])
+    assert np.array_equal(part["units"], full["units"][(full["units"] >= lo)
+                                                       & (full["units"] < hi)] - lo)
+    assert (part["inv"][~local] == -1).all()
+    for el in range(hi - lo):
+        seg_p = part["perm_slot"][part["offsets"][el]:part["offsets"][el + 1]]
+        seg_f = full["perm_slot"][full["offsets"][lo + el]:full["offsets"][lo + el + 1]]
+        assert np.array_equal(seg_p, seg_f)
+        assert part["offsets"][el] % 16 == 0
+    s = np.nonzero(local)[0]
+    assert np.array_equal(part["perm_slot"][part["inv"][s]], s)
+    assert np.array_equal(part["perm_tok"][part["inv"][s]], s // k)
