@@ -237,15 +237,16 @@ Layout layout(const moe_cfg* c, int32_t n, int path, bool gated) {
     off = align_up(off + bytes, 256);
     return o;
   };
-  L.unit_done = take((MOE_MAX_EXPERTS + 1) * moe::kLineWords * 4);
+  L.unit_done = take((MOE_MAX_EXPERTS + moe::kSharedLines) * moe::kLineWords * 4);
   L.blend_ctr = take((H + 3) / 4 * moe::kLineWords * 4);
   // the decode accumulator is part of the head in both modes, so that calls
   // of either mode can share a workspace (it is zero at rest)
   L.acc = take((size_t)moe::kNmax * H * 4);
   L.head_bytes = off;
   if (path == MOE_PATH_DECODE) {
-    L.a_routed = take(N * k * I * 8);
-    L.a_shared = take(N * (Is ? Is : 1) * 8);
+    // tagged BF16 pairs: one 8-byte word per two activations
+    L.a_routed = take(N * k * I / 2 * 8);
+    L.a_shared = take(N * (Is ? Is : 2) / 2 * 8);
     if (!atomic) L.dbuf = take((N * k + N) * H * 8);
   } else {
     const GPlan g = gplan(c, n, gated);
@@ -302,8 +303,9 @@ struct Share {
 // Gate+up geometry: a workgroup stages x once (tokens * H BF16 into LDS) and
 // then streams `sub` row blocks, enough that the staged bytes stay under a
 // quarter of the weight bytes, while keeping about two workgroups per compute
-// unit.
-moe::StageGeom gate_up_geom(int fmt, int H, int rows, int rpl, int tokens, int units) {
+// unit. At most max_tiles workgroups report to one unit's done counters.
+moe::StageGeom gate_up_geom(int fmt, int H, int rows, int rpl, int tokens, int units,
+                            int max_tiles) {
   int64_t db, sb;
   expected_bytes(fmt, 1, H, &db, &sb);
   const int64_t row_bytes = db + sb;
@@ -312,13 +314,32 @@ moe::StageGeom gate_up_geom(int fmt, int H, int rows, int rpl, int tokens, int u
   const int64_t staged = (int64_t)tokens * H * 2;
   int sub = (int)((4 * staged + block_bytes - 1) / block_bytes);
   sub = sub < 1 ? 1 : (sub > 8 ? 8 : sub);
-  // at most 64 workgroups report to one expert's done counter
-  while (sub < 16 && (rows + one.rows_per_wg * sub - 1) / (one.rows_per_wg * sub) > 64) ++sub;
+  while (sub < 16 &&
+         (rows + one.rows_per_wg * sub - 1) / (one.rows_per_wg * sub) > max_tiles)
+    ++sub;
   while (sub > 1 &&
          (int64_t)units * ((rows + one.rows_per_wg * sub - 1) / (one.rows_per_wg * sub)) < 512 &&
-         (rows + one.rows_per_wg * (sub - 1) - 1) / (one.rows_per_wg * (sub - 1)) <= 64)
+         (rows + one.rows_per_wg * (sub - 1) - 1) / (one.rows_per_wg * (sub - 1)) <= max_tiles)
     --sub;
   return moe::stage_geom(fmt, H, rows, rpl, sub);
+}
+
+// Down geometry: a workgroup stages its unit's activations once (tagged BF16
+// pairs, 4 bytes per value and token) and streams `sub` row blocks, enough
+// that the staged bytes stay under a quarter of the weight bytes, while the
+// grid keeps at least min_wgs workgroups. sub stays a power of two, so that row
+// tiles of the routed and the shared expert nest in the blend blocks.
+moe::StageGeom down_geom(int fmt, int I, int H, int rpl, int tokens, int units, int min_wgs) {
+  int64_t db, sb;
+  expected_bytes(fmt, 1, I, &db, &sb);
+  const moe::StageGeom one = moe::stage_geom(fmt, I, H, rpl, 1);
+  const int64_t block_bytes = (int64_t)one.rows_per_wg * (db + sb);
+  const int64_t staged = (int64_t)tokens * I * 4;
+  int sub = 1;
+  while (sub < 16 && sub * block_bytes < 4 * staged) sub <<= 1;
+  auto tiles = [&](int s) { return (H + one.rows_per_wg * s - 1) / (one.rows_per_wg * s); };
+  while (sub > 1 && (int64_t)units * tiles(sub) < min_wgs) sub >>= 1;
+  return moe::stage_geom(fmt, I, H, rpl, sub);
 }
 
 moe::DevProj to_dev(const moe_weight& w) {
@@ -537,13 +558,23 @@ moe_status forward_impl(const moe_cfg* cfg, const moe_router* router, const moe_
   // least two workgroups per compute unit
   const moe::StageGeom g2 = moe::stage_geom(fr, a.H, a.I, 2, 1);
   const int rpl = ((long)a.maxu * g2.tiles >= 512) ? 2 : 1;
-  a.gr = gate_up_geom(fr, a.H, a.I, rpl, 1, a.maxu);
-  a.dr = moe::stage_geom(fr, a.I, a.H, rpl, 1);
+  // a routed unit's gate+up reports to one done counter (at most 64
+  // workgroups); the shared expert's, which streams from the start, to
+  // kSharedLines of them
+  a.gr = gate_up_geom(fr, a.H, a.I, rpl, 1, a.maxu, 64);
+  a.dr = down_geom(fr, a.I, a.H, rpl, a.N, a.maxu, 512);
   if (a.I_s > 0) {
-    a.gs = gate_up_geom(fs, a.H, a.I_s, rpl, a.N, 1);
-    a.ds = moe::stage_geom(fs, a.I_s, a.H, rpl, 1);
+    a.gs = gate_up_geom(fs, a.H, a.I_s, rpl, a.N, 1, 64 * moe::kSharedLines);
+    a.ds = down_geom(fs, a.I_s, a.H, rpl, a.N, 1, 64);
   }
-  a.nR = (a.E + (a.shared_gate ? 1 : 0) + 3) / 4;  // one router row per wave (+ the gate)
+  // router: up to four waves per row, so that each wave covers its part of a
+  // row in one round of IT loads per lane (+ one row for the shared gate)
+  const int rcpr = a.H / 8;
+  a.r_wpr = 1;
+  while (a.r_wpr < 4 && a.r_wpr * 64 * 4 < rcpr) a.r_wpr <<= 1;
+  const int rrows = a.E + (a.shared_gate ? 1 : 0);
+  const int rows_per_wg = 4 / a.r_wpr;
+  a.nR = (rrows + rows_per_wg - 1) / rows_per_wg;
   a.nGs = a.I_s > 0 ? a.gs.tiles : 0;
   a.nGr = a.maxu * a.gr.tiles;
   a.nDs = a.I_s > 0 ? a.ds.tiles : 0;

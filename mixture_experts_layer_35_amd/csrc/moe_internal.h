@@ -29,7 +29,8 @@ struct DevProj {
 // plan) carry the call's tag, so they never need clearing. Counters sit on
 // their own 128-byte lines so pollers and atomics do not pile onto one line.
 constexpr int kLineWords = 32;    // 128 bytes
-constexpr int kDoneGroups = 64;   // workgroup i reports to done group i % 64
+constexpr int kDoneGroups = 64;
+constexpr int kSharedLines = 4;  // done counters of the shared expert's gate+up (one line each)   // workgroup i reports to done group i % 64
 constexpr int kPlanStride = 16;   // 64-bit plan words per unit (one line)
 struct Ctl {
   unsigned done;   // done groups finished
@@ -78,12 +79,13 @@ struct DecodeArgs {
   // phases (workgroup id ranges, in this order): router, shared gate+up,
   // routed gate+up, shared down, routed down
   int nR, nGs, nGr, nDs, nDr;
+  int r_wpr;  // waves per router row (1, 2 or 4)
   StageGeom gr, gs, dr, ds;
   int blend_rows;  // output rows per blend block
   unsigned spin_limit;
   // workspace
   Ctl* ctl;
-  unsigned* unit_done;  // [(maxu + 1) * kLineWords]; entry maxu is the shared expert
+  unsigned* unit_done;  // [(maxu + kSharedLines) * kLineWords]; from maxu: the shared expert
   unsigned* blend_ctr;  // [ceil(H / blend_rows) * kLineWords]
   unsigned long long* a_routed;  // [N*k, I] tagged FP32 SiLU(gate)*up
   unsigned long long* a_shared;  // [N, I_s] tagged FP32

@@ -53,7 +53,8 @@
 namespace moe {
 
 constexpr int IT = 4;  // 16-byte chunks per lane per row in flight per pass
-constexpr int SB = 4;  // staging loads in flight per thread
+// rows of one row block: 4 waves x (64 / lanes per row >= 8) x 2 rows per lane group
+constexpr int kBlockRowsMax = 64;
 
 typedef unsigned long long u64;
 
@@ -90,16 +91,22 @@ __device__ __forceinline__ void set_error(const DecodeArgs& a, unsigned code) {
   __hip_atomic_fetch_or(&a.ctl->error, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Thread 0 spins until *p >= target (bounded), then the workgroup proceeds.
-__device__ __forceinline__ void wg_wait_geq(const DecodeArgs& a, const unsigned* p,
-                                            unsigned target, unsigned code) {
+// Thread 0 spins until each of `lines` counters (one cache line apart)
+// reaches its count (bounded), then the workgroup proceeds. Producer w of
+// `total` reports to line w % lines.
+__device__ __forceinline__ void wg_wait_lines(const DecodeArgs& a, const unsigned* p, int lines,
+                                              unsigned total, unsigned code) {
   if (threadIdx.x == 0) {
     unsigned spins = 0;
-    while (ld_coh(p) < target) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > a.spin_limit) {
-        set_error(a, code);
-        break;
+    for (int i = 0; i < lines; ++i) {
+      const unsigned target = (total - (unsigned)i + (unsigned)lines - 1u) / (unsigned)lines;
+      while (ld_coh(p + i * kLineWords) < target) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > a.spin_limit) {
+          set_error(a, code);
+          i = lines;
+          break;
+        }
       }
     }
   }
@@ -246,76 +253,74 @@ __device__ __forceinline__ MatView view_of(const DevProj& p, int e) {
 // loads before it stores any.
 // ---------------------------------------------------------------------------
 // BF16 input rows: token t at x + t * cols
-__device__ __forceinline__ void stage_x(uint4* lds, const uint16_t* x, uint32_t mask, int cols) {
-  const int m = __builtin_popcount(mask);
-  const int per = cols / 8;  // uint4 per row
-  const int total = m * per;
-  auto src = [&](int i) {
-    const int j = i / per;
-    return reinterpret_cast<const uint4*>(x + (size_t)nth_token(mask, j) * cols) + (i - j * per);
-  };
-  auto dst = [&](int i) {
-    const int j = i / per;
-    return lds + nth_token(mask, j) * per + (i - j * per);
-  };
-  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-  for (int i0 = threadIdx.x; i0 < total; i0 += kThreads * SB) {
-    const int i1 = i0 + kThreads, i2 = i0 + 2 * kThreads, i3 = i0 + 3 * kThreads;
-    // explicit branches: a select of the two sources would become a
-    // generic-pointer load of a private copy of z
-    const uint4 v0 = *src(i0);
-    uint4 v1 = z, v2 = z, v3 = z;
-    if (i1 < total) v1 = *src(i1);
-    if (i2 < total) v2 = *src(i2);
-    if (i3 < total) v3 = *src(i3);
-    *dst(i0) = v0;
-    if (i1 < total) *dst(i1) = v1;
-    if (i2 < total) *dst(i2) = v2;
-    if (i3 < total) *dst(i3) = v3;
+// All n rows of x ([n, cols] BF16, contiguous) into LDS bytes [0, n*cols*2)
+// with direct global-to-LDS loads: each wave instruction moves 1 KiB (16
+// bytes per lane, lane i to LDS offset 16 i) and no registers hold the data,
+// so the whole block is in flight at once. The caller waits (vmcnt) and
+// synchronises before reading it.
+__device__ __forceinline__ void stage_x_async(uint4* lds, const uint16_t* x, int n, int cols) {
+  const int bytes = n * cols * 2;  // a multiple of 16
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(x);
+  uint8_t* dst = reinterpret_cast<uint8_t*>(lds);
+  for (int off = wave * 1024; off < bytes; off += (kThreads / 64) * 1024) {
+    const int my = off + lane * 16;
+    if (my < bytes)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + my),
+                                       (__attribute__((address_space(3))) void*)(dst + off), 16,
+                                       0, 0);
   }
 }
 
-// Tagged FP32 activation rows from other workgroups: token t's row at
-// base + row_t * cols words. Words without the current tag are read again
-// (bounded). Rounded to BF16 (nearest even) into LDS.
+
+// Tagged BF16 activation pairs from other workgroups: token t's row of cols
+// values is cols/2 words at base + row_t * cols/2, each word a BF16 pair
+// (high half) and the call's tag (low half). Words without the current tag
+// are read again (bounded). The pairs go to LDS as they are.
 __device__ __forceinline__ void stage_tagged(const DecodeArgs& a, uint4* lds, const u64* base,
                                              int r0, int r1, int r2, int r3, uint32_t mask,
                                              int cols, unsigned tag) {
+  constexpr int Q = 4;  // loads in flight per thread
   const int m = __builtin_popcount(mask);
   uint32_t* w = reinterpret_cast<uint32_t*>(lds);
-  const int per = cols / 2;  // BF16 pairs per row
+  const int per = cols / 2;  // pairs per row
   const int total = m * per;
-  auto src = [&](int i, int half) {
+  auto src = [&](int i) {
     const int j = i / per;
     const int row = sel4(nth_token(mask, j), r0, r1, r2, r3);
-    return base + (size_t)row * cols + 2 * (i - j * per) + half;
+    return base + (size_t)row * per + (i - j * per);
   };
-  auto put = [&](int i, u64 lo, u64 hi) {
-    const int j = i / per;
-    w[nth_token(mask, j) * per + (i - j * per)] =
-        (uint32_t)f32_to_bf16_rne(tag_value(lo)) | ((uint32_t)f32_to_bf16_rne(tag_value(hi)) << 16);
-  };
-  for (int i0 = threadIdx.x; i0 < total; i0 += kThreads * 2) {
-    const int i1 = i0 + kThreads;
-    const bool has1 = i1 < total;
-    u64 v0 = ld_coh64(src(i0, 0)), v1 = ld_coh64(src(i0, 1));
-    u64 v2 = has1 ? ld_coh64(src(i1, 0)) : (u64)tag;
-    u64 v3 = has1 ? ld_coh64(src(i1, 1)) : (u64)tag;
+  for (int i0 = threadIdx.x; i0 < total; i0 += kThreads * Q) {
+    u64 v[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int i = i0 + q * kThreads;
+      v[q] = i < total ? ld_coh64(src(i)) : (u64)tag;
+    }
     unsigned spins = 0;
-    while ((unsigned)v0 != tag || (unsigned)v1 != tag || (unsigned)v2 != tag ||
-           (unsigned)v3 != tag) {
+    for (;;) {
+      bool ok = true;
+#pragma unroll
+      for (int q = 0; q < Q; ++q) ok = ok && (unsigned)v[q] == tag;
+      if (ok) break;
       __builtin_amdgcn_s_sleep(2);
       if (++spins > a.spin_limit) {
         set_error(a, 2u);
         break;
       }
-      if ((unsigned)v0 != tag) v0 = ld_coh64(src(i0, 0));
-      if ((unsigned)v1 != tag) v1 = ld_coh64(src(i0, 1));
-      if ((unsigned)v2 != tag) v2 = ld_coh64(src(i1, 0));
-      if ((unsigned)v3 != tag) v3 = ld_coh64(src(i1, 1));
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+        if ((unsigned)v[q] != tag) v[q] = ld_coh64(src(i0 + q * kThreads));
     }
-    put(i0, v0, v1);
-    if (has1) put(i1, v2, v3);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int i = i0 + q * kThreads;
+      if (i < total) {
+        const int j = i / per;
+        w[nth_token(mask, j) * per + (i - j * per)] = (uint32_t)(v[q] >> 32);
+      }
+    }
   }
 }
 
@@ -440,19 +445,25 @@ __device__ __forceinline__ void topk_and_plan(const DecodeArgs& a, TopkScratch* 
   }
 }
 
-__device__ __forceinline__ void router_phase(const DecodeArgs& a, int wg, uint4* smem, unsigned tag) {
+__device__ __forceinline__ void router_phase(const DecodeArgs& a, int wg, uint4* smem,
+                                             float* s_part, unsigned tag) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int e = wg * (kThreads / 64) + wave;
+  // a.r_wpr waves share one router row (K split), so that a long row is one
+  // round of loads per wave
+  const int wpr = a.r_wpr;
+  const int q = wave & (wpr - 1);
+  const int e = wg * ((kThreads / 64) / wpr) + wave / wpr;
   // rows 0..E-1: the router; row E (with a shared-expert gate): w_sg
-  if (e < a.E + (a.shared_gate ? 1 : 0)) {
+  const bool has_row = e < a.E + (a.shared_gate ? 1 : 0);
+  float acc[kNmax] = {0.f, 0.f, 0.f, 0.f};
+  if (has_row) {
     const int cpr = a.H / 8;
     const uint8_t* wrow = e < a.E
                               ? reinterpret_cast<const uint8_t*>(a.router_w) + (size_t)e * a.H * 2
                               : reinterpret_cast<const uint8_t*>(a.shared_gate);
     const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.x);
-    float acc[kNmax] = {0.f, 0.f, 0.f, 0.f};
-    for (int c0 = 0; c0 < cpr; c0 += 64 * IT) {
+    for (int c0 = q * 64 * IT; c0 < cpr; c0 += wpr * 64 * IT) {
       // router and token loads go out together
       uint4 wq[IT], xq[IT][kNmax];
       const uint4 z = make_uint4(0u, 0u, 0u, 0u);
@@ -475,11 +486,29 @@ __device__ __forceinline__ void router_phase(const DecodeArgs& a, int wg, uint4*
       }
     }
 #pragma unroll
-    for (int t = 0; t < kNmax; ++t) {
-      const float s = wave_sum_dpp(acc[t]);
-      if (lane == 0 && t < a.N)
-        st_coh64(e < a.E ? a.ctl->zlog + t * 256 + e : a.ctl->glog + t, tagged(s, tag));
+    for (int t = 0; t < kNmax; ++t) acc[t] = wave_sum_dpp(acc[t]);
+  }
+  if (wpr > 1) {
+    // the row's partial sums meet in LDS; the row's first wave adds them in
+    // a fixed order
+    if (lane == 0)
+#pragma unroll
+      for (int t = 0; t < kNmax; ++t) s_part[wave * kNmax + t] = acc[t];
+    __syncthreads();
+    if (q == 0) {
+#pragma unroll
+      for (int t = 0; t < kNmax; ++t) {
+        float v = s_part[wave * kNmax + t];
+        for (int i = 1; i < wpr; ++i) v += s_part[(wave + i) * kNmax + t];
+        acc[t] = v;
+      }
     }
+  }
+  if (has_row && q == 0 && lane == 0) {
+#pragma unroll
+    for (int t = 0; t < kNmax; ++t)
+      if (t < a.N)
+        st_coh64(e < a.E ? a.ctl->zlog + t * 256 + e : a.ctl->glog + t, tagged(acc[t], tag));
   }
   // the last router workgroup (it waits only on lower ids) routes
   if (wg != a.nR - 1) return;
@@ -529,8 +558,8 @@ template <int F, int RPL>
 __device__ __forceinline__ void gate_up_tile(const DecodeArgs& a, const DevProj& pg,
                                              const DevProj& pu, int e, int tile,
                                              const StageGeom& g, int nrows, uint4* smem,
-                                             uint32_t mask, const int (&slots)[kNmax], u64* dst,
-                                             unsigned tag) {
+                                             float* s_rows, uint32_t mask,
+                                             const int (&slots)[kNmax], u64* dst, unsigned tag) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lpr = g.lpr;
@@ -553,43 +582,59 @@ __device__ __forceinline__ void gate_up_tile(const DecodeArgs& a, const DevProj&
       st.compute(cpr, lpr, li, c0, xs, a.H / 2, mask);
     }
     st.reduce(lpr, mask);
+    // the block's activations meet in LDS, then go out as tagged BF16 pairs
+    // of adjacent rows (half the words of one FP32 value per word)
     if (li == lpr - 1) {
 #pragma unroll
       for (int r = 0; r < RPL; ++r) {
         const int row = row_base + r;
-        if (row >= nrows) continue;
-        const float sg = row_scale<F>(mv[0], row);
-        const float su = row_scale<F>(mv[1], row);
+        const float sg = row < nrows ? row_scale<F>(mv[0], row) : 0.f;
+        const float su = row < nrows ? row_scale<F>(mv[1], row) : 0.f;
 #pragma unroll
         for (int t = 0; t < kNmax; ++t) {
-          if (!((mask >> t) & 1u)) continue;
           const float gv = st.acc[0][r][t] * sg;
           const float uv = st.acc[1][r][t] * su;
-          const int slot = sel4(t, slots[0], slots[1], slots[2], slots[3]);
-          st_coh64(dst + (size_t)slot * nrows + row, tagged(silu_f32(gv) * uv, tag));
+          s_rows[(lane_row + r) * kNmax + t] = silu_f32(gv) * uv;
         }
       }
     }
+    __syncthreads();
+    const int row0 = tile * g.rows_per_wg + sb * block_rows;  // even
+    const int pairs = block_rows / 2;
+    const int m = __builtin_popcount(mask);
+    for (int i = threadIdx.x; i < m * pairs; i += kThreads) {
+      const int j = i / pairs;
+      const int p = i - j * pairs;
+      const int row = row0 + 2 * p;
+      if (row >= nrows) continue;  // nrows is even: the pair is whole
+      const int t = nth_token(mask, j);
+      const uint32_t lo = f32_to_bf16_rne(s_rows[(2 * p) * kNmax + t]);
+      const uint32_t hi = f32_to_bf16_rne(s_rows[(2 * p + 1) * kNmax + t]);
+      const int slot = sel4(t, slots[0], slots[1], slots[2], slots[3]);
+      st_coh64(dst + (size_t)slot * (nrows / 2) + row / 2, tagged_u(lo | (hi << 16), tag));
+    }
+    __syncthreads();  // s_rows is refilled by the next block
   }
 }
 
 template <int FR, int FS, int RPL>
-__device__ __forceinline__ void gate_up_phase(const DecodeArgs& a, int wg, uint4* smem, unsigned* s_tmp,
-                              u64* s_words, unsigned tag) {
+__device__ __forceinline__ void gate_up_phase(const DecodeArgs& a, int wg, uint4* smem,
+                                              float* s_rows, u64* s_words, unsigned tag) {
   int slots[kNmax];
   uint32_t mask = 0;
   // x does not depend on the routing: stage every token now, while the
   // router and top-k still run
   const uint32_t all = (1u << a.N) - 1u;
-  stage_x(smem, a.x, all, a.H);
+  stage_x_async(smem, a.x, a.N, a.H);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (wg < a.nGs) {
     if constexpr (FS != FMT_NONE) {
 #pragma unroll
       for (int t = 0; t < kNmax; ++t) slots[t] = t;
-      gate_up_tile<FS, RPL>(a, a.sgate, a.sup, 0, wg, a.gs, a.I_s, smem, all, slots, a.a_shared,
-                            tag);
-      wg_hint(&a.unit_done[a.maxu * kLineWords]);
+      gate_up_tile<FS, RPL>(a, a.sgate, a.sup, 0, wg, a.gs, a.I_s, smem, s_rows, all, slots,
+                            a.a_shared, tag);
+      wg_hint(&a.unit_done[(a.maxu + (wg & (kSharedLines - 1))) * kLineWords]);
     }
     return;
   }
@@ -599,8 +644,8 @@ __device__ __forceinline__ void gate_up_phase(const DecodeArgs& a, int wg, uint4
   int e;
   float wt[kNmax];
   if (!read_plan(a, unit, tag, e, slots, wt, mask, s_words)) return;
-  gate_up_tile<FR, RPL>(a, a.gate, a.up, e - a.e_lo, tile, a.gr, a.I, smem, mask, slots,
-                        a.a_routed, tag);
+  gate_up_tile<FR, RPL>(a, a.gate, a.up, e - a.e_lo, tile, a.gr, a.I, smem, s_rows, mask,
+                        slots, a.a_routed, tag);
   wg_hint(&a.unit_done[unit * kLineWords]);
 }
 
@@ -650,46 +695,55 @@ __device__ __forceinline__ void down_tile(const DecodeArgs& a, const DevProj& pd
                                           const StageGeom& g, int cols, uint4* smem,
                                           uint32_t mask, const int (&slots)[kNmax],
                                           const float (&wt)[kNmax], const u64* src, bool shared,
-                                          const unsigned* ready, unsigned ready_target,
-                                          unsigned tag) {
+                                          const unsigned* ready, int ready_lines,
+                                          unsigned ready_total, unsigned tag) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lpr = g.lpr;
   const int li = lane & (lpr - 1);
-  const int row_base = tile * g.rows_per_wg + (wave * (64 / lpr) + lane / lpr) * RPL;
+  const int block_rows = g.rows_per_wg / g.sub;
+  const int lane_row = (wave * (64 / lpr) + lane / lpr) * RPL;
   const int cpr = cols / Fmt<F>::VPC;
   const MatView mv[1] = {view_of(pd, e)};
-  Stream<F, 1, RPL> st;
-  st.zero();
-  st.load(mv, row_base, a.H, cpr, lpr, li, 0);
-  // weights are in flight; now wait for this unit's activations
-  wg_wait_geq(a, ready, ready_target, 2u);
-  stage_tagged(a, smem, src, slots[0] < 0 ? 0 : slots[0], slots[1] < 0 ? 0 : slots[1],
-               slots[2] < 0 ? 0 : slots[2], slots[3] < 0 ? 0 : slots[3], mask, cols, tag);
-  __syncthreads();
   const uint32_t* xs = reinterpret_cast<const uint32_t*>(smem);
-  st.compute(cpr, lpr, li, 0, xs, cols / 2, mask);
-  for (int c0 = lpr * IT; c0 < cpr; c0 += lpr * IT) {
-    st.load(mv, row_base, a.H, cpr, lpr, li, c0);
-    st.compute(cpr, lpr, li, c0, xs, cols / 2, mask);
-  }
-  st.reduce(lpr, mask);
-  if (li == lpr - 1) {
+  // the activations are staged once for g.sub row blocks; the first block's
+  // weights are in flight while the workgroup waits for them
+#pragma nounroll
+  for (int sb = 0; sb < g.sub; ++sb) {
+    if (tile * g.rows_per_wg + sb * block_rows >= a.H) break;  // uniform
+    const int row_base = tile * g.rows_per_wg + sb * block_rows + lane_row;
+    Stream<F, 1, RPL> st;
+    st.zero();
+    st.load(mv, row_base, a.H, cpr, lpr, li, 0);
+    if (sb == 0) {
+      wg_wait_lines(a, ready, ready_lines, ready_total, 2u);
+      stage_tagged(a, smem, src, slots[0] < 0 ? 0 : slots[0], slots[1] < 0 ? 0 : slots[1],
+                   slots[2] < 0 ? 0 : slots[2], slots[3] < 0 ? 0 : slots[3], mask, cols, tag);
+      __syncthreads();
+    }
+    st.compute(cpr, lpr, li, 0, xs, cols / 2, mask);
+    for (int c0 = lpr * IT; c0 < cpr; c0 += lpr * IT) {
+      st.load(mv, row_base, a.H, cpr, lpr, li, c0);
+      st.compute(cpr, lpr, li, c0, xs, cols / 2, mask);
+    }
+    st.reduce(lpr, mask);
+    if (li == lpr - 1) {
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      const int row = row_base + r;
-      if (row >= a.H) continue;
-      const float rs = row_scale<F>(mv[0], row);
+      for (int r = 0; r < RPL; ++r) {
+        const int row = row_base + r;
+        if (row >= a.H) continue;
+        const float rs = row_scale<F>(mv[0], row);
 #pragma unroll
-      for (int t = 0; t < kNmax; ++t) {
-        if (!((mask >> t) & 1u)) continue;
-        const float v = st.acc[0][r][t] * rs * sel4(t, wt[0], wt[1], wt[2], wt[3]);
-        if (a.atomic) {
-          __hip_atomic_fetch_add(a.acc + (size_t)t * a.H + row, v, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-          const int s = shared ? a.N * a.k + t : sel4(t, slots[0], slots[1], slots[2], slots[3]);
-          st_coh64(a.dbuf + (size_t)s * a.H + row, tagged(v, tag));
+        for (int t = 0; t < kNmax; ++t) {
+          if (!((mask >> t) & 1u)) continue;
+          const float v = st.acc[0][r][t] * rs * sel4(t, wt[0], wt[1], wt[2], wt[3]);
+          if (a.atomic) {
+            __hip_atomic_fetch_add(a.acc + (size_t)t * a.H + row, v, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+          } else {
+            const int s = shared ? a.N * a.k + t : sel4(t, slots[0], slots[1], slots[2], slots[3]);
+            st_coh64(a.dbuf + (size_t)s * a.H + row, tagged(v, tag));
+          }
         }
       }
     }
@@ -737,7 +791,7 @@ __device__ __forceinline__ void down_phase(const DecodeArgs& a, int wg, uint4* s
       }
       row0 = wg * a.ds.rows_per_wg;
       down_tile<FS, RPL>(a, a.sdown, 0, wg, a.ds, a.I_s, smem, mask, slots, wt, a.a_shared, true,
-                         &a.unit_done[a.maxu * kLineWords], (unsigned)a.nGs, tag);
+                         &a.unit_done[a.maxu * kLineWords], kSharedLines, (unsigned)a.nGs, tag);
     }
   } else {
     const int r = wg - a.nDs;
@@ -748,7 +802,7 @@ __device__ __forceinline__ void down_phase(const DecodeArgs& a, int wg, uint4* s
     if (read_plan(a, unit, tag, e, slots, wt, mask, s_words))
       down_tile<FR, RPL>(a, a.down, e - a.e_lo, tile, a.dr, a.I, smem, mask, slots, wt, a.a_routed,
                          false,
-                         &a.unit_done[unit * kLineWords], (unsigned)a.gr.tiles, tag);
+                         &a.unit_done[unit * kLineWords], 1, (unsigned)a.gr.tiles, tag);
   }
   const int bt = row0 / a.blend_rows;
   const int rows_bt = min(a.blend_rows, a.H - bt * a.blend_rows);
@@ -780,14 +834,15 @@ __global__ __launch_bounds__(kThreads) void k_moe_decode(DecodeArgs a) {
   extern __shared__ uint4 smem[];
   __shared__ unsigned s_tmp;
   __shared__ u64 s_words[2 * kNmax];
+  __shared__ float s_rows[kBlockRowsMax * kNmax];
   const int bid = blockIdx.x;
   // this call's tag: the workspace call counter + 1 (never 0, the value of
   // zero-filled memory); stable until the last workgroup has finished
   const unsigned tag = ld_coh(&a.ctl->epoch) + 1u;
   if (bid < a.nR) {
-    router_phase(a, bid, smem, tag);
+    router_phase(a, bid, smem, s_rows, tag);
   } else if (bid < a.nR + a.nGs + a.nGr) {
-    gate_up_phase<FR, FS, RPL>(a, bid - a.nR, smem, &s_tmp, s_words, tag);
+    gate_up_phase<FR, FS, RPL>(a, bid - a.nR, smem, s_rows, s_words, tag);
   } else {
     down_phase<FR, FS, RPL>(a, bid - a.nR - a.nGs - a.nGr, smem, &s_tmp, s_words, tag);
   }
@@ -805,7 +860,7 @@ __global__ __launch_bounds__(kThreads) void k_moe_decode(DecodeArgs a) {
     const unsigned top =
         __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (top + 1 == groups) {
-      for (int u = 0; u <= a.maxu; ++u) st_coh(&a.unit_done[u * kLineWords], 0u);
+      for (int u = 0; u < a.maxu + kSharedLines; ++u) st_coh(&a.unit_done[u * kLineWords], 0u);
       st_coh(&a.ctl->done, 0u);
       const unsigned next = tag == 0xffffffffu ? 0u : tag;  // keep the next tag non-zero
       st_coh(&a.ctl->epoch, next);
