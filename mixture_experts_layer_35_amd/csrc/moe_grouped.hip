@@ -143,7 +143,9 @@ __global__ __launch_bounds__(kGThreads) void k_g_topk(GroupedArgs a) {
     }
     int my_e;
     float w;
-    topk_wave(zv, a.E, a.k, a.scoring, a.router_bias, a.renorm, a.rsf, lane, my_e, w);
+    float bv[4];
+    load_bias4(a.router_bias, a.E, lane, bv);
+    topk_wave(zv, bv, a.E, a.k, a.scoring, a.renorm, a.rsf, lane, my_e, w);
     if (lane < a.k) {
       const int sl = t * a.k + lane;
       st_dev(a.idx + sl, my_e);

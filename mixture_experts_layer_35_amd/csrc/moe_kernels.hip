@@ -347,6 +347,12 @@ __device__ __forceinline__ void topk_and_plan(const DecodeArgs& a, TopkScratch* 
     s->jpos[i] = -1;
     s->uw[i] = 0.f;
   }
+  // routing is on the critical path of every later workgroup: issue first
+  // on this compute unit
+  __builtin_amdgcn_s_setprio(3);
+  // the bias does not depend on the logits: read it before waiting for them
+  float bv[4];
+  load_bias4(a.router_bias, a.E, lane, bv);
   for (int t = wave; t < a.N; t += kThreads / 64) {
     const u64* zrow = a.ctl->zlog + t * 256;
     u64 zw[4] = {(u64)tag, (u64)tag, (u64)tag, (u64)tag};
@@ -374,7 +380,7 @@ __device__ __forceinline__ void topk_and_plan(const DecodeArgs& a, TopkScratch* 
     }
     int my_e;
     float w;
-    topk_wave(zv, a.E, a.k, a.scoring, a.router_bias, a.renorm, a.rsf, lane, my_e, w);
+    topk_wave(zv, bv, a.E, a.k, a.scoring, a.renorm, a.rsf, lane, my_e, w);
     if (lane < a.k) {
       const int sl = t * a.k + lane;
       if (a.out_idx) a.out_idx[sl] = (uint32_t)my_e;
@@ -554,6 +560,48 @@ __device__ __forceinline__ bool read_plan(const DecodeArgs& a, int u, unsigned t
 // Phase GU: gate + up and SiLU(gate) * up. A workgroup covers g.sub row
 // blocks with one staging of x.
 // ---------------------------------------------------------------------------
+// The end of one gate+up row block, once its row sums are in st: the
+// reduction, SiLU(gate) * up, and the hand-off of the block's activations as
+// tagged BF16 pairs of adjacent rows (they meet in LDS first).
+template <int F, int RPL>
+__device__ __forceinline__ void gate_up_emit(Stream<F, 2, RPL>& st, const MatView (&mv)[2],
+                                             int row_base, int lane_row, int brow0,
+                                             int block_rows, int nrows, int lpr, int li,
+                                             float* s_rows, uint32_t mask,
+                                             const int (&slots)[kNmax], u64* dst,
+                                             unsigned tag) {
+  st.reduce(lpr, mask);
+  if (li == lpr - 1) {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const int row = row_base + r;
+      const float sg = row < nrows ? row_scale<F>(mv[0], row) : 0.f;
+      const float su = row < nrows ? row_scale<F>(mv[1], row) : 0.f;
+#pragma unroll
+      for (int t = 0; t < kNmax; ++t) {
+        const float gv = st.acc[0][r][t] * sg;
+        const float uv = st.acc[1][r][t] * su;
+        s_rows[(lane_row + r) * kNmax + t] = silu_f32(gv) * uv;
+      }
+    }
+  }
+  __syncthreads();
+  const int pairs = block_rows / 2;
+  const int m = __builtin_popcount(mask);
+  for (int i = threadIdx.x; i < m * pairs; i += kThreads) {
+    const int j = i / pairs;
+    const int p = i - j * pairs;
+    const int row = brow0 + 2 * p;  // brow0 is even
+    if (row >= nrows) continue;     // nrows is even: the pair is whole
+    const int t = nth_token(mask, j);
+    const uint32_t lo = f32_to_bf16_rne(s_rows[(2 * p) * kNmax + t]);
+    const uint32_t hi = f32_to_bf16_rne(s_rows[(2 * p + 1) * kNmax + t]);
+    const int slot = sel4(t, slots[0], slots[1], slots[2], slots[3]);
+    st_coh64(dst + (size_t)slot * (nrows / 2) + row / 2, tagged_u(lo | (hi << 16), tag));
+  }
+  __syncthreads();  // s_rows is refilled by the next block
+}
+
 template <int F, int RPL>
 __device__ __forceinline__ void gate_up_tile(const DecodeArgs& a, const DevProj& pg,
                                              const DevProj& pu, int e, int tile,
@@ -569,51 +617,22 @@ __device__ __forceinline__ void gate_up_tile(const DecodeArgs& a, const DevProj&
   const int lane_row = (wave * (64 / lpr) + lane / lpr) * RPL;
   const MatView mv[2] = {view_of(pg, e), view_of(pu, e)};
   const uint32_t* xs = reinterpret_cast<const uint32_t*>(smem);
+  const int row0 = tile * g.rows_per_wg;
+  // row blocks that hold rows (uniform)
+  const int nsub = min(g.sub, (nrows - row0 + block_rows - 1) / block_rows);
   // one row block at a time: nothing stays live across blocks, and the
   // other workgroups on the compute unit keep the memory pipe busy
 #pragma nounroll
-  for (int sb = 0; sb < g.sub; ++sb) {
-    if (tile * g.rows_per_wg + sb * block_rows >= nrows) break;  // uniform
-    const int row_base = tile * g.rows_per_wg + sb * block_rows + lane_row;
+  for (int b = 0; b < nsub; ++b) {
+    const int brow0 = row0 + b * block_rows;
     Stream<F, 2, RPL> st;
     st.zero();
     for (int c0 = 0; c0 < cpr; c0 += lpr * IT) {
-      st.load(mv, row_base, nrows, cpr, lpr, li, c0);
+      st.load(mv, brow0 + lane_row, nrows, cpr, lpr, li, c0);
       st.compute(cpr, lpr, li, c0, xs, a.H / 2, mask);
     }
-    st.reduce(lpr, mask);
-    // the block's activations meet in LDS, then go out as tagged BF16 pairs
-    // of adjacent rows (half the words of one FP32 value per word)
-    if (li == lpr - 1) {
-#pragma unroll
-      for (int r = 0; r < RPL; ++r) {
-        const int row = row_base + r;
-        const float sg = row < nrows ? row_scale<F>(mv[0], row) : 0.f;
-        const float su = row < nrows ? row_scale<F>(mv[1], row) : 0.f;
-#pragma unroll
-        for (int t = 0; t < kNmax; ++t) {
-          const float gv = st.acc[0][r][t] * sg;
-          const float uv = st.acc[1][r][t] * su;
-          s_rows[(lane_row + r) * kNmax + t] = silu_f32(gv) * uv;
-        }
-      }
-    }
-    __syncthreads();
-    const int row0 = tile * g.rows_per_wg + sb * block_rows;  // even
-    const int pairs = block_rows / 2;
-    const int m = __builtin_popcount(mask);
-    for (int i = threadIdx.x; i < m * pairs; i += kThreads) {
-      const int j = i / pairs;
-      const int p = i - j * pairs;
-      const int row = row0 + 2 * p;
-      if (row >= nrows) continue;  // nrows is even: the pair is whole
-      const int t = nth_token(mask, j);
-      const uint32_t lo = f32_to_bf16_rne(s_rows[(2 * p) * kNmax + t]);
-      const uint32_t hi = f32_to_bf16_rne(s_rows[(2 * p + 1) * kNmax + t]);
-      const int slot = sel4(t, slots[0], slots[1], slots[2], slots[3]);
-      st_coh64(dst + (size_t)slot * (nrows / 2) + row / 2, tagged_u(lo | (hi << 16), tag));
-    }
-    __syncthreads();  // s_rows is refilled by the next block
+    gate_up_emit<F, RPL>(st, mv, brow0 + lane_row, lane_row, brow0, block_rows, nrows, lpr, li,
+                         s_rows, mask, slots, dst, tag);
   }
 }
 

@@ -57,19 +57,30 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
   return __builtin_bit_cast(float, b);
 }
 
+// The correction bias of experts lane + 64 i (0 where there is none).
+__device__ __forceinline__ void load_bias4(const float* bias, int E, int lane, float bv[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    bv[i] = (bias && e < E) ? bias[e] : 0.f;
+  }
+}
+
 // Top-k routing of one token by one wave ("forward_k3.rs",
 // MoeLayer::forward_k3, step 2; "forward_batched.rs", the routing step). The
 // router logits sit four per lane: expert lane + 64 i in zv[i] (-inf past E).
 // Selection score: the logit (softmax) or sigmoid(logit) + correction bias
 // (sigmoid). Keys order by (score, -expert), so equal scores go to the lower
-// expert index. Each lane sorts its four keys once (a five-exchange network);
+// expert index. bv holds the correction bias of the same four experts (read
+// by the caller ahead of the logits; 0 without a bias). Each lane sorts its
+// four keys once (a five-exchange network);
 // each of the k rounds then takes the wave maximum of the lanes' head keys
 // and pops the winner's head. Weights: softmax over all E logits or the plain
 // sigmoid of the chosen logits (no bias), optionally divided by their sum,
 // then times the routed scaling factor. Lane j < k returns the j-th choice
 // and its weight.
-__device__ __forceinline__ void topk_wave(const float zv[4], int E, int k, int scoring,
-                                          const float* bias, int renorm, float rsf, int lane,
+__device__ __forceinline__ void topk_wave(const float zv[4], const float bv[4], int E, int k,
+                                          int scoring, int renorm, float rsf, int lane,
                                           int& my_e, float& my_w) {
   // key: hi = ordered score bits, lo = ~expert (larger lo = lower expert);
   // an absent expert has hi = lo = 0, below every real key
@@ -80,10 +91,7 @@ __device__ __forceinline__ void topk_wave(const float zv[4], int E, int k, int s
     const int e = lane + 64 * i;
     const bool in = e < E;
     float sc = zv[i];
-    if (scoring == 1) {
-      sc = 1.0f / (1.0f + expf(-zv[i]));
-      if (bias && in) sc += bias[e];
-    }
+    if (scoring == 1) sc = 1.0f / (1.0f + expf(-zv[i])) + bv[i];
     hi[i] = in ? ordered_bits(sc) : 0u;
     lo[i] = in ? 0xffffffffu - (uint32_t)e : 0u;
     zz[i] = zv[i];
