@@ -51,7 +51,20 @@ Readings where the pages are silent (each also listed in the design notes):
   R13 an expert-parallel share holds the experts of one index range; routing
       stays global, slots whose expert is outside the range add nothing, and
       the shared expert is left to the caller, who adds it once after summing
-      the shares.
+      the shares;
+  R14 the softmax+bias arm ("forward_batched.rs", router_bias_one) selects on
+      softmax(logit) + bias, the softmax counterpart of sigmoid(logit) + bias;
+      the weights stay the unbiased softmax probabilities;
+  R15 hash routing ("forward_batched.rs", the hash-routing branch) takes the k
+      experts of the token's table row, in the row's order; their weights are
+      the layer's own weight rule (softmax over the whole router width, or
+      sigmoid) at those experts, then renormalisation and the routed scaling
+      factor; the correction bias plays no part;
+  R16 zero experts ("forward_batched.rs", the router width num_experts +
+      zero_expert_num) are router columns E..E+Z-1 with no weights: routing
+      runs over all E+Z columns, and a slot that chooses a zero expert adds
+      nothing to the output while its weight still counts in the
+      renormalisation.
 """
 
 from __future__ import annotations
@@ -61,6 +74,7 @@ import numpy as np
 __all__ = [
     "e2m1_to_f64", "e8m0_to_f64", "e4m3fn_to_f64", "bf16_to_f64",
     "unpack_fp4", "dequant", "router_logits", "selection_scores", "route",
+    "softmax_rows", "routing_weights", "route_hash",
     "silu", "swiglu_expert", "moe_forward", "group_slots", "shared_gate_weight", "FORMATS",
 ]
 
@@ -193,12 +207,23 @@ def router_logits(x: np.ndarray, wr: np.ndarray) -> np.ndarray:
     return np.asarray(x, np.float64) @ np.asarray(wr, np.float64).T
 
 
+def softmax_rows(z: np.ndarray) -> np.ndarray:
+    """Softmax over each row (all router columns)."""
+    z = np.asarray(z, np.float64)
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    return p / p.sum(axis=1, keepdims=True)
+
+
 def selection_scores(z: np.ndarray, scoring: str, bias=None) -> np.ndarray:
-    """Score used to pick the experts: the logit for softmax routing, or
+    """Score used to pick the experts: the logit for softmax routing,
+    softmax(logit) + correction bias for the softmax+bias arm, or
     sigmoid(logit) + correction bias for sigmoid routing ("forward_k3.rs"
-    step 2, sigmoid+bias for DeepSeek-V3-style routers; readings R2, R3)."""
+    step 2, sigmoid+bias for DeepSeek-V3-style routers; "forward_batched.rs",
+    router_bias_one; readings R2, R3, R14)."""
     z = np.asarray(z, np.float64)
     if scoring == "softmax":
+        if bias is not None:
+            return softmax_rows(z) + np.asarray(bias, np.float64)[None, :]
         return z.copy()
     if scoring == "sigmoid":
         s = 1.0 / (1.0 + np.exp(-z))
@@ -228,15 +253,39 @@ def route(z: np.ndarray, k: int, scoring: str, bias=None,
         order = np.lexsort((ar, -s[t]))
         sel = order[:k]
         idx[t] = sel
-        if scoring == "softmax":
-            p = np.exp(z[t] - z[t].max())
-            p = p / p.sum()
-            wt = p[sel]
-        else:
-            wt = 1.0 / (1.0 + np.exp(-z[t, sel]))
-        if renorm:
-            wt = wt / wt.sum()
-        w[t] = wt * rsf
+        w[t] = routing_weights(z[t], sel, scoring, renorm, rsf)
+    return idx, w
+
+
+def routing_weights(zt: np.ndarray, sel, scoring: str, renorm: bool, rsf: float) -> np.ndarray:
+    """Weights of the chosen experts ``sel`` of one token: softmax over all
+    router columns (softmax) or sigmoid of the chosen logits (sigmoid), no
+    bias (R1, R3), then w /= sum w (with renorm) and times rsf (R5)."""
+    zt = np.asarray(zt, np.float64)
+    if scoring == "softmax":
+        p = np.exp(zt - zt.max())
+        p = p / p.sum()
+        wt = p[sel]
+    else:
+        wt = 1.0 / (1.0 + np.exp(-zt[sel]))
+    if renorm:
+        wt = wt / wt.sum()
+    return wt * rsf
+
+
+def route_hash(z: np.ndarray, tid2eid, token_ids, k: int, scoring: str,
+               renorm: bool = True, rsf: float = 1.0):
+    """Hash routing ("forward_batched.rs", the hash-routing branch, reading
+    R15): token t takes the experts ``tid2eid[token_ids[t], :k]`` in that
+    order, weighted by :func:`routing_weights`."""
+    z = np.asarray(z, np.float64)
+    table = np.asarray(tid2eid, np.int64)
+    ids = np.asarray(token_ids, np.int64)
+    n = z.shape[0]
+    idx = table[ids, :k].copy()
+    w = np.empty((n, k), dtype=np.float64)
+    for t in range(n):
+        w[t] = routing_weights(z[t], idx[t], scoring, renorm, rsf)
     return idx, w
 
 
@@ -275,7 +324,8 @@ def shared_gate_weight(x: np.ndarray, w_sg) -> np.ndarray:
     return 1.0 / (1.0 + np.exp(-g))
 
 
-def moe_forward(cfg: dict, layer: dict, x_bits, rows=None, expert_range=None) -> dict:
+def moe_forward(cfg: dict, layer: dict, x_bits, rows=None, expert_range=None,
+                token_ids=None) -> dict:
     """The whole layer for N tokens, in float64.
 
     ``cfg`` keys: H, I, E, k, I_s, scoring ('softmax' | 'sigmoid'), renorm,
@@ -287,6 +337,8 @@ def moe_forward(cfg: dict, layer: dict, x_bits, rows=None, expert_range=None) ->
     ``expert_range`` = (lo, hi) computes one expert-parallel share instead
     (reading R13): only slots with lo <= idx < hi contribute, the layer's
     ``experts`` hold experts lo..hi-1 only, and there is no shared term.
+    ``cfg["Z"]`` zero experts widen the router (R16); a router with a
+    ``tid2eid`` table routes by the tokens' ``token_ids`` (R15).
 
     y[t] = sum_j w[t, j] * d_{idx[t, j]}(x_t) + gamma[t] * s(x_t)   (R12)
     """
@@ -297,7 +349,11 @@ def moe_forward(cfg: dict, layer: dict, x_bits, rows=None, expert_range=None) ->
     bias = layer["router"].get("bias")
     bias = None if bias is None else np.asarray(bias, np.float64)
     z = router_logits(x, wr)
-    idx, w = route(z, cfg["k"], cfg["scoring"], bias, cfg["renorm"], cfg["rsf"])
+    if layer["router"].get("tid2eid") is not None:
+        idx, w = route_hash(z, layer["router"]["tid2eid"], token_ids, cfg["k"], cfg["scoring"],
+                            cfg["renorm"], cfg["rsf"])
+    else:
+        idx, w = route(z, cfg["k"], cfg["scoring"], bias, cfg["renorm"], cfg["rsf"])
 
     out_rows = np.arange(h) if rows is None else np.asarray(rows)
     k = cfg["k"]
@@ -308,7 +364,7 @@ def moe_forward(cfg: dict, layer: dict, x_bits, rows=None, expert_range=None) ->
     lo, hi = (0, cfg["E"]) if expert_range is None else expert_range
     for e in np.unique(idx):
         if not lo <= e < hi:
-            continue  # another share's expert: this share adds nothing for it
+            continue  # a zero expert (e >= E) or another share's expert: nothing
         wg, wu = dequant(ex["gate"], int(e) - lo), dequant(ex["up"], int(e) - lo)
         wd = dequant(ex["down"], int(e) - lo, rows=out_rows)
         ts, js = np.nonzero(idx == e)

@@ -26,7 +26,7 @@ import math
 import numpy as np
 import torch
 
-__all__ = ["CONFIGS", "seed_for", "make_layer", "make_tokens", "as_numpy",
+__all__ = ["CONFIGS", "seed_for", "make_layer", "make_tokens", "make_token_ids", "as_numpy",
            "layer_bytes", "reduced", "clone_weights"]
 
 # The five workloads. Sizes and distributions as stated for each shape.
@@ -64,7 +64,8 @@ CONFIGS = {
 }
 
 _TENSOR_IDS = {"router": 1, "bias": 2, "gate": 3, "up": 4, "down": 5, "shared_gate": 11,
-               "sgate": 6, "sup": 7, "sdown": 8, "x": 9, "zipf": 10}
+               "sgate": 6, "sup": 7, "sdown": 8, "x": 9, "zipf": 10, "tid2eid": 12,
+               "token_ids": 13}
 
 
 def seed_for(*parts) -> int:
@@ -187,13 +188,14 @@ def make_layer(name_or_cfg, device="cpu") -> dict:
     """Router, routed experts and shared expert for a config, on ``device``."""
     cfg = _cfg(name_or_cfg)
     H, I, E, I_s = cfg["H"], cfg["I"], cfg["E"], cfg["I_s"]
+    EW = E + cfg.get("Z", 0)  # router width: the experts and the zero experts
     g = _gen(device, cfg["cfg_id"], _TENSOR_IDS["router"])
-    wr = torch.randn((E, H), generator=g, device=device) / math.sqrt(H)
+    wr = torch.randn((EW, H), generator=g, device=device) / math.sqrt(H)
     if cfg.get("zipf"):
         # Zipf(s) skew as a log-prior: a seeded rank r_e in 1..E and offset
         # -s*ln(r_e) in the last router column; tokens carry 1.0 there.
         gz = _gen("cpu", cfg["cfg_id"], _TENSOR_IDS["zipf"])
-        ranks = torch.randperm(E, generator=gz).to(torch.float64) + 1.0
+        ranks = torch.randperm(EW, generator=gz).to(torch.float64) + 1.0
         wr[:, H - 1] = (-cfg["zipf"] * torch.log(ranks)).to(wr.dtype).to(device)
     router = {"weight": wr.to(torch.bfloat16).contiguous(), "bias": None, "shared_gate": None}
     if cfg.get("shared_gate") and I_s > 0:
@@ -203,8 +205,14 @@ def make_layer(name_or_cfg, device="cpu") -> dict:
                                  / math.sqrt(H)).to(torch.bfloat16).contiguous()
     if cfg.get("bias_std"):
         gb = _gen(device, cfg["cfg_id"], _TENSOR_IDS["bias"])
-        router["bias"] = (torch.randn((E,), generator=gb, device=device)
+        router["bias"] = (torch.randn((EW,), generator=gb, device=device)
                           * cfg["bias_std"]).float().contiguous()
+    if cfg.get("hash_vocab"):
+        # hash routing: each of `hash_vocab` token ids lists k distinct experts
+        # of the router width, a seeded permutation prefix per row
+        gh = _gen("cpu", cfg["cfg_id"], _TENSOR_IDS["tid2eid"])
+        rows = [torch.randperm(EW, generator=gh)[:cfg["k"]] for _ in range(cfg["hash_vocab"])]
+        router["tid2eid"] = torch.stack(rows).to(torch.int32).to(device).contiguous()
     std = cfg["w_std"]
     experts = {
         "gate": _projection(cfg, device, "gate", cfg["routed_fmt"], E, I, H, std),
@@ -248,6 +256,14 @@ def make_tokens(layer: dict, n: int, batch_seed: int = 0, accept=None,
     return x.contiguous()
 
 
+def make_token_ids(layer: dict, n: int, batch_seed: int = 0) -> torch.Tensor:
+    """[n] int32 token ids, uniform over the layer's hash vocabulary."""
+    cfg = layer["cfg"]
+    g = _gen("cpu", cfg["cfg_id"], _TENSOR_IDS["token_ids"], n, batch_seed)
+    ids = torch.randint(0, cfg["hash_vocab"], (n,), generator=g, dtype=torch.int64)
+    return ids.to(torch.int32).to(layer["router"]["weight"].device).contiguous()
+
+
 def _draw_token(cfg, device, n, batch_seed, t, attempt) -> torch.Tensor:
     g = _gen(device, cfg["cfg_id"], _TENSOR_IDS["x"], n, batch_seed, t, attempt)
     v = torch.randn((cfg["H"],), generator=g, device=device)
@@ -274,7 +290,8 @@ def as_numpy(layer: dict) -> dict:
     out = {"cfg": dict(layer["cfg"]),
            "router": {"weight": _np(layer["router"]["weight"]),
                       "bias": _np(layer["router"]["bias"]),
-                      "shared_gate": _np(layer["router"].get("shared_gate"))},
+                      "shared_gate": _np(layer["router"].get("shared_gate")),
+                      "tid2eid": _np(layer["router"].get("tid2eid"))},
            "experts": {k: proj(v) for k, v in layer["experts"].items()},
            "shared": None}
     if layer["shared"] is not None:
