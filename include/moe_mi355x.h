@@ -3,9 +3,13 @@
  * small token batches on AMD Instinct MI355X (gfx950).
  *
  * One call computes, for N tokens x[N,H] (BF16):
- *   z      = x * Wr^T                                    router projection
- *   idx, w = top-k of z (softmax) or of sigmoid(z)+bias (sigmoid),
- *            optional renormalisation, times the routed scaling factor
+ *   z      = x * Wr^T                 router projection, width E + Z
+ *   idx, w = top-k of z (softmax), of softmax(z)+bias (softmax with a
+ *            correction bias) or of sigmoid(z)+bias (sigmoid); or, with a
+ *            hash table, the table's k experts for the token's id; the
+ *            weights are the unbiased softmax(z) or sigmoid(z) of the chosen
+ *            experts, optional renormalisation, times the routed scaling
+ *            factor. A chosen zero expert (index >= E) adds nothing.
  *   a      = silu(Wg[e] x) * (Wu[e] x)  per routed (token, expert) pair
  *   y[t]   = sum_j w[t,j] * Wd[idx[t,j]] a  +  g[t] * shared expert(x[t]),
  *            g[t] = sigmoid(x[t] . w_sg) with a shared-expert gate, else 1
@@ -52,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -111,17 +115,42 @@ typedef struct {
   float routed_scaling_factor;  /* multiplies the routed weights (after renorm) */
   int32_t accum_mode;           /* moe_accum */
   int32_t path;                 /* moe_path */
+  /* Z: zero experts, 0 = none. The router has E + Z rows (E + Z <=
+   * MOE_MAX_EXPERTS) and routing runs over all of them; experts E..E+Z-1
+   * have no weights and a slot that chooses one adds nothing to the output,
+   * while its weight still counts in the renormalisation ("forward_batched.rs",
+   * the router width num_experts + zero_expert_num, which is also the row
+   * stride of the logits; "forward_k3.rs", the zero-expert guard). */
+  int32_t zero_experts;
 } moe_cfg;
 
 typedef struct {
-  const void* weight;  /* device, BF16 [E, H], 16-byte aligned */
-  const float* bias;   /* device, FP32 [E] correction bias for sigmoid scoring, or NULL */
+  const void* weight;  /* device, BF16 [E + Z, H], 16-byte aligned */
+  /* device, FP32 [E + Z] correction bias, or NULL. It steers selection only:
+   * sigmoid scoring selects on sigmoid(z) + bias, softmax scoring on
+   * softmax(z) + bias ("forward_batched.rs", the softmax+bias arm
+   * router_bias_one that serves zero-expert routers); the weights stay the
+   * unbiased probabilities. Ignored with a hash table. */
+  const float* bias;
   /* device, BF16 [H], 16-byte aligned, or NULL: the shared-expert gate. With
    * it, token t's shared-expert output is added with weight
    * sigmoid(x[t] . shared_gate); without it, with weight 1 ("forward_k3.rs",
    * the EP all-reduce block: the batched blend with a sigmoid gate, or a
    * plain residual add when the layer has no gate). Needs shared_inter > 0. */
   const void* shared_gate;
+  /* Hash routing ("forward_batched.rs", the hash-routing branch: expert ids
+   * from a token-id to expert table, weights from the logits), or NULL:
+   * tid2eid is device int32 [vocab, k]; token t takes experts
+   * tid2eid[token_ids[t] * k + j], j = 0..k-1, in that order, each in
+   * [0, E + Z) and distinct. token_ids is device int32 [n_tokens], per call.
+   * The weights are softmax(z) (over all E + Z logits) or sigmoid(z) at
+   * those experts, then renormalisation and the routed scaling factor as
+   * above. A token id outside [0, vocab), or a table row with an expert out
+   * of range or twice, sets the sticky device error word (bit 16) and that
+   * token's output is not valid. */
+  const int32_t* tid2eid;
+  int32_t vocab;
+  const int32_t* token_ids;
 } moe_router;
 
 typedef struct {
@@ -144,7 +173,7 @@ typedef struct {
 typedef struct {
   uint32_t* idx;  /* [N, k] selected experts, descending score, lowest index on ties */
   float* weights; /* [N, k] routing weights (after renorm and scaling) */
-  float* logits;  /* [N, E] router logits (FP32) */
+  float* logits;  /* [N, E + Z] router logits (FP32) */
 } moe_topk_out;
 
 /* Optional timing hook: when non-NULL, launch i of the call (0 <=
@@ -199,12 +228,13 @@ moe_status moe_group_layout(const moe_cfg* cfg, int32_t n_tokens, moe_group_view
  * cfg->shared_inter == 0; topk, trace: optional. workspace: device, 256-byte
  * aligned, at least moe_workspace_bytes(cfg, n_tokens) bytes, zero-filled
  * before the first call that uses it. Its head holds the decode path's
- * per-call counters (and, in ATOMIC_F32 mode, its accumulator) that every
- * decode call returns to zero and the grouped path leaves alone, so a
- * workspace sized for max_tokens serves any later call with the same cfg and
- * n_tokens <= max_tokens, on either path. Bytes 128..131 are a sticky device
- * error word: non-zero if a decode workgroup's bounded wait for another
- * expired (results of that call are then not valid). stream: hipStream_t
+ * per-call counters and FP32 accumulator, which every decode call returns to
+ * zero and the grouped path leaves alone, so a workspace sized for
+ * max_tokens serves any later call with the same cfg and n_tokens <=
+ * max_tokens, on either path. Bytes 128..131 are a sticky device error word
+ * (either path may set bits; the caller clears it): bits 0..3 a decode
+ * workgroup's bounded wait for another expired, bit 16 an invalid hash-routing
+ * input. Results of a call that set it are not valid. stream: hipStream_t
  * (NULL = default stream). */
 moe_status moe_forward(const moe_cfg* cfg, const moe_router* router,
                        const moe_experts* experts, const moe_experts* shared,
@@ -233,11 +263,10 @@ moe_status moe_forward(const moe_cfg* cfg, const moe_router* router,
  * out (router->shared_gate is then ignored); at most one share of a layer
  * should carry it. partial: device FP32 [n_tokens, H], 16-byte aligned,
  * every element written (zero for a token none of whose experts is local).
- * The decode path always accumulates in ATOMIC_F32 mode here (a share's
- * slots outside its range are never produced, which the slot-ordered blend
- * would wait for); cfg->accum_mode applies on the grouped path. The
- * workspace and the other arguments are as for moe_forward, and one
- * workspace sized by moe_workspace_bytes serves both entry points. Errors:
+ * cfg->accum_mode applies as for moe_forward (the slot-order sum skips the
+ * slots of other shares' experts). The workspace and the other arguments are
+ * as for moe_forward, and one workspace sized by moe_workspace_bytes serves
+ * both entry points. Errors:
  * MOE_ERR_INVALID_ARG for an empty range or one outside [0, E), and for
  * local_experts whose count is not the range's size. */
 moe_status moe_forward_ep_partial(const moe_cfg* cfg, const moe_router* router,

@@ -29,12 +29,14 @@ class MoeCfg(ctypes.Structure):
                 ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("shared_inter", ctypes.c_int32), ("scoring", ctypes.c_int32),
                 ("norm_topk_prob", ctypes.c_int32), ("routed_scaling_factor", ctypes.c_float),
-                ("accum_mode", ctypes.c_int32), ("path", ctypes.c_int32)]
+                ("accum_mode", ctypes.c_int32), ("path", ctypes.c_int32),
+                ("zero_experts", ctypes.c_int32)]
 
 
 class MoeRouter(ctypes.Structure):
     _fields_ = [("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p),
-                ("shared_gate", ctypes.c_void_p)]
+                ("shared_gate", ctypes.c_void_p), ("tid2eid", ctypes.c_void_p),
+                ("vocab", ctypes.c_int32), ("token_ids", ctypes.c_void_p)]
 
 
 class MoeWeight(ctypes.Structure):
@@ -142,6 +144,7 @@ def make_cfg(cfg: dict, accum: str | None = None, path: str = "auto") -> MoeCfg:
     c.routed_scaling_factor = float(cfg["rsf"])
     c.accum_mode = ACCUM[accum or cfg.get("accum", "slot")]
     c.path = PATH[path]
+    c.zero_experts = cfg.get("Z", 0) or 0
     return c
 
 
@@ -194,6 +197,10 @@ def make_router(r: dict) -> MoeRouter:
     m.weight = _ptr(r["weight"])
     m.bias = _ptr(r.get("bias"))
     m.shared_gate = _ptr(r.get("shared_gate"))
+    table = r.get("tid2eid")
+    if table is not None:
+        m.tid2eid = _ptr(table)
+        m.vocab = int(table.shape[0])
     return m
 
 
@@ -247,13 +254,14 @@ class Layer:
         self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
 
     def prepare(self, x, out, idx=None, weights=None, logits=None, stream=None, events=None,
-                share=None, with_shared=False):
+                share=None, with_shared=False, token_ids=None):
         """Marshal one call's arguments once; returns a no-argument callable
         that enqueues the call (raises MoeError on a refused call).
 
         share=(lo, hi) makes it an expert-parallel share (moe_forward_ep_partial):
         only experts lo..hi-1 are computed, out is FP32 [N, H], and the shared
-        expert's term is added only if with_shared."""
+        expert's term is added only if with_shared. token_ids: device int32
+        [N] for a layer with a hash-routing table."""
         import torch
         n = x.shape[0]
         topk = None
@@ -267,20 +275,26 @@ class Layer:
             trace = MoeTrace(ctypes.cast(arr, ctypes.c_void_p), len(events))
         if stream is None:
             stream = torch.cuda.current_stream(x.device).cuda_stream
+        router = self.router
+        if token_ids is not None:
+            # the ids are per call: this call gets its own copy of the router
+            router = MoeRouter.from_buffer_copy(self.router)
+            router.token_ids = _ptr(token_ids)
+            keep += [router, token_ids]
         tail = (ctypes.c_void_p(x.data_ptr()), ctypes.c_int32(n),
                 ctypes.c_void_p(out.data_ptr()), _ref(topk),
                 ctypes.c_void_p(self.workspace.data_ptr()),
                 ctypes.c_size_t(self.workspace.numel()), ctypes.c_void_p(stream), _ref(trace))
         if share is None:
             fn = lib().moe_forward
-            args = (ctypes.byref(self.cfg), ctypes.byref(self.router), _ref(self.experts),
+            args = (ctypes.byref(self.cfg), ctypes.byref(router), _ref(self.experts),
                     _ref(self.shared)) + tail
         else:
             lo, hi = int(share[0]), int(share[1])
             local = make_experts(slice_experts(self.layer["experts"], lo, hi))
             keep.append(local)
             fn = lib().moe_forward_ep_partial
-            args = (ctypes.byref(self.cfg), ctypes.byref(self.router), _ref(local),
+            args = (ctypes.byref(self.cfg), ctypes.byref(router), _ref(local),
                     ctypes.c_int32(lo), ctypes.c_int32(hi),
                     _ref(self.shared if with_shared else None)) + tail
         keep += [topk, trace, x, out, idx, weights, logits]
@@ -311,20 +325,20 @@ class Layer:
                 "inv": arr(v.inv, n_tokens * k)}
 
     def forward(self, x, out=None, idx=None, weights=None, logits=None, stream=None,
-                events=None):
+                events=None, token_ids=None):
         import torch
         if out is None:
             out = torch.empty_like(x)
-        self.prepare(x, out, idx, weights, logits, stream, events)()
+        self.prepare(x, out, idx, weights, logits, stream, events, token_ids=token_ids)()
         return out
 
     def forward_share(self, x, lo: int, hi: int, with_shared=False, out=None, idx=None,
-                      weights=None, logits=None, stream=None, events=None):
+                      weights=None, logits=None, stream=None, events=None, token_ids=None):
         """One expert-parallel share: FP32 [N, H] partial output of experts
         lo..hi-1 (plus the shared expert's term if with_shared)."""
         import torch
         if out is None:
             out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
         self.prepare(x, out, idx, weights, logits, stream, events, share=(lo, hi),
-                     with_shared=with_shared)()
+                     with_shared=with_shared, token_ids=token_ids)()
         return out

@@ -128,9 +128,12 @@ moe_status check_cfg(const moe_cfg* c) {
   if (c->num_experts < 1 || c->num_experts > MOE_MAX_EXPERTS)
     return fail(MOE_ERR_UNSUPPORTED, "num_experts=%d outside 1..%d", c->num_experts,
                 MOE_MAX_EXPERTS);
-  if (c->top_k < 1 || c->top_k > c->num_experts || c->top_k > MOE_MAX_TOPK)
-    return fail(MOE_ERR_INVALID_ARG, "top_k=%d must be in 1..min(E=%d, %d)", c->top_k,
-                c->num_experts, MOE_MAX_TOPK);
+  if (c->zero_experts < 0 || c->num_experts + c->zero_experts > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_UNSUPPORTED, "router width E + Z = %d + %d outside 1..%d",
+                c->num_experts, c->zero_experts, MOE_MAX_EXPERTS);
+  if (c->top_k < 1 || c->top_k > c->num_experts + c->zero_experts || c->top_k > MOE_MAX_TOPK)
+    return fail(MOE_ERR_INVALID_ARG, "top_k=%d must be in 1..min(E+Z=%d, %d)", c->top_k,
+                c->num_experts + c->zero_experts, MOE_MAX_TOPK);
   if (c->scoring != MOE_SCORE_SOFTMAX && c->scoring != MOE_SCORE_SIGMOID)
     return fail(MOE_ERR_INVALID_ARG, "unknown scoring %d", c->scoring);
   if (c->norm_topk_prob != 0 && c->norm_topk_prob != 1)
@@ -187,7 +190,8 @@ struct GPlan {
 
 GPlan gplan(const moe_cfg* c, int n, bool gated) {
   GPlan g;
-  const int ER = c->num_experts + (gated ? 1 : 0);  // router rows (+ the shared gate)
+  // router rows: E experts, Z zero experts (+ the shared gate)
+  const int ER = c->num_experts + c->zero_experts + (gated ? 1 : 0);
   const int mmax = n < 128 ? n : 128;  // tokens of one expert per pass
   g.nt = mmax <= 16 ? 1 : (mmax <= 32 ? 2 : (mmax <= 64 ? 4 : 8));
   const int T = 16 * g.nt;
@@ -266,7 +270,7 @@ Layout layout(const moe_cfg* c, int32_t n, int path, bool gated) {
       L.g_dperm = take(g.mcap * H * 4);
       if (Is) L.g_dshared = take(N * H * 4);
     }
-    L.g_zpart = take((size_t)g.ksplit * N * (E + (gated ? 1 : 0)) * 4);
+    L.g_zpart = take((size_t)g.ksplit * N * (E + c->zero_experts + (gated ? 1 : 0)) * 4);
     L.g_gamma = take(N * 4);
   }
   L.total = off;
@@ -277,8 +281,8 @@ Layout layout(const moe_cfg* c, int32_t n, int path, bool gated) {
 size_t need_bytes(const moe_cfg* c, int32_t n) {
   int path;
   if (resolve_path(c, n, &path)) return 0;
-  // a call may bring a shared-expert gate, and an expert-parallel share runs
-  // the decode path in atomic mode: size for the largest of these layouts
+  // a call may bring a shared-expert gate: size for the larger layout (of
+  // either accumulation mode, so that one workspace serves both)
   size_t most = 0;
   for (int acc = MOE_ACCUM_SLOT; acc <= MOE_ACCUM_ATOMIC_F32; ++acc) {
     moe_cfg cc = *c;
@@ -387,7 +391,12 @@ moe_status forward_grouped(const moe_cfg* cfg, const moe_router* router,
   // its router row is not needed
   a.shared_gate = a.I_s > 0 ? static_cast<const uint16_t*>(router->shared_gate) : nullptr;
   const bool gated = a.shared_gate != nullptr;
-  a.ER = a.E + (gated ? 1 : 0);
+  a.EW = a.E + cfg->zero_experts;
+  a.ER = a.EW + (gated ? 1 : 0);
+  a.tid2eid = router->tid2eid;
+  a.token_ids = router->token_ids;
+  a.vocab = router->vocab;
+  a.err = &reinterpret_cast<moe::Ctl*>(workspace)->error;
   a.gate = to_dev(experts->gate);
   a.up = to_dev(experts->up);
   a.down = to_dev(experts->down);
@@ -453,10 +462,18 @@ moe_status validate_impl(const moe_cfg* cfg, const moe_router* router,
   if (!router || !router->weight) return fail(MOE_ERR_INVALID_ARG, "null router weight");
   if (!aligned(router->weight, 16))
     return fail(MOE_ERR_INVALID_ARG, "router weight not 16-byte aligned");
-  if (cfg->scoring == MOE_SCORE_SOFTMAX && router->bias)
-    return fail(MOE_ERR_UNSUPPORTED, "a correction bias with softmax scoring is not supported");
   if (router->bias && !aligned(router->bias, 4))
     return fail(MOE_ERR_INVALID_ARG, "router bias not 4-byte aligned");
+  if (router->tid2eid) {
+    if (!router->token_ids)
+      return fail(MOE_ERR_INVALID_ARG, "hash routing needs token_ids");
+    if (router->vocab <= 0)
+      return fail(MOE_ERR_INVALID_ARG, "hash routing needs vocab > 0 (vocab=%d)", router->vocab);
+    if (!aligned(router->tid2eid, 4) || !aligned(router->token_ids, 4))
+      return fail(MOE_ERR_INVALID_ARG, "tid2eid and token_ids must be 4-byte aligned");
+  } else if (router->token_ids) {
+    return fail(MOE_ERR_INVALID_ARG, "token_ids given without a hash table (tid2eid)");
+  }
   const bool with_shared = !sh.partial || shared != nullptr;
   if (router->shared_gate && with_shared) {
     if (cfg->shared_inter <= 0)
@@ -482,10 +499,8 @@ moe_status validate_impl(const moe_cfg* cfg, const moe_router* router,
   } else if (shared) {
     return fail(MOE_ERR_INVALID_ARG, "shared is given but shared_inter == 0");
   }
-  moe_cfg cc = *cfg;
-  if (sh.partial && path == MOE_PATH_DECODE) cc.accum_mode = MOE_ACCUM_ATOMIC_F32;
   const size_t need =
-      layout(&cc, n_tokens, path, router->shared_gate != nullptr && with_shared).total;
+      layout(cfg, n_tokens, path, router->shared_gate != nullptr && with_shared).total;
   if (workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace too small: need %zu bytes, have %zu", need,
                 workspace_bytes);
@@ -524,13 +539,15 @@ moe_status forward_impl(const moe_cfg* cfg, const moe_router* router, const moe_
   a.H = cfg->hidden;
   a.I = cfg->inter;
   a.E = cfg->num_experts;
+  a.EW = a.E + cfg->zero_experts;
+  a.tid2eid = router->tid2eid;
+  a.token_ids = router->token_ids;
+  a.vocab = router->vocab;
   a.k = cfg->top_k;
   a.I_s = shared ? cfg->shared_inter : 0;
   a.scoring = cfg->scoring;
   a.renorm = cfg->norm_topk_prob;
-  // a share's slots outside its range are never written, so the slot-order
-  // blend would wait for them: a share always accumulates atomically
-  a.atomic = sh.partial || cfg->accum_mode == MOE_ACCUM_ATOMIC_F32;
+  a.atomic = cfg->accum_mode == MOE_ACCUM_ATOMIC_F32;
   a.rsf = cfg->routed_scaling_factor;
   a.e_lo = sh.lo;
   a.e_hi = sh.hi;
@@ -572,7 +589,7 @@ moe_status forward_impl(const moe_cfg* cfg, const moe_router* router, const moe_
   const int rcpr = a.H / 8;
   a.r_wpr = 1;
   while (a.r_wpr < 4 && a.r_wpr * 64 * 4 < rcpr) a.r_wpr <<= 1;
-  const int rrows = a.E + (a.shared_gate ? 1 : 0);
+  const int rrows = a.EW + (a.shared_gate ? 1 : 0);
   const int rows_per_wg = 4 / a.r_wpr;
   a.nR = (rrows + rows_per_wg - 1) / rows_per_wg;
   a.nGs = a.I_s > 0 ? a.gs.tiles : 0;

@@ -55,9 +55,10 @@ __global__ __launch_bounds__(kGThreads) void k_g_router(GroupedArgs a) {
   ARow rows[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    // rows 0..E-1: the router; row E (with a shared-expert gate): w_sg
+    // rows 0..EW-1: the router (E experts and the zero experts); row EW
+    // (with a shared-expert gate): w_sg
     const int e = min(rb * kGRowsPerWG + 32 * wave + 16 * t + (lane & 15), a.ER - 1);
-    const uint16_t* wr = e < a.E ? a.router_w + (int64_t)e * a.H : a.shared_gate;
+    const uint16_t* wr = e < a.EW ? a.router_w + (int64_t)e * a.H : a.shared_gate;
     rows[t].data = reinterpret_cast<const uint8_t*>(wr + c0 * kGKC);
     rows[t].scales = nullptr;
   }
@@ -106,6 +107,9 @@ __global__ __launch_bounds__(kGThreads) void k_g_topk(GroupedArgs a) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kGThreads / 64) + (threadIdx.x >> 6);
   if (t < a.N) {
+    const int id = a.tid2eid ? a.token_ids[t] : 0;  // hash routing: the token's id
+    float bv[4];
+    load_bias4(a.tid2eid ? nullptr : a.router_bias, a.EW, lane, bv);
     // sum the K-range partials of the lane's four logits in ascending range
     // order; lanes read consecutive experts, 16 ranges at a time
     const int ks = a.ksplit;
@@ -118,7 +122,7 @@ __global__ __launch_bounds__(kGThreads) void k_g_topk(GroupedArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int e = lane + 64 * i;
-          v[i][q] = (e < a.E && s0 + q < ks) ? p[e] : 0.f;
+          v[i][q] = (e < a.EW && s0 + q < ks) ? p[e] : 0.f;
         }
       }
 #pragma unroll
@@ -129,23 +133,24 @@ __global__ __launch_bounds__(kGThreads) void k_g_topk(GroupedArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
-      if (e < a.E) {
-        if (a.out_logits) a.out_logits[(int64_t)t * a.E + e] = zv[i];
+      if (e < a.EW) {
+        if (a.out_logits) a.out_logits[(int64_t)t * a.EW + e] = zv[i];
       } else {
         zv[i] = -INFINITY;
       }
     }
     if (a.shared_gate && lane == 0) {
-      // the shared-expert weight sigmoid(x . w_sg), from router row E
+      // the shared-expert weight sigmoid(x . w_sg), from router row EW
       float g = 0.f;
-      for (int q = 0; q < ks; ++q) g += a.zpart[((int64_t)t * ks + q) * a.ER + a.E];
+      for (int q = 0; q < ks; ++q) g += a.zpart[((int64_t)t * ks + q) * a.ER + a.EW];
       a.gamma[t] = 1.0f / (1.0f + expf(-g));
     }
     int my_e;
     float w;
-    float bv[4];
-    load_bias4(a.router_bias, a.E, lane, bv);
-    topk_wave(zv, bv, a.E, a.k, a.scoring, a.renorm, a.rsf, lane, my_e, w);
+    if (!route_token(zv, bv, a.router_bias != nullptr, a.tid2eid, a.vocab, id, a.EW, a.k,
+                     a.scoring, a.renorm, a.rsf, lane, my_e, w) &&
+        lane == 0)
+      __hip_atomic_fetch_or(a.err, kErrHashInput, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (lane < a.k) {
       const int sl = t * a.k + lane;
       st_dev(a.idx + sl, my_e);
@@ -283,7 +288,7 @@ __device__ void group_slots(const GroupedArgs& a, uint4* g_lds) {
         const int sl = s0 + q * kT + tid;
         const int e = ev[q] - a.e_lo;  // local expert index
         if (sl < nslots && (e < 0 || e >= E)) {
-          a.inv[sl] = -1;  // another share's expert
+          a.inv[sl] = -1;  // another share's expert, or a zero expert
           continue;
         }
         if (e < e0 || e >= e1) continue;

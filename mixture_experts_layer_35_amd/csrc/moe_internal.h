@@ -29,8 +29,9 @@ struct DevProj {
 // plan) carry the call's tag, so they never need clearing. Counters sit on
 // their own 128-byte lines so pollers and atomics do not pile onto one line.
 constexpr int kLineWords = 32;    // 128 bytes
-constexpr int kDoneGroups = 64;
-constexpr int kSharedLines = 4;  // done counters of the shared expert's gate+up (one line each)   // workgroup i reports to done group i % 64
+constexpr int kDoneGroups = 64;   // workgroup i reports to done group i % 64
+constexpr int kSharedLines = 4;   // done counters of the shared expert's gate+up (one line each)
+constexpr unsigned kErrHashInput = 1u << 16;  // sticky error bit: invalid hash-routing input
 constexpr int kPlanStride = 16;   // 64-bit plan words per unit (one line)
 struct Ctl {
   unsigned done;   // done groups finished
@@ -47,10 +48,14 @@ struct Ctl {
   // the plan: unit u, token t: words u * kPlanStride + 2t (info) and + 2t + 1
   // (routing weight), both tagged
   unsigned long long plan[256 * kPlanStride];
+  // per routing slot t * k + j, tagged: 1 if the slot's expert is computed by
+  // this call (not a zero expert, not another share's), else 0; the
+  // slot-order blend skips the others
+  unsigned long long slot_real[kNmax * 16];
 };
 // the error word is bytes 128..131
-static_assert(sizeof(Ctl) ==
-                  384 + kDoneGroups * 128 + kNmax * 256 * 8 + kNmax * 8 + 256 * kPlanStride * 8,
+static_assert(sizeof(Ctl) == 384 + kDoneGroups * 128 + kNmax * 256 * 8 + kNmax * 8 +
+                                 256 * kPlanStride * 8 + kNmax * 16 * 8,
               "Ctl layout");
 
 // Plan info word (high half of the tagged word):
@@ -74,7 +79,11 @@ struct DecodeArgs {
   const uint16_t* shared_gate;  // [H] BF16 or null: shared output weighted by sigmoid(x . w_sg)
   DevProj gate, up, down, sgate, sup, sdown;
   int N, H, I, E, k, I_s, scoring, renorm, atomic, maxu;
+  int EW;          // router width: E experts and the zero experts
   int e_lo, e_hi;  // experts computed: [e_lo, e_hi); weights hold these only
+  const int32_t* tid2eid;    // hash routing table [vocab, k], or null
+  const int32_t* token_ids;  // [N]
+  int vocab;
   float rsf;
   // phases (workgroup id ranges, in this order): router, shared gate+up,
   // routed gate+up, shared down, routed down
@@ -125,7 +134,12 @@ struct GroupedArgs {
   const uint16_t* shared_gate;  // [H] BF16 or null: shared output weighted by sigmoid(x . w_sg)
   DevProj gate, up, down, sgate, sup, sdown;
   int N, H, I, E, k, I_s, scoring, renorm, atomic;
-  int ER;  // router rows: E, plus the shared gate's row
+  int EW;  // router width: E experts and the zero experts
+  int ER;  // router rows: EW, plus the shared gate's row
+  const int32_t* tid2eid;    // hash routing table [vocab, k], or null
+  const int32_t* token_ids;  // [N]
+  int vocab;
+  unsigned* err;  // the workspace's sticky error word
   int e_lo, EL;  // experts computed: e_lo .. e_lo + EL - 1; weights hold these only
   float rsf;
   int nt;      // 16-token MFMA tiles per pass (1, 2, 4 or 8)
@@ -139,7 +153,7 @@ struct GroupedArgs {
   int gu_s, gu_r;   // gate+up: shared workgroups, workgroups per routed unit
   int dn_s, dn_r;   // down: same
   // workspace
-  float* zpart;      // [N, ksplit, ER] partial router logits (row E: the shared gate)
+  float* zpart;      // [N, ksplit, ER] partial router logits (row EW: the shared gate)
   float* gamma;      // [N] shared-expert weights sigmoid(x . w_sg) (with a gate)
   unsigned* ticket;  // top-k workgroups finished (zeroed by the router kernel)
   uint32_t* mask;    // [EL, W] bit t of word t/32: token t routes to expert e_lo + e

@@ -352,13 +352,14 @@ __device__ __forceinline__ void topk_and_plan(const DecodeArgs& a, TopkScratch* 
   __builtin_amdgcn_s_setprio(3);
   // the bias does not depend on the logits: read it before waiting for them
   float bv[4];
-  load_bias4(a.router_bias, a.E, lane, bv);
+  load_bias4(a.tid2eid ? nullptr : a.router_bias, a.EW, lane, bv);
   for (int t = wave; t < a.N; t += kThreads / 64) {
+    const int id = a.tid2eid ? a.token_ids[t] : 0;  // hash routing: the token's id
     const u64* zrow = a.ctl->zlog + t * 256;
     u64 zw[4] = {(u64)tag, (u64)tag, (u64)tag, (u64)tag};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i < a.E) zw[i] = ld_coh64(zrow + lane + 64 * i);
+      if (lane + 64 * i < a.EW) zw[i] = ld_coh64(zrow + lane + 64 * i);
     unsigned spins = 0;
     while (!__all((unsigned)zw[0] == tag && (unsigned)zw[1] == tag && (unsigned)zw[2] == tag &&
                   (unsigned)zw[3] == tag)) {
@@ -375,18 +376,23 @@ __device__ __forceinline__ void topk_and_plan(const DecodeArgs& a, TopkScratch* 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
-      zv[i] = e < a.E ? tag_value(zw[i]) : -INFINITY;
-      if (a.out_logits && e < a.E) a.out_logits[(size_t)t * a.E + e] = zv[i];
+      zv[i] = e < a.EW ? tag_value(zw[i]) : -INFINITY;
+      if (a.out_logits && e < a.EW) a.out_logits[(size_t)t * a.EW + e] = zv[i];
     }
     int my_e;
     float w;
-    topk_wave(zv, bv, a.E, a.k, a.scoring, a.renorm, a.rsf, lane, my_e, w);
+    if (!route_token(zv, bv, a.router_bias != nullptr, a.tid2eid, a.vocab, id, a.EW, a.k,
+                     a.scoring, a.renorm, a.rsf, lane, my_e, w) &&
+        lane == 0)
+      set_error(a, kErrHashInput);
     if (lane < a.k) {
       const int sl = t * a.k + lane;
       if (a.out_idx) a.out_idx[sl] = (uint32_t)my_e;
       if (a.out_w) a.out_w[sl] = w;
       s->idx[sl] = my_e;
       s->w[sl] = w;
+      const bool real = my_e >= a.e_lo && my_e < a.e_hi;
+      st_coh64(&a.ctl->slot_real[sl], tagged_u(real ? 1u : 0u, tag));
     }
   }
   __syncthreads();
@@ -461,11 +467,11 @@ __device__ __forceinline__ void router_phase(const DecodeArgs& a, int wg, uint4*
   const int q = wave & (wpr - 1);
   const int e = wg * ((kThreads / 64) / wpr) + wave / wpr;
   // rows 0..E-1: the router; row E (with a shared-expert gate): w_sg
-  const bool has_row = e < a.E + (a.shared_gate ? 1 : 0);
+  const bool has_row = e < a.EW + (a.shared_gate ? 1 : 0);
   float acc[kNmax] = {0.f, 0.f, 0.f, 0.f};
   if (has_row) {
     const int cpr = a.H / 8;
-    const uint8_t* wrow = e < a.E
+    const uint8_t* wrow = e < a.EW
                               ? reinterpret_cast<const uint8_t*>(a.router_w) + (size_t)e * a.H * 2
                               : reinterpret_cast<const uint8_t*>(a.shared_gate);
     const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.x);
@@ -514,7 +520,7 @@ __device__ __forceinline__ void router_phase(const DecodeArgs& a, int wg, uint4*
 #pragma unroll
     for (int t = 0; t < kNmax; ++t)
       if (t < a.N)
-        st_coh64(e < a.E ? a.ctl->zlog + t * 256 + e : a.ctl->glog + t, tagged(acc[t], tag));
+        st_coh64(e < a.EW ? a.ctl->zlog + t * 256 + e : a.ctl->glog + t, tagged(acc[t], tag));
   }
   // the last router workgroup (it waits only on lower ids) routes
   if (wg != a.nR - 1) return;
@@ -672,9 +678,28 @@ __device__ __forceinline__ void gate_up_phase(const DecodeArgs& a, int wg, uint4
 // Phase D: down projections and the blend of each finished row block.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void blend_block(const DecodeArgs& a, int bt, unsigned tag) {
+  __shared__ unsigned s_real[kNmax * 16];
   const int r0 = bt * a.blend_rows;
   const int r1 = min(a.H, r0 + a.blend_rows);
   const int rows = r1 - r0;
+  if (!a.atomic) {
+    // which slots have words (published with the routing)
+    if ((int)threadIdx.x < a.N * a.k) {
+      const u64* p = &a.ctl->slot_real[threadIdx.x];
+      u64 v = ld_coh64(p);
+      unsigned spins = 0;
+      while ((unsigned)v != tag) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > a.spin_limit) {
+          set_error(a, 8u);
+          break;
+        }
+        v = ld_coh64(p);
+      }
+      s_real[threadIdx.x] = (unsigned)(v >> 32);
+    }
+    __syncthreads();
+  }
   for (int i = threadIdx.x; i < a.N * rows; i += kThreads) {
     const int t = i / rows;
     const int r = r0 + (i - t * rows);
@@ -684,10 +709,13 @@ __device__ __forceinline__ void blend_block(const DecodeArgs& a, int bt, unsigne
       y = ld_coh(p);
       st_coh(p, 0.f);  // leave the accumulator zeroed for the next call
     } else {
-      // slots in order, then the shared expert
+      // slots in order, then the shared expert; a slot whose expert no
+      // workgroup of this call computes (a zero expert, another share's
+      // expert) has no words and adds nothing
       const int ns = a.k + (a.I_s > 0 ? 1 : 0);
       for (int j = 0; j < ns; ++j) {
         const int slot = j < a.k ? t * a.k + j : a.N * a.k + t;
+        if (j < a.k && !s_real[slot]) continue;
         const u64* p = a.dbuf + (size_t)slot * a.H + r;
         u64 v = ld_coh64(p);
         unsigned spins = 0;

@@ -67,10 +67,11 @@ __device__ __forceinline__ void load_bias4(const float* bias, int E, int lane, f
 }
 
 // Top-k routing of one token by one wave ("forward_k3.rs",
-// MoeLayer::forward_k3, step 2; "forward_batched.rs", the routing step). The
-// router logits sit four per lane: expert lane + 64 i in zv[i] (-inf past E).
-// Selection score: the logit (softmax) or sigmoid(logit) + correction bias
-// (sigmoid). Keys order by (score, -expert), so equal scores go to the lower
+// MoeLayer::forward_k3, step 2; "forward_batched.rs", the routing step and
+// its softmax+bias arm). The router logits sit four per lane: expert lane +
+// 64 i in zv[i] (-inf past the router width E). Selection score: the logit
+// (softmax, no bias), softmax(logit) + correction bias (softmax with a bias),
+// or sigmoid(logit) + correction bias (sigmoid). Keys order by (score, -expert), so equal scores go to the lower
 // expert index. bv holds the correction bias of the same four experts (read
 // by the caller ahead of the logits; 0 without a bias). Each lane sorts its
 // four keys once (a five-exchange network);
@@ -79,9 +80,18 @@ __device__ __forceinline__ void load_bias4(const float* bias, int E, int lane, f
 // sigmoid of the chosen logits (no bias), optionally divided by their sum,
 // then times the routed scaling factor. Lane j < k returns the j-th choice
 // and its weight.
-__device__ __forceinline__ void topk_wave(const float zv[4], const float bv[4], int E, int k,
-                                          int scoring, int renorm, float rsf, int lane,
-                                          int& my_e, float& my_w) {
+__device__ __forceinline__ void topk_wave(const float zv[4], const float bv[4], bool has_bias,
+                                          int E, int k, int scoring, int renorm, float rsf,
+                                          int lane, int& my_e, float& my_w) {
+  float zmax = 0.f, zsum = 1.f;
+  if (scoring == 0) {
+    zmax = wave_max_dpp(fmaxf(fmaxf(zv[0], zv[1]), fmaxf(zv[2], zv[3])));
+    float p = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i < E) p += expf(zv[i] - zmax);
+    zsum = wave_sum_dpp(p);
+  }
   // key: hi = ordered score bits, lo = ~expert (larger lo = lower expert);
   // an absent expert has hi = lo = 0, below every real key
   uint32_t hi[4], lo[4];
@@ -91,19 +101,13 @@ __device__ __forceinline__ void topk_wave(const float zv[4], const float bv[4], 
     const int e = lane + 64 * i;
     const bool in = e < E;
     float sc = zv[i];
-    if (scoring == 1) sc = 1.0f / (1.0f + expf(-zv[i])) + bv[i];
+    if (scoring == 1)
+      sc = 1.0f / (1.0f + expf(-zv[i])) + bv[i];
+    else if (has_bias)
+      sc = expf(zv[i] - zmax) / zsum + bv[i];
     hi[i] = in ? ordered_bits(sc) : 0u;
     lo[i] = in ? 0xffffffffu - (uint32_t)e : 0u;
     zz[i] = zv[i];
-  }
-  float zmax = 0.f, zsum = 1.f;
-  if (scoring == 0) {
-    zmax = wave_max_dpp(fmaxf(fmaxf(zv[0], zv[1]), fmaxf(zv[2], zv[3])));
-    float p = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i < E) p += expf(zv[i] - zmax);
-    zsum = wave_sum_dpp(p);
   }
   // sort the lane's four keys, largest first (branch-free exchanges)
   auto cx = [&](int x, int y) {
@@ -162,6 +166,72 @@ __device__ __forceinline__ void topk_wave(const float zv[4], const float bv[4], 
   if (lane < k) w = (scoring == 0) ? expf(my_z - zmax) / zsum : 1.0f / (1.0f + expf(-my_z));
   if (renorm) w = w / wave_sum_dpp(w);
   my_w = w * rsf;
+}
+
+// Hash routing of one token by one wave ("forward_batched.rs", the
+// hash-routing branch): lane j < k takes expert row[j] of the token's table
+// row; the weights are the unbiased softmax (over all E logits) or sigmoid of
+// those experts' logits, then renormalisation and the routed scaling factor
+// as in topk_wave. Returns false (on every lane) if the row has an expert
+// outside [0, E) or the same expert twice; such a slot gets expert E (past
+// every expert, so it adds nothing) and weight 0.
+__device__ __forceinline__ bool hash_wave(const float zv[4], const int32_t* row, int E, int k,
+                                          int scoring, int renorm, float rsf, int lane,
+                                          int& my_e, float& my_w) {
+  int e = lane < k ? row[lane] : 0;
+  const bool in = e >= 0 && e < E;
+  // a repeat of an earlier lane's expert: compare with each lane i < k
+  bool dup = false;
+  for (int i = 0; i < k; ++i) {
+    const int ei = __shfl(e, i, 64);
+    dup = dup || (i < lane && ei == e);
+  }
+  const bool bad = lane < k && (!in || dup);
+  const bool ok = __ballot(bad) == 0ull;
+  e = in ? e : 0;
+  // the chosen logit: expert e sits at lane e % 64, register e / 64
+  const int src = e & 63, reg = e >> 6;
+  const float z0 = __shfl(zv[0], src, 64), z1 = __shfl(zv[1], src, 64);
+  const float z2 = __shfl(zv[2], src, 64), z3 = __shfl(zv[3], src, 64);
+  const float z = reg == 0 ? z0 : (reg == 1 ? z1 : (reg == 2 ? z2 : z3));
+  float zmax = 0.f, zsum = 1.f;
+  if (scoring == 0) {
+    zmax = wave_max_dpp(fmaxf(fmaxf(zv[0], zv[1]), fmaxf(zv[2], zv[3])));
+    float p = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i < E) p += expf(zv[i] - zmax);
+    zsum = wave_sum_dpp(p);
+  }
+  float w = 0.f;
+  if (lane < k && !bad) w = (scoring == 0) ? expf(z - zmax) / zsum : 1.0f / (1.0f + expf(-z));
+  if (renorm) {
+    const float sum = wave_sum_dpp(w);
+    w = sum > 0.f ? w / sum : 0.f;
+  }
+  my_w = w * rsf;
+  my_e = bad ? E : e;
+  return ok;
+}
+
+// Route one token with one wave: hash routing when a table is given (id is
+// the token's id, read by the caller), else top-k selection. Returns false
+// for an invalid hash input (id outside [0, vocab), or a bad table row); the
+// token's slots then get expert E (past every expert) and weight 0.
+__device__ __forceinline__ bool route_token(const float zv[4], const float bv[4], bool has_bias,
+                                            const int32_t* tid2eid, int vocab, int id, int E,
+                                            int k, int scoring, int renorm, float rsf, int lane,
+                                            int& my_e, float& my_w) {
+  if (tid2eid) {
+    if (id < 0 || id >= vocab) {
+      my_e = E;
+      my_w = 0.f;
+      return false;
+    }
+    return hash_wave(zv, tid2eid + (size_t)id * k, E, k, scoring, renorm, rsf, lane, my_e, my_w);
+  }
+  topk_wave(zv, bv, has_bias, E, k, scoring, renorm, rsf, lane, my_e, my_w);
+  return true;
 }
 
 }  // namespace moe

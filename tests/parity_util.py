@@ -5,7 +5,7 @@ import numpy as np
 import torch
 
 import synth
-from oracle import (bf16_to_f64, group_slots, moe_forward, route, router_logits,
+from oracle import (bf16_to_f64, group_slots, moe_forward, route, route_hash, router_logits,
                     selection_scores)
 
 # consecutive gap among the top k+1 selection scores; about 100x the FP32
@@ -38,7 +38,7 @@ def bits(t):
     return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-def run_hip(layer, x, accum=None, out=None, path="auto"):
+def run_hip(layer, x, accum=None, out=None, path="auto", token_ids=None):
     from mixture_experts_layer_35_amd import Layer
     n = x.shape[0]
     cfg = layer["cfg"]
@@ -46,10 +46,11 @@ def run_hip(layer, x, accum=None, out=None, path="auto"):
     dev = x.device
     idx = torch.full((n, cfg["k"]), 0xFFFF, dtype=torch.int32, device=dev)
     w = torch.full((n, cfg["k"]), float("nan"), dtype=torch.float32, device=dev)
-    logits = torch.full((n, cfg["E"]), float("nan"), dtype=torch.float32, device=dev)
+    width = cfg["E"] + cfg.get("Z", 0)
+    logits = torch.full((n, width), float("nan"), dtype=torch.float32, device=dev)
     if out is None:
         out = torch.full_like(x, float("nan"))
-    L.forward(x, out=out, idx=idx, weights=w, logits=logits)
+    L.forward(x, out=out, idx=idx, weights=w, logits=logits, token_ids=token_ids)
     torch.cuda.synchronize()
     assert device_error(L) == 0, "a workgroup wait expired"
     return out, idx, w, logits, L
@@ -72,7 +73,8 @@ def check_grouping(L, n, ref_idx, num_experts, expert_range=None):
     """The grouped path's permutation against the oracle's, bit for bit
     (of one expert-parallel share's experts, with ``expert_range``)."""
     g = L.grouping(n)
-    ref = group_slots(ref_idx, num_experts, pad=16, expert_range=expert_range)
+    ref = group_slots(ref_idx, num_experts, pad=16,
+                      expert_range=(0, num_experts) if expert_range is None else expert_range)
     units = ref["units"]
     U = len(units)
     assert g["U"] == U, (g["U"], U)
@@ -86,7 +88,8 @@ def check_grouping(L, n, ref_idx, num_experts, expert_range=None):
     assert np.array_equal(g["inv"], ref["inv"])
 
 
-def check_against_oracle(layer, x, accum=None, rows=None, label="", path="auto", tokens=None):
+def check_against_oracle(layer, x, accum=None, rows=None, label="", path="auto", tokens=None,
+                         token_ids=None):
     """Run the HIP path and the oracle on the same inputs and assert the
     bar: indices bit-exact, weights within W_RTOL, logits within 1e-5 (abs,
     relative to their scale), per-token relative L2 of the output within
@@ -99,11 +102,16 @@ def check_against_oracle(layer, x, accum=None, rows=None, label="", path="auto",
     cfg = npl["cfg"]
     xb = bits(x)
     n = xb.shape[0]
-    out, idx, w, logits, L = run_hip(layer, x, accum=accum, path=path)
+    out, idx, w, logits, L = run_hip(layer, x, accum=accum, path=path, token_ids=token_ids)
+    ids = None if token_ids is None else token_ids.cpu().numpy()
     # routing of every token
     z = router_logits(bf16_to_f64(xb), bf16_to_f64(npl["router"]["weight"]))
-    ref_idx, ref_w = route(z, cfg["k"], cfg["scoring"], npl["router"]["bias"], cfg["renorm"],
-                           cfg["rsf"])
+    if npl["router"].get("tid2eid") is not None:
+        ref_idx, ref_w = route_hash(z, npl["router"]["tid2eid"], ids, cfg["k"], cfg["scoring"],
+                                    cfg["renorm"], cfg["rsf"])
+    else:
+        ref_idx, ref_w = route(z, cfg["k"], cfg["scoring"], npl["router"]["bias"],
+                               cfg["renorm"], cfg["rsf"])
     got_idx = idx.cpu().numpy().astype(np.int64)
     assert np.array_equal(got_idx, ref_idx), f"{label}: indices differ\n{got_idx}\n{ref_idx}"
     got_w = w.cpu().numpy().astype(np.float64)
@@ -117,8 +125,9 @@ def check_against_oracle(layer, x, accum=None, rows=None, label="", path="auto",
     o = bf16_to_f64(bits(out))
     assert np.isfinite(o).all(), f"{label}: non-finite output (unwritten rows?)"
     tok = np.arange(n) if tokens is None else np.asarray(tokens)
-    ref = moe_forward(cfg, npl, xb[tok], rows=rows)
+    ref = moe_forward(cfg, npl, xb[tok], rows=rows, token_ids=None if ids is None else ids[tok])
     sel = ref["rows"]
     err = rel_l2_per_token(o[tok][:, sel], ref["y"])
     assert err.max() <= OUT_RTOL, f"{label}: rel L2 {err}"
+    assert device_error(L) == 0, f"{label}: device error word set"
     return {"rel_l2": float(err.max()), "out": out, "grouped": grouped}

@@ -31,7 +31,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version():
-    assert moe.abi_version() == 3
+    assert moe.abi_version() == 4
 
 
 def _fake_weight(fmt, rows, cols, count, base):
@@ -214,10 +214,13 @@ def test_mixed_formats_within_set_refused():
     assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_UNSUPPORTED
 
 
-def test_softmax_with_bias_refused():
+def test_softmax_with_bias_accepted():
+    # the softmax+bias arm
     c, r, ex, sh = _c3()
     c.scoring = B.SCORING["softmax"]
-    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_UNSUPPORTED
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_OK
+    r.bias = FAKE + 4098
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
 
 
 def test_status_strings():
@@ -286,8 +289,7 @@ def test_ep_share_workspace_checked_against_the_same_size():
 
 
 def test_workspace_covers_a_decode_share_of_a_slot_mode_layer():
-    # a share on the decode path accumulates atomically even when the layer
-    # is configured for slot order: the one workspace size covers both
+    # the one workspace size covers a share's call as well as the layer's
     cfg = dict(H=2048, I=768, E=128, k=8, I_s=0, scoring="softmax", renorm=True, rsf=1.0)
     c = B.make_cfg(cfg, accum="slot")
     r = B.MoeRouter(FAKE, None)
@@ -299,3 +301,50 @@ def test_workspace_covers_a_decode_share_of_a_slot_mode_layer():
         assert need <= ws, n
         assert _share_call(c, r, local, 0, 32, None, n=n, ws=ws,
                            partial=FAKE + 4) == B.MOE_ERR_INVALID_ARG
+
+
+def test_zero_expert_router_width():
+    c, r, ex, sh = _c3()
+    c.zero_experts = 1  # 256 + 1 router columns
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_UNSUPPORTED
+    assert "router width" in B.last_error()
+    c.num_experts = 192
+    c.zero_experts = 64
+    ex = _fake_set("nvfp4", 7168, 2048, 192, FAKE)
+    assert B.validate(c, r, ex, sh, 4, B.workspace_bytes(c, 4)) == B.MOE_OK
+    c.zero_experts = -1
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_UNSUPPORTED
+    # top_k may exceed E when zero experts widen the router
+    c.num_experts, c.zero_experts, c.top_k = 4, 4, 6
+    ex = _fake_set("nvfp4", 7168, 2048, 4, FAKE)
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_OK
+    c.top_k = 9
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
+
+
+def test_zero_experts_grow_the_grouped_router_partials():
+    c, r, ex, sh = _c3()
+    c.num_experts, c.top_k = 128, 8
+    ex = _fake_set("nvfp4", 7168, 2048, 128, FAKE)
+    w0 = B.workspace_bytes(c, 64)
+    c.zero_experts = 64
+    assert B.workspace_bytes(c, 64) > w0
+
+
+def test_hash_routing_arguments():
+    c, r, ex, sh = _c3()
+    r.tid2eid = FAKE
+    r.vocab = 1000
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
+    assert "token_ids" in B.last_error()
+    r.token_ids = FAKE + 8192
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_OK
+    r.vocab = 0
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
+    r.vocab = 1000
+    r.token_ids = FAKE + 8194
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
+    r.tid2eid = None
+    r.token_ids = FAKE + 8192
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
+    assert "without a hash table" in B.last_error()

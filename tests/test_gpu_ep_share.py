@@ -101,7 +101,7 @@ def test_decode_shares_tiny(n):
 
 
 def test_decode_shares_slot_layer_shared_added_once_by_caller():
-    # a slot-mode layer: the shares accumulate atomically all the same
+    # a slot-mode layer: the slot-order sum skips the other shares' slots
     _run_shares("tiny_bf16", 4, 610, _split(8, 3), carrier=None, accum="slot",
                 label="decode tiny_bf16 slot G=3 no carrier")
 
