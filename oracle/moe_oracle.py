@@ -64,7 +64,10 @@ Readings where the pages are silent (each also listed in the design notes):
       zero_expert_num) are router columns E..E+Z-1 with no weights: routing
       runs over all E+Z columns, and a slot that chooses a zero expert adds
       nothing to the output while its weight still counts in the
-      renormalisation.
+      renormalisation;
+  R17 an NVFP4 router is dequantised exactly like the NVFP4 experts (E2M1
+      values, E4M3 scale per 16 columns, one FP32 tensor scale) and the
+      logits are x . W in full precision; the shared-expert gate stays BF16.
 """
 
 from __future__ import annotations
@@ -73,7 +76,7 @@ import numpy as np
 
 __all__ = [
     "e2m1_to_f64", "e8m0_to_f64", "e4m3fn_to_f64", "bf16_to_f64",
-    "unpack_fp4", "dequant", "router_logits", "selection_scores", "route",
+    "unpack_fp4", "dequant", "router_matrix", "router_logits", "selection_scores", "route",
     "softmax_rows", "routing_weights", "route_hash",
     "silu", "swiglu_expert", "moe_forward", "group_slots", "shared_gate_weight", "FORMATS",
 ]
@@ -199,6 +202,16 @@ def dequant(w: dict, e: int, rows=None) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Router and routing.
 # --------------------------------------------------------------------------
+
+def router_matrix(router: dict) -> np.ndarray:
+    """The router as FP64 [E + Z, H]: the BF16 ``weight``, or the dequantised
+    NVFP4 ``weight_q`` (a projection dict with count 1), the router GEMV and
+    GEMM that "forward_k3.rs", "forward_atomic_c4.rs" and "forward_ep.rs"
+    take when the layer has an NVFP4 gate (reading R17)."""
+    if router.get("weight_q") is not None:
+        return dequant(router["weight_q"], 0)
+    return bf16_to_f64(np.asarray(router["weight"]))
+
 
 def router_logits(x: np.ndarray, wr: np.ndarray) -> np.ndarray:
     """z[t, e] = sum_h x[t, h] * Wr[e, h]: one projection for all N tokens
@@ -345,7 +358,7 @@ def moe_forward(cfg: dict, layer: dict, x_bits, rows=None, expert_range=None,
     x = bf16_to_f64(np.asarray(x_bits))
     n, h = x.shape
     assert h == cfg["H"]
-    wr = bf16_to_f64(np.asarray(layer["router"]["weight"]))
+    wr = router_matrix(layer["router"])
     bias = layer["router"].get("bias")
     bias = None if bias is None else np.asarray(bias, np.float64)
     z = router_logits(x, wr)

@@ -198,6 +198,13 @@ def make_layer(name_or_cfg, device="cpu") -> dict:
         ranks = torch.randperm(EW, generator=gz).to(torch.float64) + 1.0
         wr[:, H - 1] = (-cfg["zipf"] * torch.log(ranks)).to(wr.dtype).to(device)
     router = {"weight": wr.to(torch.bfloat16).contiguous(), "bias": None, "shared_gate": None}
+    if cfg.get("router_fmt") == "nvfp4":
+        # the same N(0, 1/sqrt(H)) rows, quantised to NVFP4 (one projection of
+        # count 1); the BF16 weight is then absent
+        q = _quantize(wr.float().unsqueeze(0), "nvfp4")
+        q.update({"format": "nvfp4", "rows": EW, "cols": H, "count": 1})
+        router["weight_q"] = q
+        router["weight"] = None
     if cfg.get("shared_gate") and I_s > 0:
         # the shared-expert gate vector, N(0, 1/sqrt(H)) like a router row
         gg = _gen(device, cfg["cfg_id"], _TENSOR_IDS["shared_gate"])
@@ -237,7 +244,7 @@ def make_tokens(layer: dict, n: int, batch_seed: int = 0, accept=None,
     tokens are redrawn with the next attempt number."""
     cfg = layer["cfg"]
     H = cfg["H"]
-    device = layer["router"]["weight"].device
+    device = layer["experts"]["gate"]["data"].device
     rows = []
     for t in range(n):
         rows.append(_draw_token(cfg, device, n, batch_seed, t, 0))
@@ -261,7 +268,7 @@ def make_token_ids(layer: dict, n: int, batch_seed: int = 0) -> torch.Tensor:
     cfg = layer["cfg"]
     g = _gen("cpu", cfg["cfg_id"], _TENSOR_IDS["token_ids"], n, batch_seed)
     ids = torch.randint(0, cfg["hash_vocab"], (n,), generator=g, dtype=torch.int64)
-    return ids.to(torch.int32).to(layer["router"]["weight"].device).contiguous()
+    return ids.to(torch.int32).to(layer["experts"]["gate"]["data"].device).contiguous()
 
 
 def _draw_token(cfg, device, n, batch_seed, t, attempt) -> torch.Tensor:
@@ -289,6 +296,9 @@ def as_numpy(layer: dict) -> dict:
         return {k: (_np(v) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
     out = {"cfg": dict(layer["cfg"]),
            "router": {"weight": _np(layer["router"]["weight"]),
+                      "weight_q": (None if layer["router"].get("weight_q") is None else
+                                   {k: (_np(v) if isinstance(v, torch.Tensor) else v)
+                                    for k, v in layer["router"]["weight_q"].items()}),
                       "bias": _np(layer["router"]["bias"]),
                       "shared_gate": _np(layer["router"].get("shared_gate")),
                       "tid2eid": _np(layer["router"].get("tid2eid"))},
@@ -305,7 +315,8 @@ def clone_weights(layer: dict) -> dict:
     def proj(p):
         return {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
     out = dict(layer)
-    out["router"] = {k: (v.clone() if v is not None else None)
+    out["router"] = {k: (proj(v) if isinstance(v, dict) else
+                         (v.clone() if v is not None else None))
                      for k, v in layer["router"].items()}
     out["experts"] = {k: proj(v) for k, v in layer["experts"].items()}
     out["shared"] = None if layer["shared"] is None else {
@@ -332,7 +343,9 @@ def layer_bytes(layer: dict) -> dict:
     if layer["shared"] is not None:
         b_s = sum(projection_bytes(layer["shared"][k]) for k in ("gate", "up", "down"))
     r = layer["router"]
-    b_r = r["weight"].numel() * 2 + (0 if r["bias"] is None else r["bias"].numel() * 4)
+    b_r = (projection_bytes(r["weight_q"]) if r.get("weight_q") is not None
+           else r["weight"].numel() * 2)
+    b_r += 0 if r["bias"] is None else r["bias"].numel() * 4
     if r.get("shared_gate") is not None:
         b_r += r["shared_gate"].numel() * 2
     b_e_gu = sum(projection_bytes(ex[k]) for k in ("gate", "up"))

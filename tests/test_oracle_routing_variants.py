@@ -130,3 +130,32 @@ def test_zero_experts_count_in_renormalisation():
         np.testing.assert_allclose(
             ref["w"][t], routing_weights(z[t], ref["idx"][t], cfg["scoring"], True, cfg["rsf"]),
             rtol=1e-15)
+
+
+# ---- NVFP4 router ------------------------------------------------------------
+
+@pytest.mark.parametrize("ts", [1.0, 0.25])
+def test_nvfp4_router_equals_bf16_router_of_its_values(ts):
+    # with a power-of-two tensor scale every dequantised router weight (an
+    # E2M1 value times an E4M3 scale: at most 6 significant bits) is a BF16
+    # value, so a BF16 router holding those values must route and compute
+    # exactly alike
+    import torch
+    from oracle import dequant
+    cfg = synth.reduced("deepseek_v3_nvfp4", H=256, I=64, E=16, k=4, I_s=64, Z=2,
+                        router_fmt="nvfp4", name="nvfp4_router_pin")
+    npl = synth.as_numpy(synth.make_layer(cfg))
+    q = npl["router"]["weight_q"]
+    q["tensor_scale"] = np.full_like(q["tensor_scale"], ts)
+    w = dequant(q, 0)
+    wb = torch.from_numpy(w).to(torch.bfloat16)
+    assert np.array_equal(wb.double().numpy(), w), "values not BF16-exact"
+    bf = dict(npl)
+    bf["router"] = dict(npl["router"], weight=wb.view(torch.int16).numpy().view(np.uint16),
+                        weight_q=None)
+    x = synth.make_tokens(synth.make_layer(cfg), 6, 9).view(torch.int16).numpy().view(np.uint16)
+    a = moe_forward(cfg, npl, x)
+    b = moe_forward(cfg, bf, x)
+    assert np.array_equal(a["z"], b["z"])
+    assert np.array_equal(a["idx"], b["idx"])
+    assert np.array_equal(a["y"], b["y"])
