@@ -134,8 +134,8 @@ def test_zero_experts_count_in_renormalisation():
 
 # ---- NVFP4 router ------------------------------------------------------------
 
-@pytest.mark.parametrize("ts", [1.0, 0.25])
-def test_nvfp4_router_equals_bf16_router_of_its_values(ts):
+@pytest.mark.parametrize("mult", [1.0, 0.5])
+def test_nvfp4_router_equals_bf16_router_of_its_values(mult):
     # with a power-of-two tensor scale every dequantised router weight (an
     # E2M1 value times an E4M3 scale: at most 6 significant bits) is a BF16
     # value, so a BF16 router holding those values must route and compute
@@ -146,7 +146,9 @@ def test_nvfp4_router_equals_bf16_router_of_its_values(ts):
                         router_fmt="nvfp4", name="nvfp4_router_pin")
     npl = synth.as_numpy(synth.make_layer(cfg))
     q = npl["router"]["weight_q"]
-    q["tensor_scale"] = np.full_like(q["tensor_scale"], ts)
+    # the nearest power of two to the quantiser's own tensor scale
+    ts0 = float(q["tensor_scale"][0])
+    q["tensor_scale"] = np.full_like(q["tensor_scale"], mult * 2.0 ** round(math.log2(ts0)))
     w = dequant(q, 0)
     wb = torch.from_numpy(w).to(torch.bfloat16)
     assert np.array_equal(wb.double().numpy(), w), "values not BF16-exact"
