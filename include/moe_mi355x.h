@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum {
   MOE_OK = 0,
@@ -124,8 +124,26 @@ typedef struct {
   int32_t zero_experts;
 } moe_cfg;
 
+
 typedef struct {
-  const void* weight;  /* device, BF16 [E + Z, H], 16-byte aligned */
+  int32_t format;            /* moe_format */
+  const void* data;          /* device, 16-byte aligned */
+  size_t data_bytes;         /* must equal the size implied by format/count/rows/cols */
+  const void* scales;        /* device; NULL for BF16 */
+  size_t scale_bytes;        /* must equal the size implied by the format */
+  const float* tensor_scale; /* device FP32 [count] for NVFP4, else NULL */
+  int32_t rows, cols, count;
+} moe_weight;
+
+/* gate and up: rows = I (I_s), cols = H; down: rows = H, cols = I (I_s).
+ * All three projections of one set share one format. */
+typedef struct {
+  moe_weight gate, up, down;
+} moe_experts;
+
+typedef struct {
+  /* device, BF16 [E + Z, H], 16-byte aligned; NULL when weight_q is given */
+  const void* weight;
   /* device, FP32 [E + Z] correction bias, or NULL. It steers selection only:
    * sigmoid scoring selects on sigmoid(z) + bias, softmax scoring on
    * softmax(z) + bias ("forward_batched.rs", the softmax+bias arm
@@ -151,23 +169,14 @@ typedef struct {
   const int32_t* tid2eid;
   int32_t vocab;
   const int32_t* token_ids;
+  /* A quantised router in place of weight, or NULL: NVFP4 only (rows E + Z,
+   * cols H, count 1, the layout of moe_weight), the router weights
+   * dequantised in registers against BF16 activations, FP32 logits
+   * ("forward_k3.rs" and "forward_atomic_c4.rs", the NVFP4 router GEMV and
+   * GEMM taken when the layer has an NVFP4 gate; "forward_ep.rs", the same
+   * for one token). The shared-expert gate stays BF16. */
+  const moe_weight* weight_q;
 } moe_router;
-
-typedef struct {
-  int32_t format;            /* moe_format */
-  const void* data;          /* device, 16-byte aligned */
-  size_t data_bytes;         /* must equal the size implied by format/count/rows/cols */
-  const void* scales;        /* device; NULL for BF16 */
-  size_t scale_bytes;        /* must equal the size implied by the format */
-  const float* tensor_scale; /* device FP32 [count] for NVFP4, else NULL */
-  int32_t rows, cols, count;
-} moe_weight;
-
-/* gate and up: rows = I (I_s), cols = H; down: rows = H, cols = I (I_s).
- * All three projections of one set share one format. */
-typedef struct {
-  moe_weight gate, up, down;
-} moe_experts;
 
 /* Optional per-call outputs (each pointer may be NULL, device memory). */
 typedef struct {

@@ -36,7 +36,8 @@ class MoeCfg(ctypes.Structure):
 class MoeRouter(ctypes.Structure):
     _fields_ = [("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p),
                 ("shared_gate", ctypes.c_void_p), ("tid2eid", ctypes.c_void_p),
-                ("vocab", ctypes.c_int32), ("token_ids", ctypes.c_void_p)]
+                ("vocab", ctypes.c_int32), ("token_ids", ctypes.c_void_p),
+                ("weight_q", ctypes.c_void_p)]
 
 
 class MoeWeight(ctypes.Structure):
@@ -201,6 +202,10 @@ def make_router(r: dict) -> MoeRouter:
     if table is not None:
         m.tid2eid = _ptr(table)
         m.vocab = int(table.shape[0])
+    if r.get("weight_q") is not None:
+        # the struct must outlive every call: it rides on the router object
+        m._weight_q = make_weight(r["weight_q"])
+        m.weight_q = ctypes.addressof(m._weight_q)
     return m
 
 
@@ -249,7 +254,7 @@ class Layer:
         self.shared = make_experts(layer["shared"])
         self.max_tokens = max_tokens
         nbytes = workspace_bytes(self.cfg, max_tokens)
-        dev = layer["router"]["weight"].device
+        dev = layer["experts"]["gate"]["data"].device
         # zero-filled once: the counter head must start at zero (calls keep it so)
         self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
 

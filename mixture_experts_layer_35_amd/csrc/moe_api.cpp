@@ -190,8 +190,9 @@ struct GPlan {
 
 GPlan gplan(const moe_cfg* c, int n, bool gated) {
   GPlan g;
-  // router rows: E experts, Z zero experts (+ the shared gate)
-  const int ER = c->num_experts + c->zero_experts + (gated ? 1 : 0);
+  // router rows: E experts and Z zero experts in blocks of 128, plus a block
+  // of its own for the shared gate's row
+  const int EW = c->num_experts + c->zero_experts;
   const int mmax = n < 128 ? n : 128;  // tokens of one expert per pass
   g.nt = mmax <= 16 ? 1 : (mmax <= 32 ? 2 : (mmax <= 64 ? 4 : 8));
   const int T = 16 * g.nt;
@@ -199,7 +200,7 @@ GPlan gplan(const moe_cfg* c, int n, bool gated) {
   const int64_t slots = (int64_t)n * c->top_k;
   g.maxu = (int)(slots < c->num_experts ? slots : c->num_experts);
   const int chunks = c->hidden / moe::kGKC;
-  g.r_rb = (ER + moe::kGRowsPerWG - 1) / moe::kGRowsPerWG;
+  g.r_rb = (EW + moe::kGRowsPerWG - 1) / moe::kGRowsPerWG + (gated ? 1 : 0);
   g.r_tg = (n + T - 1) / T;
   // split H so that the router has about 256 workgroups
   int want = (256 + g.r_rb * g.r_tg - 1) / (g.r_rb * g.r_tg);
@@ -386,6 +387,8 @@ moe_status forward_grouped(const moe_cfg* cfg, const moe_router* router,
   else
     a.out = static_cast<uint16_t*>(out);
   a.router_w = static_cast<const uint16_t*>(router->weight);
+  a.router_fmt = router->weight_q ? moe::FMT_NVFP4_HOST : moe::FMT_BF16_HOST;
+  if (router->weight_q) a.router_q = to_dev(*router->weight_q);
   a.router_bias = router->bias;
   // the gate weights the shared expert's output: without it in this call,
   // its router row is not needed
@@ -459,9 +462,19 @@ moe_status validate_impl(const moe_cfg* cfg, const moe_router* router,
   int path;
   st = resolve_path(cfg, n_tokens, &path);
   if (st) return st;
-  if (!router || !router->weight) return fail(MOE_ERR_INVALID_ARG, "null router weight");
-  if (!aligned(router->weight, 16))
+  if (!router) return fail(MOE_ERR_INVALID_ARG, "null router");
+  if (!router->weight == !router->weight_q)
+    return fail(MOE_ERR_INVALID_ARG, "give exactly one of router weight (BF16) and weight_q");
+  if (router->weight && !aligned(router->weight, 16))
     return fail(MOE_ERR_INVALID_ARG, "router weight not 16-byte aligned");
+  if (router->weight_q) {
+    if (router->weight_q->format != MOE_FMT_NVFP4)
+      return fail(MOE_ERR_UNSUPPORTED, "a quantised router must be NVFP4, got %s",
+                  fmt_name(router->weight_q->format));
+    st = check_weight(*router->weight_q, "router", cfg->num_experts + cfg->zero_experts,
+                      cfg->hidden, 1);
+    if (st) return st;
+  }
   if (router->bias && !aligned(router->bias, 4))
     return fail(MOE_ERR_INVALID_ARG, "router bias not 4-byte aligned");
   if (router->tid2eid) {
@@ -558,6 +571,8 @@ moe_status forward_impl(const moe_cfg* cfg, const moe_router* router, const moe_
   else
     a.out = static_cast<uint16_t*>(out);
   a.router_w = static_cast<const uint16_t*>(router->weight);
+  a.router_fmt = router->weight_q ? moe::FMT_NVFP4_HOST : moe::FMT_BF16_HOST;
+  if (router->weight_q) a.router_q = to_dev(*router->weight_q);
   a.router_bias = router->bias;
   a.shared_gate = a.I_s > 0 ? static_cast<const uint16_t*>(router->shared_gate) : nullptr;
   a.gate = to_dev(experts->gate);

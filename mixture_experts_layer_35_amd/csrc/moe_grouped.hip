@@ -52,21 +52,14 @@ __global__ __launch_bounds__(kGThreads) void k_g_router(GroupedArgs a) {
   const int nch = min(a.kcps, a.H / kGKC - c0);
   const int t0 = tg * 16 * NT;
   const int m = min(a.N - t0, 16 * NT);
-  ARow rows[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    // rows 0..EW-1: the router (E experts and the zero experts); row EW
-    // (with a shared-expert gate): w_sg
-    const int e = min(rb * kGRowsPerWG + 32 * wave + 16 * t + (lane & 15), a.ER - 1);
-    const uint16_t* wr = e < a.EW ? a.router_w + (int64_t)e * a.H : a.shared_gate;
-    rows[t].data = reinterpret_cast<const uint8_t*>(wr + c0 * kGKC);
-    rows[t].scales = nullptr;
-  }
   const XRows x{a.x + (int64_t)t0 * a.H + c0 * kGKC, a.H, nullptr, m};
-  with_tiles<NT>((m + 15) >> 4, [&](auto ntc) {
+  // Row blocks of 128 rows: rows 0..EW-1 are the router (E experts and the
+  // zero experts, BF16 or NVFP4); with a shared-expert gate, the last block
+  // holds only row EW, w_sg (BF16), since one block streams one format.
+  const bool q_router = a.router_fmt == FMT_NVFP4;
+  const bool gate_block = a.shared_gate && rb == a.r_rb - 1;
+  auto store = [&](auto& acc, auto ntc, float scale) {
     constexpr int V = decltype(ntc)::value;
-    f32x4 acc[2][V];
-    stream_gemm<FMT_BF16, 2, V>(acc, rows, x, nch, g_lds);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -75,11 +68,48 @@ __global__ __launch_bounds__(kGThreads) void k_g_router(GroupedArgs a) {
         if (j < m) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int e = rb * kGRowsPerWG + 32 * wave + 16 * t + 4 * (lane >> 4) + r;
-            if (e < a.ER) a.zpart[((int64_t)(t0 + j) * a.ksplit + s) * a.ER + e] = acc[t][n][r];
+            const int lr = 32 * wave + 16 * t + 4 * (lane >> 4) + r;  // row in the block
+            int e;
+            if (gate_block)
+              e = lr == 0 ? a.EW : -1;
+            else
+              e = rb * kGRowsPerWG + lr;
+            if (e >= 0 && (gate_block || e < a.EW))
+              a.zpart[((int64_t)(t0 + j) * a.ksplit + s) * a.ER + e] = acc[t][n][r] * scale;
           }
         }
       }
+  };
+  ARow rows[2];
+  if (q_router && !gate_block) {
+    const MatView mq = gview(a.router_q, 0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int e = min(rb * kGRowsPerWG + 32 * wave + 16 * t + (lane & 15), a.EW - 1);
+      rows[t] = arow(mq, e);
+      rows[t].data += c0 * kGKC / 2;     // two E2M1 values per byte
+      rows[t].scales += c0 * kGKC / 16;  // one E4M3 scale per 16 values
+    }
+    with_tiles<NT>((m + 15) >> 4, [&](auto ntc) {
+      constexpr int V = decltype(ntc)::value;
+      f32x4 acc[2][V];
+      stream_gemm<FMT_NVFP4, 2, V>(acc, rows, x, nch, g_lds);
+      store(acc, ntc, mq.tensor_scale);
+    });
+    return;
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int e = min(rb * kGRowsPerWG + 32 * wave + 16 * t + (lane & 15), a.EW - 1);
+    const uint16_t* wr = gate_block ? a.shared_gate : a.router_w + (int64_t)e * a.H;
+    rows[t].data = reinterpret_cast<const uint8_t*>(wr + c0 * kGKC);
+    rows[t].scales = nullptr;
+  }
+  with_tiles<NT>((m + 15) >> 4, [&](auto ntc) {
+    constexpr int V = decltype(ntc)::value;
+    f32x4 acc[2][V];
+    stream_gemm<FMT_BF16, 2, V>(acc, rows, x, nch, g_lds);
+    store(acc, ntc, 1.0f);
   });
 }
 

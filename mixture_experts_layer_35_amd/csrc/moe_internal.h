@@ -11,6 +11,8 @@ namespace moe {
 constexpr int kNmax = 4;          // tokens per call on the decode path
 constexpr int kThreads = 256;     // threads per workgroup (4 waves)
 constexpr int FMT_NONE_HOST = 7;  // no shared expert (same value as FMT_NONE)
+constexpr int FMT_BF16_HOST = 0;   // the values of moe_format / the device FMT_ codes
+constexpr int FMT_NVFP4_HOST = 3;
 
 // One projection for all experts of a set, in the canonical layout.
 struct DevProj {
@@ -77,6 +79,8 @@ struct DecodeArgs {
   const uint16_t* router_w;
   const float* router_bias;
   const uint16_t* shared_gate;  // [H] BF16 or null: shared output weighted by sigmoid(x . w_sg)
+  DevProj router_q;             // the router as NVFP4 [EW, H] (router_fmt NVFP4), else unused
+  int router_fmt;               // FMT_BF16 (router_w) or FMT_NVFP4 (router_q)
   DevProj gate, up, down, sgate, sup, sdown;
   int N, H, I, E, k, I_s, scoring, renorm, atomic, maxu;
   int EW;          // router width: E experts and the zero experts
@@ -132,6 +136,8 @@ struct GroupedArgs {
   const uint16_t* router_w;
   const float* router_bias;
   const uint16_t* shared_gate;  // [H] BF16 or null: shared output weighted by sigmoid(x . w_sg)
+  DevProj router_q;             // the router as NVFP4 [EW, H] (router_fmt NVFP4), else unused
+  int router_fmt;               // FMT_BF16 (router_w) or FMT_NVFP4 (router_q)
   DevProj gate, up, down, sgate, sup, sdown;
   int N, H, I, E, k, I_s, scoring, renorm, atomic;
   int EW;  // router width: E experts and the zero experts

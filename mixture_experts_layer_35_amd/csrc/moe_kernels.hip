@@ -457,6 +457,57 @@ __device__ __forceinline__ void topk_and_plan(const DecodeArgs& a, TopkScratch* 
   }
 }
 
+// This wave's part (chunks q*64*ITR + ..., stride wpr*64*ITR) of one router
+// row's dot products with the N tokens, format RF: BF16 (8 values per chunk,
+// ITR = 4 chunks per lane per round) or NVFP4 (32 values per chunk with two
+// E4M3 block scales, ITR = 1, so that the matching 64 bytes of x per token
+// stay few registers). x is read from global memory (L2).
+template <int RF>
+__device__ __forceinline__ void router_row(const DecodeArgs& a, const uint8_t* wrow,
+                                           const uint8_t* srow, int q, int wpr, int lane,
+                                           float (&acc)[kNmax]) {
+  constexpr int VPC = Fmt<RF>::VPC;
+  constexpr int XU = VPC / 8;  // 16-byte x loads per token and chunk
+  constexpr int ITR = RF == FMT_BF16 ? IT : 1;
+  const int cpr = a.H / VPC;
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.x);
+  for (int c0 = q * 64 * ITR; c0 < cpr; c0 += wpr * 64 * ITR) {
+    // router and token loads go out together
+    uint4 wq[ITR], xq[ITR][kNmax][XU];
+    uint32_t sc[ITR];
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int it = 0; it < ITR; ++it) {
+      const int c = c0 + it * 64 + lane;
+      const bool in = c < cpr;
+      wq[it] = in ? ldg16(wrow + (size_t)c * 16) : z;
+      sc[it] = (RF != FMT_BF16 && in) ? load_chunk_scale<RF>(srow, c) : 0u;
+#pragma unroll
+      for (int t = 0; t < kNmax; ++t)
+#pragma unroll
+        for (int u = 0; u < XU; ++u)
+          xq[it][t][u] = (in && t < a.N)
+                             ? ldg16(xb + (size_t)t * a.H * 2 + (size_t)c * VPC * 2 + u * 16)
+                             : z;
+    }
+#pragma unroll
+    for (int it = 0; it < ITR; ++it) {
+#pragma unroll
+      for (int t = 0; t < kNmax; ++t) {
+        uint32_t xv[VPC / 2];
+#pragma unroll
+        for (int u = 0; u < XU; ++u) {
+          xv[4 * u + 0] = xq[it][t][u].x;
+          xv[4 * u + 1] = xq[it][t][u].y;
+          xv[4 * u + 2] = xq[it][t][u].z;
+          xv[4 * u + 3] = xq[it][t][u].w;
+        }
+        acc[t] += chunk_dot<RF>(wq[it], sc[it], xv);
+      }
+    }
+  }
+}
+
 __device__ __forceinline__ void router_phase(const DecodeArgs& a, int wg, uint4* smem,
                                              float* s_part, unsigned tag) {
   const int wave = threadIdx.x >> 6;
@@ -466,36 +517,22 @@ __device__ __forceinline__ void router_phase(const DecodeArgs& a, int wg, uint4*
   const int wpr = a.r_wpr;
   const int q = wave & (wpr - 1);
   const int e = wg * ((kThreads / 64) / wpr) + wave / wpr;
-  // rows 0..E-1: the router; row E (with a shared-expert gate): w_sg
+  // rows 0..EW-1: the router (BF16 or NVFP4); row EW (with a shared-expert
+  // gate): w_sg, BF16
   const bool has_row = e < a.EW + (a.shared_gate ? 1 : 0);
   float acc[kNmax] = {0.f, 0.f, 0.f, 0.f};
   if (has_row) {
-    const int cpr = a.H / 8;
-    const uint8_t* wrow = e < a.EW
-                              ? reinterpret_cast<const uint8_t*>(a.router_w) + (size_t)e * a.H * 2
-                              : reinterpret_cast<const uint8_t*>(a.shared_gate);
-    const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.x);
-    for (int c0 = q * 64 * IT; c0 < cpr; c0 += wpr * 64 * IT) {
-      // router and token loads go out together
-      uint4 wq[IT], xq[IT][kNmax];
-      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    if (e < a.EW && a.router_fmt == FMT_NVFP4) {
+      const MatView m = view_of(a.router_q, 0);
+      router_row<FMT_NVFP4>(a, m.data + (size_t)e * m.row_bytes,
+                            m.scales + (size_t)e * m.scale_row_bytes, q, wpr, lane, acc);
 #pragma unroll
-      for (int it = 0; it < IT; ++it) {
-        const int c = c0 + it * 64 + lane;
-        const bool in = c < cpr;
-        wq[it] = in ? ldg16(wrow + (size_t)c * 16) : z;
-#pragma unroll
-        for (int t = 0; t < kNmax; ++t)
-          xq[it][t] = (in && t < a.N) ? ldg16(xb + (size_t)t * a.H * 2 + (size_t)c * 16) : z;
-      }
-#pragma unroll
-      for (int it = 0; it < IT; ++it) {
-#pragma unroll
-        for (int t = 0; t < kNmax; ++t) {
-          const uint32_t xv[4] = {xq[it][t].x, xq[it][t].y, xq[it][t].z, xq[it][t].w};
-          acc[t] += chunk_dot<FMT_BF16>(wq[it], 0u, xv);
-        }
-      }
+      for (int t = 0; t < kNmax; ++t) acc[t] *= m.tensor_scale;
+    } else {
+      const uint8_t* wrow = e < a.EW
+                                ? reinterpret_cast<const uint8_t*>(a.router_w) + (size_t)e * a.H * 2
+                                : reinterpret_cast<const uint8_t*>(a.shared_gate);
+      router_row<FMT_BF16>(a, wrow, nullptr, q, wpr, lane, acc);
     }
 #pragma unroll
     for (int t = 0; t < kNmax; ++t) acc[t] = wave_sum_dpp(acc[t]);

@@ -6,7 +6,7 @@ import torch
 
 import synth
 from oracle import (bf16_to_f64, group_slots, moe_forward, route, route_hash, router_logits,
-                    selection_scores)
+                    router_matrix, selection_scores)
 
 # consecutive gap among the top k+1 selection scores; about 100x the FP32
 # error of a router logit at H = 7168
@@ -19,7 +19,7 @@ W_RTOL = 1e-5
 
 def tie_free_filter(npl, gap=TIE_GAP):
     cfg = npl["cfg"]
-    wr = bf16_to_f64(npl["router"]["weight"])
+    wr = router_matrix(npl["router"])
     bias = npl["router"]["bias"]
     k = cfg["k"]
 
@@ -105,7 +105,7 @@ def check_against_oracle(layer, x, accum=None, rows=None, label="", path="auto",
     out, idx, w, logits, L = run_hip(layer, x, accum=accum, path=path, token_ids=token_ids)
     ids = None if token_ids is None else token_ids.cpu().numpy()
     # routing of every token
-    z = router_logits(bf16_to_f64(xb), bf16_to_f64(npl["router"]["weight"]))
+    z = router_logits(bf16_to_f64(xb), router_matrix(npl["router"]))
     if npl["router"].get("tid2eid") is not None:
         ref_idx, ref_w = route_hash(z, npl["router"]["tid2eid"], ids, cfg["k"], cfg["scoring"],
                                     cfg["renorm"], cfg["rsf"])

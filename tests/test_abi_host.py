@@ -31,7 +31,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version():
-    assert moe.abi_version() == 4
+    assert moe.abi_version() == 5
 
 
 def _fake_weight(fmt, rows, cols, count, base):
@@ -348,3 +348,25 @@ def test_hash_routing_arguments():
     r.token_ids = FAKE + 8192
     assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
     assert "without a hash table" in B.last_error()
+
+
+def test_nvfp4_router_arguments():
+    c, r, ex, sh = _c3()
+    wq = _fake_weight("nvfp4", 256, 7168, 1, FAKE + (16 << 32))
+    r.weight_q = ctypes.addressof(wq)
+    # both a BF16 weight and a quantised one
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
+    assert "exactly one" in B.last_error()
+    r.weight = None
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_OK
+    # rows must be the router width E + Z
+    c.zero_experts = 0
+    wq.rows = 255
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
+    wq.rows = 256
+    # only NVFP4
+    mx = _fake_weight("mxfp4", 256, 7168, 1, FAKE + (16 << 32))
+    r.weight_q = ctypes.addressof(mx)
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_UNSUPPORTED
+    r.weight_q = None
+    assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG

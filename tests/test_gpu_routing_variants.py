@@ -146,3 +146,42 @@ def test_hash_bad_table_row_sets_error(path, n):
     err, idx, layer = _bad_hash_run(path, n, mutate)
     assert err & (1 << 16)
     assert idx[0, 1] == layer["cfg"]["E"] and idx[2, 0] == layer["cfg"]["E"]
+
+
+# ---- NVFP4 router ("forward_k3.rs", "forward_atomic_c4.rs", "forward_ep.rs":
+# the w4a16 router GEMV/GEMM taken when the layer has an NVFP4 gate) ---------
+
+QR_MX = synth.reduced("qwen3_30b_a3b_mxfp4", H=1024, I=256, E=64, k=8, router_fmt="nvfp4",
+                      name="nvfp4_router_mxfp4_experts")
+QR_GATED = synth.reduced("deepseek_v3_nvfp4", H=1024, I=256, E=48, Z=4, k=8, I_s=256,
+                         router_fmt="nvfp4", shared_gate=True, name="nvfp4_router_gated_z4")
+
+
+@pytest.mark.parametrize("n", [1, 3])
+def test_nvfp4_router_decode(n):
+    _case(QR_MX, n, 740 + n)
+
+
+def test_nvfp4_router_gated_decode():
+    _case(QR_GATED, 4, 742)
+
+
+@pytest.mark.parametrize("n", [16, 70])
+def test_nvfp4_router_grouped(n):
+    _case(QR_MX, n, 743 + n, path="grouped")
+
+
+def test_nvfp4_router_gated_grouped():
+    _case(QR_GATED, 33, 745, path="grouped")
+
+
+def test_nvfp4_router_deepseek_v3_full_sampled_rows():
+    # the DeepSeek-V3 shape with its router in NVFP4 too, N = 4, output
+    # checked on 128 sampled rows
+    cfg = synth.reduced("deepseek_v3_nvfp4", router_fmt="nvfp4", name="ds_v3_nvfp4_router")
+    layer = synth.make_layer(cfg, device=DEV)
+    npl = synth.as_numpy(layer)
+    x = synth.make_tokens(layer, 4, 746, accept=tie_free_filter(npl))
+    rows = np.sort(np.random.default_rng(746).choice(7168, size=128, replace=False))
+    print("[variant] ds_v3_nvfp4_router n=4", flush=True)
+    check_against_oracle(layer, x, rows=rows, label="ds_v3 nvfp4 router")
