@@ -564,6 +564,7 @@ moe_status forward_impl(const moe_cfg* cfg, const moe_router* router, const moe_
   a.rsf = cfg->routed_scaling_factor;
   a.e_lo = sh.lo;
   a.e_hi = sh.hi;
+  a.slot_flags = (a.EW > a.E || sh.partial || router->tid2eid) ? 1 : 0;
   a.maxu = (a.N * a.k < sh.hi - sh.lo) ? a.N * a.k : sh.hi - sh.lo;
   a.x = static_cast<const uint16_t*>(x);
   if (sh.partial)

@@ -85,6 +85,10 @@ struct DecodeArgs {
   int N, H, I, E, k, I_s, scoring, renorm, atomic, maxu;
   int EW;          // router width: E experts and the zero experts
   int e_lo, e_hi;  // experts computed: [e_lo, e_hi); weights hold these only
+  // 1 when a slot's expert may not be computed by this call (zero experts,
+  // an expert-parallel share, hash routing): the routing then publishes a
+  // flag per slot, which the slot-order blend reads
+  int slot_flags;
   const int32_t* tid2eid;    // hash routing table [vocab, k], or null
   const int32_t* token_ids;  // [N]
   int vocab;

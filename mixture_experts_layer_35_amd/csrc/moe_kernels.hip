@@ -391,8 +391,10 @@ __device__ __forceinline__ void topk_and_plan(const DecodeArgs& a, TopkScratch* 
       if (a.out_w) a.out_w[sl] = w;
       s->idx[sl] = my_e;
       s->w[sl] = w;
-      const bool real = my_e >= a.e_lo && my_e < a.e_hi;
-      st_coh64(&a.ctl->slot_real[sl], tagged_u(real ? 1u : 0u, tag));
+      if (a.slot_flags) {
+        const bool real = my_e >= a.e_lo && my_e < a.e_hi;
+        st_coh64(&a.ctl->slot_real[sl], tagged_u(real ? 1u : 0u, tag));
+      }
     }
   }
   __syncthreads();
@@ -719,7 +721,7 @@ __device__ __forceinline__ void blend_block(const DecodeArgs& a, int bt, unsigne
   const int r0 = bt * a.blend_rows;
   const int r1 = min(a.H, r0 + a.blend_rows);
   const int rows = r1 - r0;
-  if (!a.atomic) {
+  if (!a.atomic && a.slot_flags) {
     // which slots have words (published with the routing)
     if ((int)threadIdx.x < a.N * a.k) {
       const u64* p = &a.ctl->slot_real[threadIdx.x];
@@ -752,7 +754,7 @@ __device__ __forceinline__ void blend_block(const DecodeArgs& a, int bt, unsigne
       const int ns = a.k + (a.I_s > 0 ? 1 : 0);
       for (int j = 0; j < ns; ++j) {
         const int slot = j < a.k ? t * a.k + j : a.N * a.k + t;
-        if (j < a.k && !s_real[slot]) continue;
+        if (j < a.k && a.slot_flags && !s_real[slot]) continue;
         const u64* p = a.dbuf + (size_t)slot * a.H + r;
         u64 v = ld_coh64(p);
         unsigned spins = 0;

@@ -36,12 +36,14 @@ CONFIGS = {
                       renorm=True, rsf=1.0, routed_fmt="bf16", shared_fmt="bf16",
                       w_std=0.02, bias_std=None, zipf=None, n_list=(3,),
                       accum="slot"),
-    # Qwen3-30B-A3B-shaped layer, MXFP4 routed experts, no shared expert
+    # Qwen3-30B-A3B-shaped layer, MXFP4 routed experts, no shared expert;
+    # FP32 atomic accumulation (at N = 1 it finishes sooner than the
+    # slot-order sum, which stays available and tested)
     "qwen3_30b_a3b_mxfp4": dict(cfg_id=1, H=2048, I=768, E=128, k=8, I_s=0,
                                 scoring="softmax", renorm=True, rsf=1.0,
                                 routed_fmt="mxfp4", shared_fmt=None, w_std=0.02,
                                 bias_std=None, zipf=None, n_list=(1, 3),
-                                accum="slot"),
+                                accum="atomic"),
     # DeepSeek-V3-shaped layer, NVFP4 routed experts, BF16 shared expert,
     # sigmoid router with FP32 correction bias, FP32 atomic accumulation
     "deepseek_v3_nvfp4": dict(cfg_id=2, H=7168, I=2048, E=256, k=8, I_s=2048,

@@ -99,9 +99,10 @@ def test_max_topk():
 
 # ---- full sizes -------------------------------------------------------------
 
+@pytest.mark.parametrize("accum", ["atomic", "slot"])
 @pytest.mark.parametrize("n", [1, 3])
-def test_qwen3_30b_a3b_full(n):
-    _case("qwen3_30b_a3b_mxfp4", n, seed=100 + n)
+def test_qwen3_30b_a3b_full(n, accum):
+    _case("qwen3_30b_a3b_mxfp4", n, seed=100 + n, accum=accum)
 
 
 @pytest.mark.parametrize("accum", ["atomic", "slot"])
