@@ -322,8 +322,11 @@ __device__ __forceinline__ void gate_up_pass(const MatView& mg, const MatView& m
   }
 }
 
+// With one token tile (units of at most 16 tokens) the kernel is held to 128
+// registers, four workgroups per compute unit: the grid then fits in one
+// round of workgroups at the batched-decode sizes instead of leaving a tail.
 template <int FR, int FS, int NTMAX>
-__global__ __launch_bounds__(kGThreads) void k_g_gate_up(GroupedArgs a) {
+__global__ __launch_bounds__(kGThreads, NTMAX == 1 ? 4 : 1) void k_g_gate_up(GroupedArgs a) {
   extern __shared__ uint4 g_lds[];
   const int bid = blockIdx.x;
   constexpr int T = 16 * NTMAX;
