@@ -65,6 +65,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="budget of the oracle baseline (0 = skip)")
     p.add_argument("--no-trace", action="store_true", help="time without per-kernel events")
+    p.add_argument("--graph", action="store_true",
+                   help="time the K calls as one captured HIP graph (replayed once) instead "
+                        "of K eager launches")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device copy three times (for scaling "
                         "FETCH_SIZE / WRITE_SIZE counter readings) and exit")
@@ -178,11 +181,29 @@ def main():
         c()
     torch.cuda.synchronize()
 
-    t0 = time.perf_counter()
-    for c in calls:
-        c()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    if args.graph:
+        # the same K calls captured once and replayed once (a warm-up replay
+        # first); the library enqueues only kernel launches
+        side = torch.cuda.Stream()
+        gcalls = [bound[(args.warmup + i) % copies].prepare(
+            xs[i % args.pool], out, idx=idx_all[i], stream=side.cuda_stream)
+            for i in range(args.steps)]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for c in gcalls:
+                c()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        t0 = time.perf_counter()
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     us_per_call = wall / args.steps * 1e6
     traced_us = None
     if traced is not None:
@@ -276,7 +297,8 @@ def main():
                                f"k={k} I_s={cfg['I_s']} {cfg['routed_fmt']} N={n}",
                    "n_tokens": n, "routed_format": cfg["routed_fmt"], "path": path,
                    "accum": accum, "weight_copies": copies, "token_batches": args.pool,
-                   "launch": f"eager stream, {nl} launch(es) per call"},
+                   "launch": (f"one HIP graph of {args.steps} calls" if args.graph else
+                              "eager stream") + f", {nl} launch(es) per call"},
         "expert_weight_gbps_call": round(float(expert_bytes.mean() / (us_per_call * 1e-6) / 1e9), 1),
         "expert_weight_gbps_kernels": None if experts_gbs is None else round(experts_gbs, 1),
         "pct_hbm_peak_kernels": None if experts_gbs is None else round(100 * experts_gbs / HBM_PEAK_GBS, 2),
