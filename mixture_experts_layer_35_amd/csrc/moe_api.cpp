@@ -587,10 +587,11 @@ moe_status forward_impl(const moe_cfg* cfg, const moe_router* router, const moe_
     a.sdown = to_dev(shared->down);
     fs = shared->gate.format;
   }
-  // two rows per lane group when the routed gate+up grid still gives at
-  // least two workgroups per compute unit
+  // two rows per lane group only when the routed gate+up grid still gives
+  // about eight workgroups per compute unit with them (a large layer such as
+  // H = 7168); smaller grids run faster as more, lighter workgroups
   const moe::StageGeom g2 = moe::stage_geom(fr, a.H, a.I, 2, 1);
-  const int rpl = ((long)a.maxu * g2.tiles >= 512) ? 2 : 1;
+  const int rpl = ((long)a.maxu * g2.tiles >= 2048) ? 2 : 1;
   // a routed unit's gate+up reports to one done counter (at most 64
   // workgroups); the shared expert's, which streams from the start, to
   // kSharedLines of them
