@@ -593,9 +593,10 @@ moe_status forward_impl(const moe_cfg* cfg, const moe_router* router, const moe_
   const moe::StageGeom g2 = moe::stage_geom(fr, a.H, a.I, 2, 1);
   const int rpl = ((long)a.maxu * g2.tiles >= 2048) ? 2 : 1;
   // a routed unit's gate+up reports to one done counter (at most 64
-  // workgroups); the shared expert's, which streams from the start, to
+  // workgroups, 32 for the large layers, whose longer workgroups measured
+  // faster); the shared expert's, which streams from the start, to
   // kSharedLines of them
-  a.gr = gate_up_geom(fr, a.H, a.I, rpl, 1, a.maxu, 64);
+  a.gr = gate_up_geom(fr, a.H, a.I, rpl, 1, a.maxu, rpl == 2 ? 32 : 64);
   a.dr = down_geom(fr, a.I, a.H, rpl, a.N, a.maxu, 512);
   if (a.I_s > 0) {
     a.gs = gate_up_geom(fs, a.H, a.I_s, rpl, a.N, 1, 64 * moe::kSharedLines);
