@@ -224,7 +224,7 @@ struct Layout {
   size_t head_bytes = 0;
   size_t total = 0;
   // decode
-  size_t unit_done = 0, blend_ctr = 0, acc = 0;
+  size_t blend_ctr = 0, acc = 0;
   size_t a_routed = 0, a_shared = 0, dbuf = 0;
   // grouped
   size_t g_zpart = 0, g_gamma = 0, g_ticket = 0, g_mask = 0, g_idx = 0, g_wts = 0, g_info = 0, g_ptok = 0, g_pslot = 0,
@@ -242,7 +242,6 @@ Layout layout(const moe_cfg* c, int32_t n, int path, bool gated) {
     off = align_up(off + bytes, 256);
     return o;
   };
-  L.unit_done = take((MOE_MAX_EXPERTS + moe::kSharedLines) * moe::kLineWords * 4);
   L.blend_ctr = take((H + 3) / 4 * moe::kLineWords * 4);
   // the decode accumulator is part of the head in both modes, so that calls
   // of either mode can share a workspace (it is zero at rest)
@@ -308,7 +307,7 @@ struct Share {
 // Gate+up geometry: a workgroup stages x once (tokens * H BF16 into LDS) and
 // then streams `sub` row blocks, enough that the staged bytes stay under a
 // quarter of the weight bytes, while keeping about two workgroups per compute
-// unit. At most max_tiles workgroups report to one unit's done counters.
+// unit, and at most max_tiles workgroups per unit.
 moe::StageGeom gate_up_geom(int fmt, int H, int rows, int rpl, int tokens, int units,
                             int max_tiles) {
   int64_t db, sb;
@@ -592,14 +591,13 @@ moe_status forward_impl(const moe_cfg* cfg, const moe_router* router, const moe_
   // H = 7168); smaller grids run faster as more, lighter workgroups
   const moe::StageGeom g2 = moe::stage_geom(fr, a.H, a.I, 2, 1);
   const int rpl = ((long)a.maxu * g2.tiles >= 2048) ? 2 : 1;
-  // a routed unit's gate+up reports to one done counter (at most 64
-  // workgroups, 32 for the large layers, whose longer workgroups measured
-  // faster); the shared expert's, which streams from the start, to
-  // kSharedLines of them
+  // at most 64 gate+up workgroups per routed unit (32 for the large layers,
+  // whose longer workgroups measured faster), 256 for the shared expert,
+  // which streams from the start
   a.gr = gate_up_geom(fr, a.H, a.I, rpl, 1, a.maxu, rpl == 2 ? 32 : 64);
   a.dr = down_geom(fr, a.I, a.H, rpl, a.N, a.maxu, 512);
   if (a.I_s > 0) {
-    a.gs = gate_up_geom(fs, a.H, a.I_s, rpl, a.N, 1, 64 * moe::kSharedLines);
+    a.gs = gate_up_geom(fs, a.H, a.I_s, rpl, a.N, 1, 256);
     a.ds = down_geom(fs, a.I_s, a.H, rpl, a.N, 1, 64);
   }
   // router: up to four waves per row, so that each wave covers its part of a
@@ -623,7 +621,6 @@ moe_status forward_impl(const moe_cfg* cfg, const moe_router* router, const moe_
   cc.accum_mode = a.atomic ? MOE_ACCUM_ATOMIC_F32 : MOE_ACCUM_SLOT;
   const Layout L = layout(&cc, n_tokens, MOE_PATH_DECODE, false);
   a.ctl = reinterpret_cast<moe::Ctl*>(base);
-  a.unit_done = reinterpret_cast<unsigned*>(base + L.unit_done);
   a.blend_ctr = reinterpret_cast<unsigned*>(base + L.blend_ctr);
   a.acc = a.atomic ? reinterpret_cast<float*>(base + L.acc) : nullptr;
   a.a_routed = reinterpret_cast<unsigned long long*>(base + L.a_routed);

@@ -32,7 +32,6 @@ struct DevProj {
 // their own 128-byte lines so pollers and atomics do not pile onto one line.
 constexpr int kLineWords = 32;    // 128 bytes
 constexpr int kDoneGroups = 64;   // workgroup i reports to done group i % 64
-constexpr int kSharedLines = 4;   // done counters of the shared expert's gate+up (one line each)
 constexpr unsigned kErrHashInput = 1u << 16;  // sticky error bit: invalid hash-routing input
 constexpr int kPlanStride = 16;   // 64-bit plan words per unit (one line)
 struct Ctl {
@@ -102,7 +101,6 @@ struct DecodeArgs {
   unsigned spin_limit;
   // workspace
   Ctl* ctl;
-  unsigned* unit_done;  // [(maxu + kSharedLines) * kLineWords]; from maxu: the shared expert
   unsigned* blend_ctr;  // [ceil(H / blend_rows) * kLineWords]
   unsigned long long* a_routed;  // [N*k, I] tagged FP32 SiLU(gate)*up
   unsigned long long* a_shared;  // [N, I_s] tagged FP32

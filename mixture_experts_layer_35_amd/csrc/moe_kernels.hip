@@ -19,7 +19,7 @@
 //               shared expert is one more unit that takes every token and
 //               needs no plan, so it streams while the router runs.
 //   D   down    one workgroup per (unit, row tile): loads its weights first,
-//               then waits for the unit's activations, d = Wd a. Slot mode
+//               then reads the unit's activations as they land, d = Wd a. Slot mode
 //               stores w*d per (slot, row); atomic mode adds w*d into an FP32
 //               [N,H] accumulator ("forward_atomic_c4.rs"). The last
 //               contributor to a block of output rows sums it (slot mode: in
@@ -32,10 +32,11 @@
 // relaxed agent-scope atomics (coherent per access, sc1). Data words are
 // 64-bit, value in the high half and the call's tag in the low half; a reader
 // accepts a word only with the current tag, so nothing has to be cleared
-// between calls and a producer never waits for its stores to complete. Per
-// unit and per row-block counters only say when to start reading. The tag is
-// the workspace's call counter plus one; the last workgroup to finish bumps
-// the counter and clears the counters.
+// between calls and a producer never waits for its stores to complete. A
+// consumer reads the words it needs until they carry the tag (bounded); the
+// only counters are the blend tickets of the atomic mode and the done count.
+// The tag is the workspace's call counter plus one; the last workgroup to
+// finish bumps the counter and clears the done count.
 //
 // Weights are read with 128-bit loads, `lpr` lanes per row, and dequantised
 // in registers: FP4/FP8 pairs go to BF16 pairs with the gfx950 scaled
@@ -91,28 +92,6 @@ __device__ __forceinline__ void set_error(const DecodeArgs& a, unsigned code) {
   __hip_atomic_fetch_or(&a.ctl->error, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Thread 0 spins until each of `lines` counters (one cache line apart)
-// reaches its count (bounded), then the workgroup proceeds. Producer w of
-// `total` reports to line w % lines.
-__device__ __forceinline__ void wg_wait_lines(const DecodeArgs& a, const unsigned* p, int lines,
-                                              unsigned total, unsigned code) {
-  if (threadIdx.x == 0) {
-    unsigned spins = 0;
-    for (int i = 0; i < lines; ++i) {
-      const unsigned target = (total - (unsigned)i + (unsigned)lines - 1u) / (unsigned)lines;
-      while (ld_coh(p + i * kLineWords) < target) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++spins > a.spin_limit) {
-          set_error(a, code);
-          i = lines;
-          break;
-        }
-      }
-    }
-  }
-  __syncthreads();
-}
-
 // Add 1 to *p once every wave of the workgroup got here; returns the old
 // value to every thread. With `complete`, this thread's memory operations
 // finish first (needed where the reader does not check tags).
@@ -123,15 +102,6 @@ __device__ __forceinline__ unsigned wg_signal(unsigned* p, unsigned* s_tmp, bool
     *s_tmp = __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   return *s_tmp;
-}
-
-// Add 1 to *p once every wave of the workgroup has issued its stores, without
-// waiting for them (or the add) to complete. The count is only a hint to
-// start reading: the readers check the tags of the words they read.
-__device__ __forceinline__ void wg_hint(unsigned* p) {
-  __builtin_amdgcn_s_barrier();
-  if (threadIdx.x == 0)
-    (void)__hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename T>
@@ -698,7 +668,6 @@ __device__ __forceinline__ void gate_up_phase(const DecodeArgs& a, int wg, uint4
       for (int t = 0; t < kNmax; ++t) slots[t] = t;
       gate_up_tile<FS, RPL>(a, a.sgate, a.sup, 0, wg, a.gs, a.I_s, smem, s_rows, all, slots,
                             a.a_shared, tag);
-      wg_hint(&a.unit_done[(a.maxu + (wg & (kSharedLines - 1))) * kLineWords]);
     }
     return;
   }
@@ -710,7 +679,6 @@ __device__ __forceinline__ void gate_up_phase(const DecodeArgs& a, int wg, uint4
   if (!read_plan(a, unit, tag, e, slots, wt, mask, s_words)) return;
   gate_up_tile<FR, RPL>(a, a.gate, a.up, e - a.e_lo, tile, a.gr, a.I, smem, s_rows, mask,
                         slots, a.a_routed, tag);
-  wg_hint(&a.unit_done[unit * kLineWords]);
 }
 
 // ---------------------------------------------------------------------------
@@ -781,8 +749,7 @@ __device__ __forceinline__ void down_tile(const DecodeArgs& a, const DevProj& pd
                                           const StageGeom& g, int cols, uint4* smem,
                                           uint32_t mask, const int (&slots)[kNmax],
                                           const float (&wt)[kNmax], const u64* src, bool shared,
-                                          const unsigned* ready, int ready_lines,
-                                          unsigned ready_total, unsigned tag) {
+                                          unsigned tag) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lpr = g.lpr;
@@ -793,7 +760,9 @@ __device__ __forceinline__ void down_tile(const DecodeArgs& a, const DevProj& pd
   const MatView mv[1] = {view_of(pd, e)};
   const uint32_t* xs = reinterpret_cast<const uint32_t*>(smem);
   // the activations are staged once for g.sub row blocks; the first block's
-  // weights are in flight while the workgroup waits for them
+  // weights are in flight while the workgroup waits for them (it reads the
+  // tagged activation words until they carry this call's tag: no counter
+  // sits between the two phases)
 #pragma nounroll
   for (int sb = 0; sb < g.sub; ++sb) {
     if (tile * g.rows_per_wg + sb * block_rows >= a.H) break;  // uniform
@@ -802,7 +771,6 @@ __device__ __forceinline__ void down_tile(const DecodeArgs& a, const DevProj& pd
     st.zero();
     st.load(mv, row_base, a.H, cpr, lpr, li, 0);
     if (sb == 0) {
-      wg_wait_lines(a, ready, ready_lines, ready_total, 2u);
       stage_tagged(a, smem, src, slots[0] < 0 ? 0 : slots[0], slots[1] < 0 ? 0 : slots[1],
                    slots[2] < 0 ? 0 : slots[2], slots[3] < 0 ? 0 : slots[3], mask, cols, tag);
       __syncthreads();
@@ -877,7 +845,7 @@ __device__ __forceinline__ void down_phase(const DecodeArgs& a, int wg, uint4* s
       }
       row0 = wg * a.ds.rows_per_wg;
       down_tile<FS, RPL>(a, a.sdown, 0, wg, a.ds, a.I_s, smem, mask, slots, wt, a.a_shared, true,
-                         &a.unit_done[a.maxu * kLineWords], kSharedLines, (unsigned)a.nGs, tag);
+                         tag);
     }
   } else {
     const int r = wg - a.nDs;
@@ -887,8 +855,7 @@ __device__ __forceinline__ void down_phase(const DecodeArgs& a, int wg, uint4* s
     int e;
     if (read_plan(a, unit, tag, e, slots, wt, mask, s_words))
       down_tile<FR, RPL>(a, a.down, e - a.e_lo, tile, a.dr, a.I, smem, mask, slots, wt, a.a_routed,
-                         false,
-                         &a.unit_done[unit * kLineWords], 1, (unsigned)a.gr.tiles, tag);
+                         false, tag);
   }
   const int bt = row0 / a.blend_rows;
   const int rows_bt = min(a.blend_rows, a.H - bt * a.blend_rows);
@@ -946,7 +913,6 @@ __global__ __launch_bounds__(kThreads) void k_moe_decode(DecodeArgs a) {
     const unsigned top =
         __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (top + 1 == groups) {
-      for (int u = 0; u < a.maxu + kSharedLines; ++u) st_coh(&a.unit_done[u * kLineWords], 0u);
       st_coh(&a.ctl->done, 0u);
       const unsigned next = tag == 0xffffffffu ? 0u : tag;  // keep the next tag non-zero
       st_coh(&a.ctl->epoch, next);
