@@ -142,10 +142,13 @@ struct Stream {
         for (int t = 0; t < kNmax; ++t) acc[m][r][t] = 0.f;
   }
 
-  __device__ __forceinline__ void load(const MatView (&mv)[NM], int row_base, int nrows, int cpr,
-                                       int lpr, int li, int c0) {
+  // chunk sets I0 .. I1-1 of one pass (the pipelined loops below fetch the
+  // two halves of the next pass while computing the two halves of this one)
+  template <int I0, int I1>
+  __device__ __forceinline__ void load_its(const MatView (&mv)[NM], int row_base, int nrows,
+                                           int cpr, int lpr, int li, int c0) {
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
+    for (int it = I0; it < I1; ++it) {
       const int c = c0 + it * lpr + li;
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
@@ -165,11 +168,17 @@ struct Stream {
     }
   }
 
-  __device__ __forceinline__ void compute(int cpr, int lpr, int li, int c0, const uint32_t* xs,
-                                          int xs_tok_words, uint32_t mask) {
+  __device__ __forceinline__ void load(const MatView (&mv)[NM], int row_base, int nrows, int cpr,
+                                       int lpr, int li, int c0) {
+    load_its<0, IT>(mv, row_base, nrows, cpr, lpr, li, c0);
+  }
+
+  template <int I0, int I1>
+  __device__ __forceinline__ void compute_its(int cpr, int lpr, int li, int c0, const uint32_t* xs,
+                                              int xs_tok_words, uint32_t mask) {
     constexpr int XW = Fmt<F>::VPC / 2;  // 32-bit activation words per chunk
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
+    for (int it = I0; it < I1; ++it) {
       const int c = c0 + it * lpr + li;
       if (c >= cpr) continue;
 #pragma unroll
@@ -193,6 +202,24 @@ struct Stream {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  }
+
+  __device__ __forceinline__ void compute(int cpr, int lpr, int li, int c0, const uint32_t* xs,
+                                          int xs_tok_words, uint32_t mask) {
+    compute_its<0, IT>(cpr, lpr, li, c0, xs, xs_tok_words, mask);
+  }
+
+  // One step of a software-pipelined stream: compute this pass (column
+  // offset c0) half by half, and after each half issue the same half of the
+  // next pass (rows nrow_base, offset nc0) into the registers it freed, so
+  // that the next pass's weights are in flight while this one is computed.
+  __device__ __forceinline__ void step(const MatView (&mv)[NM], bool more, int nrow_base,
+                                       int nrows, int nc0, int cpr, int lpr, int li, int c0,
+                                       const uint32_t* xs, int xs_tok_words, uint32_t mask) {
+    compute_its<0, IT / 2>(cpr, lpr, li, c0, xs, xs_tok_words, mask);
+    if (more) load_its<0, IT / 2>(mv, nrow_base, nrows, cpr, lpr, li, nc0);
+    compute_its<IT / 2, IT>(cpr, lpr, li, c0, xs, xs_tok_words, mask);
+    if (more) load_its<IT / 2, IT>(mv, nrow_base, nrows, cpr, lpr, li, nc0);
   }
 
   // row sums land in the last lane of each lane group
@@ -635,19 +662,33 @@ __device__ __forceinline__ void gate_up_tile(const DecodeArgs& a, const DevProj&
   const int row0 = tile * g.rows_per_wg;
   // row blocks that hold rows (uniform)
   const int nsub = min(g.sub, (nrows - row0 + block_rows - 1) / block_rows);
-  // one row block at a time: nothing stays live across blocks, and the
-  // other workgroups on the compute unit keep the memory pipe busy
+  // passes (lpr * IT chunks of every row) of all row blocks in order, each
+  // pass's weights fetched while the previous pass is computed; a block's
+  // activations leave after its last pass
+  const int step_c = lpr * IT;
+  const int npass = (cpr + step_c - 1) / step_c;
+  const int nsteps = nsub * npass;
+  Stream<F, 2, RPL> st;
+  st.zero();
+  st.load(mv, row0 + lane_row, nrows, cpr, lpr, li, 0);
+  int b = 0, p = 0;
 #pragma nounroll
-  for (int b = 0; b < nsub; ++b) {
-    const int brow0 = row0 + b * block_rows;
-    Stream<F, 2, RPL> st;
-    st.zero();
-    for (int c0 = 0; c0 < cpr; c0 += lpr * IT) {
-      st.load(mv, brow0 + lane_row, nrows, cpr, lpr, li, c0);
-      st.compute(cpr, lpr, li, c0, xs, a.H / 2, mask);
+  for (int s = 0; s < nsteps; ++s) {
+    int nb = b, np = p + 1;
+    if (np == npass) {
+      np = 0;
+      ++nb;
     }
-    gate_up_emit<F, RPL>(st, mv, brow0 + lane_row, lane_row, brow0, block_rows, nrows, lpr, li,
-                         s_rows, mask, slots, dst, tag);
+    st.step(mv, s + 1 < nsteps, row0 + nb * block_rows + lane_row, nrows, np * step_c, cpr, lpr,
+            li, p * step_c, xs, a.H / 2, mask);
+    if (np == 0) {
+      const int brow0 = row0 + b * block_rows;
+      gate_up_emit<F, RPL>(st, mv, brow0 + lane_row, lane_row, brow0, block_rows, nrows, lpr,
+                           li, s_rows, mask, slots, dst, tag);
+      st.zero();
+    }
+    b = nb;
+    p = np;
   }
 }
 
@@ -759,27 +800,38 @@ __device__ __forceinline__ void down_tile(const DecodeArgs& a, const DevProj& pd
   const int cpr = cols / Fmt<F>::VPC;
   const MatView mv[1] = {view_of(pd, e)};
   const uint32_t* xs = reinterpret_cast<const uint32_t*>(smem);
-  // the activations are staged once for g.sub row blocks; the first block's
+  // the activations are staged once for g.sub row blocks; the first pass's
   // weights are in flight while the workgroup waits for them (it reads the
   // tagged activation words until they carry this call's tag: no counter
-  // sits between the two phases)
+  // sits between the two phases). Row blocks that hold rows (uniform, at
+  // least one):
+  const int row0 = tile * g.rows_per_wg;
+  const int nsb = min(g.sub, (a.H - row0 + block_rows - 1) / block_rows);
+  // passes of all row blocks in order, each pass's weights fetched while the
+  // previous pass is computed (as in gate+up)
+  const int step_c = lpr * IT;
+  const int npass = (cpr + step_c - 1) / step_c;
+  const int nsteps = nsb * npass;
+  Stream<F, 1, RPL> st;
+  st.zero();
+  st.load(mv, row0 + lane_row, a.H, cpr, lpr, li, 0);
+  stage_tagged(a, smem, src, slots[0] < 0 ? 0 : slots[0], slots[1] < 0 ? 0 : slots[1],
+               slots[2] < 0 ? 0 : slots[2], slots[3] < 0 ? 0 : slots[3], mask, cols, tag);
+  __syncthreads();
+  int b = 0, p = 0;
 #pragma nounroll
-  for (int sb = 0; sb < g.sub; ++sb) {
-    if (tile * g.rows_per_wg + sb * block_rows >= a.H) break;  // uniform
-    const int row_base = tile * g.rows_per_wg + sb * block_rows + lane_row;
-    Stream<F, 1, RPL> st;
-    st.zero();
-    st.load(mv, row_base, a.H, cpr, lpr, li, 0);
-    if (sb == 0) {
-      stage_tagged(a, smem, src, slots[0] < 0 ? 0 : slots[0], slots[1] < 0 ? 0 : slots[1],
-                   slots[2] < 0 ? 0 : slots[2], slots[3] < 0 ? 0 : slots[3], mask, cols, tag);
-      __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    int nb = b, np = p + 1;
+    if (np == npass) {
+      np = 0;
+      ++nb;
     }
-    st.compute(cpr, lpr, li, 0, xs, cols / 2, mask);
-    for (int c0 = lpr * IT; c0 < cpr; c0 += lpr * IT) {
-      st.load(mv, row_base, a.H, cpr, lpr, li, c0);
-      st.compute(cpr, lpr, li, c0, xs, cols / 2, mask);
-    }
+    st.step(mv, s + 1 < nsteps, row0 + nb * block_rows + lane_row, a.H, np * step_c, cpr, lpr,
+            li, p * step_c, xs, cols / 2, mask);
+    const int row_base = row0 + b * block_rows + lane_row;
+    b = nb;
+    p = np;
+    if (np != 0) continue;  // the block has passes left
     st.reduce(lpr, mask);
     if (li == lpr - 1) {
 #pragma unroll
@@ -795,12 +847,14 @@ __device__ __forceinline__ void down_tile(const DecodeArgs& a, const DevProj& pd
             __hip_atomic_fetch_add(a.acc + (size_t)t * a.H + row, v, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
           } else {
-            const int s = shared ? a.N * a.k + t : sel4(t, slots[0], slots[1], slots[2], slots[3]);
-            st_coh64(a.dbuf + (size_t)s * a.H + row, tagged(v, tag));
+            const int sl =
+                shared ? a.N * a.k + t : sel4(t, slots[0], slots[1], slots[2], slots[3]);
+            st_coh64(a.dbuf + (size_t)sl * a.H + row, tagged(v, tag));
           }
         }
       }
     }
+    st.zero();
   }
 }
 
@@ -883,7 +937,7 @@ __device__ __forceinline__ void down_phase(const DecodeArgs& a, int wg, uint4* s
 // The kernel.
 // ---------------------------------------------------------------------------
 template <int FR, int FS, int RPL>
-__global__ __launch_bounds__(kThreads) void k_moe_decode(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, RPL == 1 ? 4 : 2) void k_moe_decode(DecodeArgs a) {
   extern __shared__ uint4 smem[];
   __shared__ unsigned s_tmp;
   __shared__ u64 s_words[2 * kNmax];
