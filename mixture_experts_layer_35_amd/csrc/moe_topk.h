@@ -66,20 +66,81 @@ __device__ __forceinline__ void load_bias4(const float* bias, int E, int lane, f
   }
 }
 
+// Exact top-k of (score bits hi, expert) keys, one wave, k rounds: each lane
+// sorts its four keys once (a five-exchange network); each round takes the
+// wave maximum of the lanes' head scores, breaks a tie between heads by the
+// lower expert, and pops the winner's head. Lane j < k returns the j-th
+// expert. Used when the packed keys of topk_wave cannot decide.
+__device__ __forceinline__ int topk_exact(const uint32_t hi_in[4], int E, int k, int lane) {
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    hi[i] = e < E ? hi_in[i] : 0u;
+    lo[i] = e < E ? 0xffffffffu - (uint32_t)e : 0u;  // larger lo = lower expert
+  }
+  auto cx = [&](int x, int y) {
+    const bool sw = hi[y] > hi[x] || (hi[y] == hi[x] && lo[y] > lo[x]);
+    const uint32_t h0 = hi[x], l0 = lo[x];
+    hi[x] = sw ? hi[y] : hi[x];
+    lo[x] = sw ? lo[y] : lo[x];
+    hi[y] = sw ? h0 : hi[y];
+    lo[y] = sw ? l0 : lo[y];
+  };
+  cx(0, 1);
+  cx(2, 3);
+  cx(0, 2);
+  cx(1, 3);
+  cx(1, 2);
+  int my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t mh = wave_max_u32(hi[0]);
+    const unsigned long long tied = __ballot(hi[0] == mh);
+    int wl;
+    uint32_t ml;
+    if (__popcll(tied) == 1) {
+      wl = __ffsll((long long)tied) - 1;
+      ml = (uint32_t)__builtin_amdgcn_readlane((int)lo[0], wl);
+    } else {
+      ml = wave_max_u32(hi[0] == mh ? lo[0] : 0u);
+      wl = __ffsll((long long)__ballot(hi[0] == mh && lo[0] == ml)) - 1;
+    }
+    if (lane == wl) {
+      hi[0] = hi[1];
+      lo[0] = lo[1];
+      hi[1] = hi[2];
+      lo[1] = lo[2];
+      hi[2] = hi[3];
+      lo[2] = lo[3];
+      hi[3] = 0u;
+      lo[3] = 0u;
+    }
+    if (lane == j) my_e = (int)(0xffffffffu - ml);
+  }
+  return my_e;
+}
+
 // Top-k routing of one token by one wave ("forward_k3.rs",
 // MoeLayer::forward_k3, step 2; "forward_batched.rs", the routing step and
 // its softmax+bias arm). The router logits sit four per lane: expert lane +
 // 64 i in zv[i] (-inf past the router width E). Selection score: the logit
-// (softmax, no bias), softmax(logit) + correction bias (softmax with a bias),
-// or sigmoid(logit) + correction bias (sigmoid). Keys order by (score, -expert), so equal scores go to the lower
-// expert index. bv holds the correction bias of the same four experts (read
-// by the caller ahead of the logits; 0 without a bias). Each lane sorts its
-// four keys once (a five-exchange network);
-// each of the k rounds then takes the wave maximum of the lanes' head keys
-// and pops the winner's head. Weights: softmax over all E logits or the plain
-// sigmoid of the chosen logits (no bias), optionally divided by their sum,
-// then times the routed scaling factor. Lane j < k returns the j-th choice
-// and its weight.
+// (softmax, no bias), softmax(logit) + correction bias (softmax with a
+// bias), or sigmoid(logit) + correction bias (sigmoid). Keys order by
+// (score, -expert), so equal scores go to the lower expert index. bv holds
+// the correction bias of the same four experts (read by the caller ahead of
+// the logits; 0 without a bias).
+//
+// Selection packs each key into 32 bits: the score's top 24 ordered bits,
+// then 255 - expert. These keys are distinct, so each of k + 1 rounds is one
+// wave maximum, and the winner's lane (expert % 64) pops its head with no
+// tie handling. The packed order equals the true order wherever two keys
+// differ in their top 24 bits; if none of the k + 1 largest packed keys
+// shares its top 24 bits with the next one, the first k are exactly the true
+// top k in order (any other key is below the (k+1)-th in its top bits).
+// Otherwise the exact rounds of topk_exact decide. Weights: softmax over all
+// E logits or the plain sigmoid of the chosen logits (no bias), optionally
+// divided by their sum, then times the routed scaling factor. Lane j < k
+// returns the j-th choice and its weight.
 __device__ __forceinline__ void topk_wave(const float zv[4], const float bv[4], bool has_bias,
                                           int E, int k, int scoring, int renorm, float rsf,
                                           int lane, int& my_e, float& my_w) {
@@ -92,10 +153,7 @@ __device__ __forceinline__ void topk_wave(const float zv[4], const float bv[4], 
       if (lane + 64 * i < E) p += expf(zv[i] - zmax);
     zsum = wave_sum_dpp(p);
   }
-  // key: hi = ordered score bits, lo = ~expert (larger lo = lower expert);
-  // an absent expert has hi = lo = 0, below every real key
-  uint32_t hi[4], lo[4];
-  float zz[4];
+  uint32_t hi[4], key[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
@@ -106,62 +164,42 @@ __device__ __forceinline__ void topk_wave(const float zv[4], const float bv[4], 
     else if (has_bias)
       sc = expf(zv[i] - zmax) / zsum + bv[i];
     hi[i] = in ? ordered_bits(sc) : 0u;
-    lo[i] = in ? 0xffffffffu - (uint32_t)e : 0u;
-    zz[i] = zv[i];
+    key[i] = in ? ((hi[i] & 0xffffff00u) | (255u - (uint32_t)e)) : 0u;
   }
-  // sort the lane's four keys, largest first (branch-free exchanges)
+  // the lane's four keys, largest first
   auto cx = [&](int x, int y) {
-    const bool sw = hi[y] > hi[x] || (hi[y] == hi[x] && lo[y] > lo[x]);
-    const uint32_t h0 = hi[x], l0 = lo[x];
-    const float z0 = zz[x];
-    hi[x] = sw ? hi[y] : hi[x];
-    lo[x] = sw ? lo[y] : lo[x];
-    zz[x] = sw ? zz[y] : zz[x];
-    hi[y] = sw ? h0 : hi[y];
-    lo[y] = sw ? l0 : lo[y];
-    zz[y] = sw ? z0 : zz[y];
+    const uint32_t a = key[x], b = key[y];
+    key[x] = max(a, b);
+    key[y] = min(a, b);
   };
   cx(0, 1);
   cx(2, 3);
   cx(0, 2);
   cx(1, 3);
   cx(1, 2);
-  my_e = 0;
-  float my_z = 0.f;
-  for (int j = 0; j < k; ++j) {
-    // the largest head score; its lane when unique, else the largest key
-    // among the tied heads
-    const uint32_t mh = wave_max_u32(hi[0]);
-    const unsigned long long tied = __ballot(hi[0] == mh);
-    int wl;
-    uint32_t ml;
-    if (__popcll(tied) == 1) {
-      wl = __ffsll((long long)tied) - 1;
-      ml = (uint32_t)__builtin_amdgcn_readlane((int)lo[0], wl);
-    } else {
-      ml = wave_max_u32(hi[0] == mh ? lo[0] : 0u);
-      wl = __ffsll((long long)__ballot(hi[0] == mh && lo[0] == ml)) - 1;
+  uint32_t mine = 0u;
+  for (int j = 0; j <= k; ++j) {
+    const uint32_t m = wave_max_u32(key[0]);
+    const int lw = (int)(255u - (m & 255u)) & 63;  // the winner's lane
+    if (lane == lw) {
+      key[0] = key[1];
+      key[1] = key[2];
+      key[2] = key[3];
+      key[3] = 0u;
     }
-    const float zsel =
-        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, zz[0]), wl));
-    if (lane == wl) {  // pop the winner's head
-      hi[0] = hi[1];
-      lo[0] = lo[1];
-      zz[0] = zz[1];
-      hi[1] = hi[2];
-      lo[1] = lo[2];
-      zz[1] = zz[2];
-      hi[2] = hi[3];
-      lo[2] = lo[3];
-      zz[2] = zz[3];
-      hi[3] = 0u;
-      lo[3] = 0u;
-    }
-    if (lane == j) {
-      my_e = (int)(0xffffffffu - ml);
-      my_z = zsel;
-    }
+    if (lane == j) mine = m;
   }
+  const uint32_t next = (uint32_t)__shfl((int)mine, lane + 1 < 64 ? lane + 1 : lane, 64);
+  const bool amb = lane < k && (mine >> 8) == (next >> 8);
+  if (__ballot(amb) == 0ull)
+    my_e = lane < k ? (int)(255u - (mine & 255u)) : 0;
+  else
+    my_e = topk_exact(hi, E, k, lane);
+  // the chosen expert's logit: expert e sits in lane e % 64, register e / 64
+  const int src = my_e & 63, reg = (my_e >> 6) & 3;
+  const float z0 = __shfl(zv[0], src, 64), z1 = __shfl(zv[1], src, 64);
+  const float z2 = __shfl(zv[2], src, 64), z3 = __shfl(zv[3], src, 64);
+  const float my_z = reg == 0 ? z0 : (reg == 1 ? z1 : (reg == 2 ? z2 : z3));
   float w = 0.f;
   if (lane < k) w = (scoring == 0) ? expf(my_z - zmax) / zsum : 1.0f / (1.0f + expf(-my_z));
   if (renorm) w = w / wave_sum_dpp(w);

@@ -11,7 +11,8 @@ import torch
 
 import synth
 from oracle import moe_forward
-from parity_util import (OUT_RTOL, bits, check_against_oracle, run_hip, tie_free_filter)
+from parity_util import (OUT_RTOL, bits, check_against_oracle, device_error, run_hip,
+                         tie_free_filter)
 
 pytestmark = pytest.mark.gpu
 
@@ -132,6 +133,35 @@ def test_lowest_index_wins_exact_ties():
         out, idx, w, _, _ = run_hip(lay, x)
         assert idx.cpu().numpy().tolist() == ref["idx"].tolist() == [[min(top, other), max(top, other)]]
         np.testing.assert_allclose(w.cpu().numpy(), ref["w"], rtol=1e-5)
+
+
+@pytest.mark.parametrize("path", ["decode", "grouped"])
+def test_near_ties_follow_own_logits(path):
+    """Two router rows a few ULPs apart: their logits agree in all but the
+    last mantissa bits, where a selection on truncated score bits could not
+    decide. The chosen experts must be the top k of the kernel's own FP32
+    logits, ordered by (logit, -expert)."""
+    print(f"[parity] near ties {path}", flush=True)
+    cfg = synth.reduced("tiny_bf16", E=16, k=4, I_s=0, name="near_ties")
+    layer = synth.make_layer(cfg, device=DEV)
+    x = synth.make_tokens(layer, 4, 70)
+    xf = x.float().cpu()
+    ref0 = moe_forward(synth.as_numpy(layer)["cfg"], synth.as_numpy(layer), bits(x))
+    wr = layer["router"]["weight"].clone()
+    h = int(torch.argmin(xf[0].abs()))  # the smallest activation of token 0
+    for j in range(3):
+        top = int(ref0["idx"][0, j])
+        other = (top + 5) % 16
+        wr[other] = wr[top]
+        v = wr[other, h].view(torch.int16)
+        wr[other, h] = (v + (1 if j % 2 else -1)).view(torch.bfloat16)  # one BF16 ULP
+    lay = dict(layer, router={"weight": wr, "bias": None})
+    out, idx, w, logits, L = run_hip(lay, x, path=path)
+    z = logits.cpu().numpy()
+    for t in range(4):
+        order = sorted(range(16), key=lambda e: (-float(z[t, e]), e))[:4]
+        assert idx[t].cpu().numpy().tolist() == order, (t, z[t].tolist())
+    assert device_error(L) == 0
 
 
 def test_slot_mode_is_deterministic():
