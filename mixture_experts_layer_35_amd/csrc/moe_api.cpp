@@ -595,10 +595,12 @@ moe_status forward_impl(const moe_cfg* cfg, const moe_router* router, const moe_
   // whose longer workgroups measured faster), 256 for the shared expert,
   // which streams from the start
   a.gr = gate_up_geom(fr, a.H, a.I, rpl, 1, a.maxu, rpl == 2 ? 32 : 64);
-  a.dr = down_geom(fr, a.I, a.H, rpl, a.N, a.maxu, 512);
+  // the down phase of the two-row kernels streams four rows per lane group
+  const int rpl_down = rpl == 2 ? 4 : rpl;
+  a.dr = down_geom(fr, a.I, a.H, rpl_down, a.N, a.maxu, 512);
   if (a.I_s > 0) {
     a.gs = gate_up_geom(fs, a.H, a.I_s, rpl, a.N, 1, 256);
-    a.ds = down_geom(fs, a.I_s, a.H, rpl, a.N, 1, 64);
+    a.ds = down_geom(fs, a.I_s, a.H, rpl_down, a.N, 1, 64);
   }
   // router: up to four waves per row, so that each wave covers its part of a
   // row in one round of IT loads per lane (+ one row for the shared gate)

@@ -858,6 +858,12 @@ __device__ __forceinline__ void down_tile(const DecodeArgs& a, const DevProj& pd
   }
 }
 
+// Rows per lane group in the down phase: twice the gate+up count for the
+// two-row (large layer) kernels, so that a down workgroup, which streams a
+// short matrix, has as many weight bytes in flight as a gate+up workgroup.
+template <int RPL>
+constexpr int kDownRpl = RPL == 2 ? 4 : RPL;
+
 template <int FR, int FS, int RPL>
 __device__ __forceinline__ void down_phase(const DecodeArgs& a, int wg, uint4* smem, unsigned* s_tmp,
                            u64* s_words, unsigned tag) {
@@ -898,7 +904,7 @@ __device__ __forceinline__ void down_phase(const DecodeArgs& a, int wg, uint4* s
           if (t < a.N) wt[t] = 1.0f / (1.0f + expf(-tag_value(s_words[t])));
       }
       row0 = wg * a.ds.rows_per_wg;
-      down_tile<FS, RPL>(a, a.sdown, 0, wg, a.ds, a.I_s, smem, mask, slots, wt, a.a_shared, true,
+      down_tile<FS, kDownRpl<RPL>>(a, a.sdown, 0, wg, a.ds, a.I_s, smem, mask, slots, wt, a.a_shared, true,
                          tag);
     }
   } else {
@@ -908,7 +914,7 @@ __device__ __forceinline__ void down_phase(const DecodeArgs& a, int wg, uint4* s
     row0 = tile * a.dr.rows_per_wg;
     int e;
     if (read_plan(a, unit, tag, e, slots, wt, mask, s_words))
-      down_tile<FR, RPL>(a, a.down, e - a.e_lo, tile, a.dr, a.I, smem, mask, slots, wt, a.a_routed,
+      down_tile<FR, kDownRpl<RPL>>(a, a.down, e - a.e_lo, tile, a.dr, a.I, smem, mask, slots, wt, a.a_routed,
                          false, tag);
   }
   const int bt = row0 / a.blend_rows;
