@@ -227,6 +227,14 @@ __device__ void group_slots(const GroupedArgs& a, uint4* g_lds) {
   uint32_t* mlds = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(pre) + kPreBytes);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int E = a.EL, W = a.W;  // the experts this call computes
+  // the first 8 * kT slots' experts, requested together with the masks
+  const int nslots = a.N * a.k;
+  int ev0[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int sl = q * kT + tid;
+    ev0[q] = sl < nslots ? ld_dev(a.idx + sl) : -1;
+  }
   // the token masks, from LDS when they fit (one coalesced copy)
   const bool staged = E * W <= kMaskLdsWords;
   if (staged)
@@ -294,7 +302,6 @@ __device__ void group_slots(const GroupedArgs& a, uint4* g_lds) {
   // ranks, in batches of experts whose word prefixes fit in LDS: thread e
   // writes the running popcount before each of its words
   const int eb_max = kPreBytes / (2 * W);
-  const int nslots = a.N * a.k;
   for (int e0 = 0; e0 < E; e0 += eb_max) {
     const int e1 = min(E, e0 + eb_max);
     if (tid >= e0 && tid < e1) {
@@ -311,7 +318,10 @@ __device__ void group_slots(const GroupedArgs& a, uint4* g_lds) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int sl = s0 + q * kT + tid;
-        ev[q] = sl < nslots ? ld_dev(a.idx + sl) : -1;
+        if (s0 == 0)
+          ev[q] = ev0[q];
+        else
+          ev[q] = sl < nslots ? ld_dev(a.idx + sl) : -1;
       }
 #pragma unroll
       for (int q = 0; q < 8; ++q) {

@@ -325,31 +325,31 @@ __device__ __forceinline__ void stage_tagged(const DecodeArgs& a, uint4* lds, co
 // Phase R: router rows, then (last router workgroup) top-k and the plan.
 // ---------------------------------------------------------------------------
 struct TopkScratch {
-  int idx[kNmax * 16];
-  float w[kNmax * 16];
-  int present[256];
-  int unit_of[256];
+  unsigned bits[8];  // the selected experts of [e_lo, e_hi), one bit each
   int uexp[256];
   int jpos[256 * kNmax];
   float uw[256 * kNmax];
-  int nunits;
 };
 
 __device__ __forceinline__ void topk_and_plan(const DecodeArgs& a, TopkScratch* s, unsigned tag) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  s->present[tid] = 0;
+  if (tid < 8) s->bits[tid] = 0u;
   for (int i = tid; i < 256 * kNmax; i += kThreads) {
     s->jpos[i] = -1;
     s->uw[i] = 0.f;
   }
+  __syncthreads();  // (before the logits arrive)
   // routing is on the critical path of every later workgroup: issue first
   // on this compute unit
   __builtin_amdgcn_s_setprio(3);
   // the bias does not depend on the logits: read it before waiting for them
   float bv[4];
   load_bias4(a.tid2eid ? nullptr : a.router_bias, a.EW, lane, bv);
+  // wave t routes token t (N <= kNmax waves); lane j < k holds slot (t, j)
+  int slot_e = -1;
+  float slot_w = 0.f;
   for (int t = wave; t < a.N; t += kThreads / 64) {
     const int id = a.tid2eid ? a.token_ids[t] : 0;  // hash routing: the token's id
     const u64* zrow = a.ctl->zlog + t * 256;
@@ -386,55 +386,41 @@ __device__ __forceinline__ void topk_and_plan(const DecodeArgs& a, TopkScratch* 
       const int sl = t * a.k + lane;
       if (a.out_idx) a.out_idx[sl] = (uint32_t)my_e;
       if (a.out_w) a.out_w[sl] = w;
-      s->idx[sl] = my_e;
-      s->w[sl] = w;
-      if (a.slot_flags) {
-        const bool real = my_e >= a.e_lo && my_e < a.e_hi;
-        st_coh64(&a.ctl->slot_real[sl], tagged_u(real ? 1u : 0u, tag));
-      }
+      const bool real = my_e >= a.e_lo && my_e < a.e_hi;
+      if (a.slot_flags) st_coh64(&a.ctl->slot_real[sl], tagged_u(real ? 1u : 0u, tag));
+      if (real) atomicOr(&s->bits[my_e >> 5], 1u << (my_e & 31));
+      slot_e = my_e;
+      slot_w = w;
     }
   }
   __syncthreads();
-  const int nslots = a.N * a.k;
   // units: the distinct selected experts this call computes (those in
-  // [e_lo, e_hi): all of them, or one expert-parallel share's range)
-  if (tid < nslots) {
-    const int e = s->idx[tid];
-    if (e >= a.e_lo && e < a.e_hi) s->present[e] = 1;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    // units in ascending expert order: exclusive scan of the presence flags
-    int cnt = 0;
-    int loc[4];
+  // [e_lo, e_hi): all of them, or one expert-parallel share's range), in
+  // ascending order; a slot's unit is the number of selected experts below
+  // its own
+  unsigned bw[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      loc[q] = cnt;
-      cnt += s->present[lane * 4 + q];
+  for (int q = 0; q < 8; ++q) bw[q] = s->bits[q];
+  int nu = 0;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) nu += __popc(bw[q]);
+  if (slot_e >= a.e_lo && slot_e < a.e_hi) {
+    const int wq = slot_e >> 5;
+    int u = 0;
+    unsigned word = 0u;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      u += q < wq ? __popc(bw[q]) : 0;
+      word = q == wq ? bw[q] : word;
     }
-    int incl = cnt;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const int o = __shfl_up(incl, m, 64);
-      if (lane >= m) incl += o;
-    }
-    const int base = incl - cnt;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) s->unit_of[lane * 4 + q] = base + loc[q];
-    if (lane == 63) s->nunits = incl;
-  }
-  __syncthreads();
-  if (tid < nslots && s->idx[tid] >= a.e_lo && s->idx[tid] < a.e_hi) {
-    const int e = s->idx[tid];
-    const int u = s->unit_of[e];
-    const int t = tid / a.k;
-    s->uexp[u] = e;
-    s->jpos[u * kNmax + t] = tid - t * a.k;
-    s->uw[u * kNmax + t] = s->w[tid];
+    u += __popc(word & ((1u << (slot_e & 31)) - 1u));
+    const int t = wave, j = lane;
+    s->uexp[u] = slot_e;
+    s->jpos[u * kNmax + t] = j;
+    s->uw[u * kNmax + t] = slot_w;
   }
   __syncthreads();
   // publish two tagged words per (unit, token): the plan info and the weight
-  const int nu = s->nunits;
   for (int i = tid; i < a.maxu * kNmax; i += kThreads) {
     const int u = i / kNmax;
     const int t = i - u * kNmax;
