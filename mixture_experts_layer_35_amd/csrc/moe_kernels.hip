@@ -556,15 +556,21 @@ __device__ __forceinline__ bool read_plan(const DecodeArgs& a, int u, unsigned t
                                           uint32_t& mask, u64* s_words) {
   if (threadIdx.x < 2 * kNmax) {
     const u64* p = a.ctl->plan + u * kPlanStride + threadIdx.x;
-    u64 v = ld_coh64(p);
+    // first a plain load, which a workgroup starting after the plan was
+    // published usually serves from its XCD's L2 (another workgroup of the
+    // unit brought the line in); a word with another call's tag is read
+    // again coherently, from memory. A word carries its tag, so a line
+    // cached before the plan was written is never taken for it.
+    u64 v = *p;
     unsigned spins = 0;
     while ((unsigned)v != tag) {
+      v = ld_coh64(p);
+      if ((unsigned)v == tag) break;
       __builtin_amdgcn_s_sleep(1);
       if (++spins > a.spin_limit) {
         set_error(a, 1u);
         break;
       }
-      v = ld_coh64(p);
     }
     s_words[threadIdx.x] = v;
   }
@@ -687,9 +693,9 @@ __device__ __forceinline__ void gate_up_phase(const DecodeArgs& a, int wg, uint4
   // router and top-k still run
   const uint32_t all = (1u << a.N) - 1u;
   stage_x_async(smem, a.x, a.N, a.H);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
   if (wg < a.nGs) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     if constexpr (FS != FMT_NONE) {
 #pragma unroll
       for (int t = 0; t < kNmax; ++t) slots[t] = t;
@@ -703,7 +709,12 @@ __device__ __forceinline__ void gate_up_phase(const DecodeArgs& a, int wg, uint4
   const int tile = r - unit * a.gr.tiles;
   int e;
   float wt[kNmax];
-  if (!read_plan(a, unit, tag, e, slots, wt, mask, s_words)) return;
+  // the plan is read while x is still landing in LDS (one memory round trip
+  // for both)
+  const bool present = read_plan(a, unit, tag, e, slots, wt, mask, s_words);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (!present) return;
   gate_up_tile<FR, RPL>(a, a.gate, a.up, e - a.e_lo, tile, a.gr, a.I, smem, s_rows, mask,
                         slots, a.a_routed, tag);
 }
