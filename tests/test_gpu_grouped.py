@@ -122,6 +122,16 @@ def test_prefill_bf16_h4096_full_sampled():
     _case("prefill_bf16_h4096", 512, seed=500, rows=rows, tokens=tokens)
 
 
+def test_prefill_bf16_h4096_max_tokens_sampled():
+    # the largest batch the library takes (MOE_MAX_TOKENS = 4096): 128 mask
+    # words per expert and 256 rows per expert on average, checked on 12
+    # sampled tokens x 64 sampled rows; the grouping is checked whole
+    g = np.random.default_rng(11)
+    rows = np.sort(g.choice(4096, size=64, replace=False))
+    tokens = np.sort(g.choice(4096, size=12, replace=False))
+    _case("prefill_bf16_h4096", 4096, seed=501, rows=rows, tokens=tokens)
+
+
 # ---- shared-expert sigmoid gate ---------------------------------------------
 
 @pytest.mark.parametrize("accum", ["slot", "atomic"])
