@@ -184,7 +184,7 @@ moe_status resolve_path(const moe_cfg* c, int32_t n, int* path) {
 
 // Launch plan of the grouped path for n tokens.
 struct GPlan {
-  int nt, W, maxu, ksplit, kcps, r_rb, r_tg, s_tg, gu_s, gu_r, dn_s, dn_r;
+  int nt, W, maxu, max_items, ksplit, kcps, r_rb, r_tg, s_tg, gu_s, gu_r, dn_s, dn_r;
   size_t mcap;  // rows of the permuted buffers
 };
 
@@ -193,12 +193,16 @@ GPlan gplan(const moe_cfg* c, int n, bool gated) {
   // router rows: E experts and Z zero experts in blocks of 128, plus a block
   // of its own for the shared gate's row
   const int EW = c->num_experts + c->zero_experts;
-  const int mmax = n < 128 ? n : 128;  // tokens of one expert per pass
-  g.nt = mmax <= 16 ? 1 : (mmax <= 32 ? 2 : (mmax <= 64 ? 4 : 8));
+  // 16-token tiles per pass of the expert kernels: one up to 64 tokens (a
+  // unit with more rows than that is split into several work items, one
+  // workgroup each, so the kernel keeps the registers of one tile and four
+  // workgroups per compute unit), eight above
+  g.nt = n <= 64 ? 1 : 8;
   const int T = 16 * g.nt;
   g.W = (n + 31) / 32;
   const int64_t slots = (int64_t)n * c->top_k;
   g.maxu = (int)(slots < c->num_experts ? slots : c->num_experts);
+  g.max_items = g.maxu + (int)((slots + T - 1) / T);
   const int chunks = c->hidden / moe::kGKC;
   g.r_rb = (EW + moe::kGRowsPerWG - 1) / moe::kGRowsPerWG + (gated ? 1 : 0);
   g.r_tg = (n + T - 1) / T;
@@ -414,6 +418,10 @@ moe_status forward_grouped(const moe_cfg* cfg, const moe_router* router,
   a.nt = g.nt;
   a.W = g.W;
   a.maxu = g.maxu < a.EL ? g.maxu : a.EL;
+  a.max_items = a.maxu + (g.max_items - g.maxu);
+  if (a.max_items > moe::kMaxItems)
+    return fail(MOE_ERR_UNSUPPORTED, "grouped path: %d work items exceed %d", a.max_items,
+                moe::kMaxItems);
   a.ksplit = g.ksplit;
   a.kcps = g.kcps;
   a.r_rb = g.r_rb;

@@ -346,20 +346,21 @@ __global__ __launch_bounds__(kGThreads, NTMAX == 1 ? 4 : 1) void k_g_gate_up(Gro
     }
     return;
   }
+  // one work item: T rows (a pass) of one unit
   const int b = bid - a.gu_s;
-  const int u = b / a.gu_r, tile = b % a.gu_r;
-  if (u >= a.info->U) return;
+  const int i = b / a.gu_r, tile = b % a.gu_r;
+  if (i >= a.info->nitems) return;
+  const int item = a.info->item[i];
+  const int u = item >> 16, p0 = (item & 0xffff) * T;
   const int e = a.info->uexp[u], cnt = a.info->ucount[u], rb = a.info->ubase[u];
   const int mpad = (cnt + 15) & ~15;
   const MatView mg = gview(a.gate, e), mu = gview(a.up, e);
-  for (int p0 = 0; p0 < mpad; p0 += T) {
-    const XRows x{a.x, a.H, a.perm_tok + rb + p0, min(cnt - p0, T)};
-    const int rows = min(mpad - p0, T);  // padding rows get a = 0
-    uint16_t* dst = a.a_perm + (int64_t)(rb + p0) * a.I;
-    with_tiles<NTMAX>((rows + 15) >> 4, [&](auto nt) {
-      gate_up_pass<FR, decltype(nt)::value>(mg, mu, tile * 64, x, dst, a.I, rows, nch, g_lds);
-    });
-  }
+  const XRows x{a.x, a.H, a.perm_tok + rb + p0, min(cnt - p0, T)};
+  const int rows = min(mpad - p0, T);  // padding rows get a = 0
+  uint16_t* dst = a.a_perm + (int64_t)(rb + p0) * a.I;
+  with_tiles<NTMAX>((rows + 15) >> 4, [&](auto nt) {
+    gate_up_pass<FR, decltype(nt)::value>(mg, mu, tile * 64, x, dst, a.I, rows, nch, g_lds);
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -430,19 +431,20 @@ __global__ __launch_bounds__(kGThreads) void k_g_down(GroupedArgs a) {
     }
     return;
   }
+  // one work item: T rows (a pass) of one unit
   const int b = bid - a.dn_s;
-  const int u = b / a.dn_r, tile = b % a.dn_r;
-  if (u >= a.info->U) return;
+  const int i = b / a.dn_r, tile = b % a.dn_r;
+  if (i >= a.info->nitems) return;
+  const int item = a.info->item[i];
+  const int u = item >> 16, p0 = (item & 0xffff) * T;
   const int e = a.info->uexp[u], cnt = a.info->ucount[u], rb = a.info->ubase[u];
   const MatView md = gview(a.down, e);
-  for (int p0 = 0; p0 < cnt; p0 += T) {
-    const int m = min(cnt - p0, T);
-    const XRows x{a.a_perm + (int64_t)(rb + p0) * a.I, a.I, nullptr, m};
-    with_tiles<NTMAX>((m + 15) >> 4, [&](auto nt) {
-      down_pass<FR, decltype(nt)::value>(a, md, tile * kGRowsPerWG, x, a.I / kGKC, m, false,
-                                         rb + p0, g_lds);
-    });
-  }
+  const int m = min(cnt - p0, T);
+  const XRows x{a.a_perm + (int64_t)(rb + p0) * a.I, a.I, nullptr, m};
+  with_tiles<NTMAX>((m + 15) >> 4, [&](auto nt) {
+    down_pass<FR, decltype(nt)::value>(a, md, tile * kGRowsPerWG, x, a.I / kGKC, m, false,
+                                       rb + p0, g_lds);
+  });
 }
 
 // Bytes of dynamic LDS of the expert kernels: two chunk buffers of 16*NT
@@ -468,10 +470,11 @@ hipError_t launch_experts<FMT_NVFP4>(const GroupedArgs&, int, hipStream_t, hipEv
 template <int FR, int FS, int NT>
 hipError_t launch_experts_t(const GroupedArgs& a, hipStream_t st, hipEvent_t* ev) {
   hipError_t err = launch_one(reinterpret_cast<const void*>(&k_g_gate_up<FR, FS, NT>),
-                              a.gu_s + a.maxu * a.gu_r, kGThreads, gemm_lds(NT), st, a, ev, 2);
+                              a.gu_s + a.max_items * a.gu_r, kGThreads, gemm_lds(NT), st, a, ev,
+                              2);
   if (err != hipSuccess) return err;
   return launch_one(reinterpret_cast<const void*>(&k_g_down<FR, FS, NT>),
-                    a.dn_s + a.maxu * a.dn_r, kGThreads, gemm_lds(NT), st, a, ev, 3);
+                    a.dn_s + a.max_items * a.dn_r, kGThreads, gemm_lds(NT), st, a, ev, 3);
 }
 
 template <int FR, int FS>

@@ -248,29 +248,36 @@ __device__ void group_slots(const GroupedArgs& a, uint4* g_lds) {
     cnt[tid] = c;
   }
   __syncthreads();
-  // padded exclusive scan and the unit list (wave 0, four experts per lane)
+  // padded exclusive scan, the unit list and the work items (wave 0, four
+  // experts per lane): a unit of c rows has ceil(c / T) items, T = 16 * nt
+  // rows per pass of the expert kernels
   if (wave == 0) {
-    int pc[4], fl[4], ps = 0, fs = 0;
+    const int T = 16 * a.nt;
+    int pc[4], fl[4], ni[4], ps = 0, fs = 0, is = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane * 4 + q;
       const int c = e < E ? cnt[e] : 0;
       pc[q] = (c + 15) & ~15;
       fl[q] = c > 0;
+      ni[q] = (c + T - 1) / T;
       ps += pc[q];
       fs += fl[q];
+      is += ni[q];
     }
-    int ip = ps, ifl = fs;
+    int ip = ps, ifl = fs, ii = is;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const int o1 = __shfl_up(ip, d, 64);
       const int o2 = __shfl_up(ifl, d, 64);
+      const int o3 = __shfl_up(ii, d, 64);
       if (lane >= d) {
         ip += o1;
         ifl += o2;
+        ii += o3;
       }
     }
-    int b = ip - ps, u = ifl - fs;
+    int b = ip - ps, u = ifl - fs, it = ii - is;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane * 4 + q;
@@ -280,14 +287,17 @@ __device__ void group_slots(const GroupedArgs& a, uint4* g_lds) {
           a.info->uexp[u] = e;
           a.info->ubase[u] = b;
           a.info->ucount[u] = cnt[e];
+          for (int p = 0; p < ni[q]; ++p) a.info->item[it + p] = (u << 16) | p;
         }
       }
       b += pc[q];
       u += fl[q];
+      it += ni[q];
     }
     if (lane == 63) {
       a.info->U = ifl;
       a.info->M = ip;
+      a.info->nitems = ii;
       base[E] = ip;
     }
   }

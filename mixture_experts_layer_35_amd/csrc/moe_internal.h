@@ -124,6 +124,11 @@ constexpr int kGRowsPerWG = 128;  // weight rows per workgroup (4 waves x 2 tile
 constexpr int kGLaunches = 5;     // router, top-k (+ grouping), gate+up, down, combine
 
 // Result of the grouping step, read by the expert kernels.
+// Upper bound on the grouped path's work items: maxu + ceil(N * k / (16 * nt))
+// with nt = 1 up to 64 tokens and nt = 8 above (at most 256 + 64 and
+// 256 + 512).
+constexpr int kMaxItems = 1024;
+
 struct GroupInfo {
   int U;         // distinct routed experts in the batch ("units")
   int M;         // rows of the permuted buffers in use (per-unit counts padded to 16)
@@ -131,6 +136,11 @@ struct GroupInfo {
   int uexp[256];    // expert of unit u (local index: expert - e_lo), ascending
   int ubase[256];   // first permuted row of unit u (a multiple of 16)
   int ucount[256];  // tokens routed to unit u
+  // work items of the expert kernels: one per (unit, pass of 16 * nt of its
+  // rows), unit in bits 16.., pass index in bits 0..15, units in order
+  int nitems;
+  int pad2[31];
+  int item[kMaxItems];
 };
 
 struct GroupedArgs {
@@ -153,6 +163,7 @@ struct GroupedArgs {
   int nt;      // 16-token MFMA tiles per pass (1, 2, 4 or 8)
   int W;       // token-mask words per expert, ceil(N / 32)
   int maxu;    // min(E, N * k)
+  int max_items;  // bound on the work items: maxu + ceil(N * k / (16 * nt))
   int ksplit;  // router: H split into ksplit ranges of kcps 128-column chunks
   int kcps;
   // grids
