@@ -357,6 +357,7 @@ __device__ void group_slots(const GroupedArgs& a, uint4* g_lds) {
 
 // ---------------------------------------------------------------------------
 // Combine: four output columns per thread.
+constexpr int kMaxTopk = 16;
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kGThreads) void k_g_combine(GroupedArgs a) {
   const int64_t q = (int64_t)blockIdx.x * kGThreads + threadIdx.x;
@@ -369,16 +370,27 @@ __global__ __launch_bounds__(kGThreads) void k_g_combine(GroupedArgs a) {
     y = *reinterpret_cast<const float4*>(a.acc + (int64_t)t * a.H + h);
   } else {
     y = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < a.k; ++j) {
-      const int s = t * a.k + j;
-      const int row = a.inv[s];
-      if (row < 0) continue;  // another share's expert
-      const float w = a.wts[s];
-      const float4 d = *reinterpret_cast<const float4*>(a.d_perm + (int64_t)row * a.H + h);
-      y.x += w * d.x;
-      y.y += w * d.y;
-      y.z += w * d.z;
-      y.w += w * d.w;
+    // the token's slot rows and weights first, then every slot's row of d,
+    // all requested before any is added (k <= 16), added in slot order
+    int row[kMaxTopk];
+    float w[kMaxTopk];
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j) {
+      row[j] = j < a.k ? a.inv[t * a.k + j] : -1;
+      w[j] = j < a.k ? a.wts[t * a.k + j] : 0.f;
+    }
+    float4 d[kMaxTopk];
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j)  // row < 0: another share's expert, or no slot
+      d[j] = row[j] >= 0 ? *reinterpret_cast<const float4*>(a.d_perm + (int64_t)row[j] * a.H + h)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j) {
+      if (row[j] < 0) continue;
+      y.x += w[j] * d[j].x;
+      y.y += w[j] * d[j].y;
+      y.z += w[j] * d[j].z;
+      y.w += w[j] * d[j].w;
     }
     if (a.I_s > 0) {
       const float4 d = *reinterpret_cast<const float4*>(a.d_shared + (int64_t)t * a.H + h);
