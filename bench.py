@@ -31,6 +31,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+H = None                       # libamdhip64 (ctypes), loaded by main()
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
 MALL_BYTES = 256 << 20
@@ -54,7 +55,11 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=50)
-    p.add_argument("--config", default="qwen3_30b_a3b_mxfp4")
+    p.add_argument("--config", default=None,
+                   help="workload (default: qwen3_30b_a3b_mxfp4 at N=1, plus the points "
+                        "N=3 of the same layer and deepseek_v3_nvfp4 at N=4)")
+    p.add_argument("--no-points", action="store_true",
+                   help="default run: time only the N=1 headline workload")
     p.add_argument("--n", type=int, default=None, help="tokens per call")
     p.add_argument("--accum", default=None, choices=[None, "slot", "atomic"])
     p.add_argument("--path", default="auto", choices=["auto", "decode", "grouped"])
@@ -71,6 +76,9 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device copy three times (for scaling "
                         "FETCH_SIZE / WRITE_SIZE counter readings) and exit")
+    p.add_argument("--read-calibration", action="store_true",
+                   help="only run a 256 MiB read-only reduction three times (a second "
+                        "FETCH_SIZE scale) and exit")
     return p.parse_args()
 
 
@@ -86,6 +94,21 @@ def copy_calibration():
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_per_dispatch": nbytes, "dispatches": 3}), flush=True)
+
+
+def read_calibration():
+    """A reduction that reads 256 MiB and writes a few bytes per dispatch: a
+    FETCH_SIZE reading of it gives the counter's scale for a pure read
+    stream."""
+    import torch
+    nbytes = 256 << 20
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    torch.cuda.synchronize()
+    for _ in range(3):
+        s = a.sum()
+    torch.cuda.synchronize()
+    print(json.dumps({"read_bytes_per_dispatch": nbytes, "dispatches": 3,
+                      "sum": float(s.item())}), flush=True)
 
 
 def kernel_sources_sha256() -> str:
@@ -115,17 +138,10 @@ def traffic_for(key: str):
     return (ent["fetch_kib"] * rec["fetch_scale"] + ent["write_kib"] * rec["write_scale"]) * 1024.0
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(expert parallelism would shard experts across GPUs; see the design notes).",
-              file=sys.stderr)
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration()
-        return
-
+def measure(args, config, n, accum=None, layer=None, cpu_seconds=0.0):
+    """Time K calls of one workload (config, n tokens) after W warm-up calls;
+    returns the record of that workload (value, per-kernel times, roofline)
+    and the layer it built."""
     import numpy as np
     import torch
 
@@ -133,11 +149,10 @@ def main():
     from mixture_experts_layer_35_amd import Layer, num_launches
 
     dev = "cuda:0"
-    torch.cuda.set_device(0)
-    cfg = dict(synth.CONFIGS[args.config])
-    n = args.n or cfg["n_list"][0]
-    accum = args.accum or cfg["accum"]
-    layer = synth.make_layer(args.config, device=dev)
+    cfg = dict(synth.CONFIGS[config])
+    accum = accum or cfg["accum"]
+    if layer is None:
+        layer = synth.make_layer(config, device=dev)
     by = synth.layer_bytes(layer)
 
     # rotate weight copies so that the traffic between two uses of a copy is
@@ -153,7 +168,6 @@ def main():
     k = cfg["k"]
     idx_all = torch.zeros((args.steps, n, k), dtype=torch.int32, device=dev)
 
-    H = hip()
     nl = num_launches(bound[0].cfg, n)
     names = KERNELS[nl]
     stream = torch.cuda.current_stream().cuda_stream
@@ -212,8 +226,8 @@ def main():
             c()
         torch.cuda.synchronize()
         traced_us = (time.perf_counter() - t0) / args.steps * 1e6
-    if nl == 1:
-        err = int(bound[0].workspace[128:132].view(torch.int32).item())
+    for b in bound:
+        err = int(b.workspace[128:132].view(torch.int32).item())
         if err:
             raise RuntimeError(f"device error word {err}: a workgroup wait expired")
 
@@ -252,7 +266,7 @@ def main():
         else:
             dom, dom_bytes, dom_us = "k_g_gate_up", bytes_gu, durs[:, 2]
         achieved = float(dom_bytes.sum() / (dom_us.sum() * 1e-6) / 1e9)
-        key = f"{dom}:{args.config}:N={n}:{accum}"
+        key = f"{dom}:{config}:N={n}:{accum}"
         traffic = traffic_for(key)
         roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -276,24 +290,14 @@ def main():
         experts_gbs = None
 
     cpu = None
-    if args.cpu_seconds > 0:
-        cpu = cpu_baseline(layer, xs, n, args.cpu_seconds)
+    if cpu_seconds > 0:
+        cpu = cpu_baseline(layer, xs, n, cpu_seconds)
 
     path = "decode" if nl == 1 else "grouped"
     rec = {
-        "metric": "MoE layer us/call + expert-weight HBM GB/s (% peak) at N=1,3,4 tokens",
         "value": round(us_per_call, 3),
         "unit": "us/call",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(us_per_call / 1e3, 6),
-        "higher_is_better": False,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": f"{args.config} H={cfg['H']} I={cfg['I']} E={cfg['E']} "
+        "config": {"workload": f"{config} H={cfg['H']} I={cfg['I']} E={cfg['E']} "
                                f"k={k} I_s={cfg['I_s']} {cfg['routed_fmt']} N={n}",
                    "n_tokens": n, "routed_format": cfg["routed_fmt"], "path": path,
                    "accum": accum, "weight_copies": copies, "token_batches": args.pool,
@@ -310,22 +314,102 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(rec), flush=True)
+    del bound, layers, calls, traced, warm, xs, out, idx_all
+    torch.cuda.synchronize()
+    return rec, layer
+
+
+# the other points of the headline metric, measured in the default run
+# beside the N = 1 line: (config, tokens)
+DEFAULT_POINTS = (("qwen3_30b_a3b_mxfp4", 3), ("deepseek_v3_nvfp4", 4))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(expert parallelism would shard experts across GPUs; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.read_calibration:
+        read_calibration()
+        return
+
+    import torch
+
+    global H
+    H = hip()
+    torch.cuda.set_device(0)
+    config = args.config or "qwen3_30b_a3b_mxfp4"
+    n = args.n or __import__("synth").CONFIGS[config]["n_list"][0]
+    rec, layer = measure(args, config, n, args.accum, cpu_seconds=args.cpu_seconds)
+    points = []
+    if args.config is None and args.n is None and not args.no_points:
+        # the headline metric's other token counts, each timed the same way
+        # (K calls after W warm-up calls) with its own roofline
+        for pc, pn in DEFAULT_POINTS:
+            print(f"[bench] point {pc} N={pn}", file=sys.stderr, flush=True)
+            prec, _ = measure(args, pc, pn, None, layer=layer if pc == config else None)
+            points.append(prec)
+            torch.cuda.empty_cache()
+    line = {
+        "metric": "MoE layer us/call + expert-weight HBM GB/s (% peak) at N=1,3,4 tokens",
+        "value": rec["value"],
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(rec["value"] / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+    }
+    line.update({k: v for k, v in rec.items() if k not in ("value", "unit")})
+    if points:
+        line["points"] = points
+    print(json.dumps(line), flush=True)
+
+
+def host_cores() -> int:
+    """CPU threads this process may use: the OpenMP thread budget when one is
+    set (the GPU machine sets it to its CPU share), else the affinity mask."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(layer, xs, n, budget_s):
     """The FP64 oracle on the host: as many calls of the same workload as fit
-    in the budget (at least one), reported per call."""
+    in the budget (at least one), reported per call, with NumPy's BLAS given
+    every host thread."""
     import numpy as np
     import torch
     import synth
     from oracle import moe_forward
     from threadpoolctl import threadpool_limits
     npl = synth.as_numpy(layer)
+    cores = host_cores()
     times = []
     start = time.perf_counter()
     i = 0
-    with threadpool_limits(1):
+    with threadpool_limits(cores):
         while True:
             xb = xs[i % len(xs)].cpu().view(torch.int16).numpy().view(np.uint16)
             t = time.perf_counter()
@@ -335,9 +419,11 @@ def cpu_baseline(layer, xs, n, budget_s):
             if time.perf_counter() - start > budget_s:
                 break
     us = float(np.median(times) * 1e6)
-    return {"value": round(us, 1), "unit": "us/call", "cores": 1, "kind": "oracle",
-            "sample": f"{len(times)} full calls of the same workload (N={n}), median, "
-                      f"single-threaded NumPy FP64"}
+    return {"value": round(us, 1), "unit": "us/call", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{len(times)} full calls of the same workload (N={n}), median; "
+                      f"NumPy FP64, BLAS on {cores} threads (the element-wise dequantisation "
+                      f"runs on one)"}
 
 
 if __name__ == "__main__":

@@ -194,8 +194,17 @@ typedef struct {
   int32_t count;
 } moe_trace;
 
-/* Bytes of workspace moe_forward needs for cfg and up to max_tokens tokens.
- * Returns 0 if cfg is invalid (moe_last_error() says why). */
+/* Bytes of workspace moe_forward needs for cfg and up to max_tokens tokens:
+ * the caller-owned scratch whose size every call checks before it enqueues
+ * anything ("forward_atomic_c4.rs", MoeLayer::forward_atomic_c4_decode: the
+ * scratch arena size check that refuses with a need/have message). The
+ * workspace has three regions: a head of counters and the decode FP32
+ * accumulator, the decode path's hand-off region (sized for
+ * MOE_MAX_DECODE_TOKENS tokens whatever max_tokens is) and, for
+ * max_tokens above MOE_MAX_DECODE_TOKENS, the grouped path's per-call
+ * buffers. The regions never overlap, so calls of either path may share one
+ * workspace in any order. Host only. Returns 0 if cfg is invalid or
+ * max_tokens is outside 1..MOE_MAX_TOKENS (moe_last_error() says why). */
 size_t moe_workspace_bytes(const moe_cfg* cfg, int32_t max_tokens);
 
 /* Validates a call exactly as moe_forward does, without enqueueing anything.
@@ -238,9 +247,11 @@ moe_status moe_group_layout(const moe_cfg* cfg, int32_t n_tokens, moe_group_view
  * aligned, at least moe_workspace_bytes(cfg, n_tokens) bytes, zero-filled
  * before the first call that uses it. Its head holds the decode path's
  * per-call counters and FP32 accumulator, which every decode call returns to
- * zero and the grouped path leaves alone, so a workspace sized for
- * max_tokens serves any later call with the same cfg and n_tokens <=
- * max_tokens, on either path. Bytes 128..131 are a sticky device error word
+ * zero and the grouped path leaves alone; the decode path's hand-off words
+ * (each tagged with its call's number) sit in a region of their own that no
+ * grouped call writes. So a workspace sized for max_tokens serves any later
+ * call with the same cfg and n_tokens <= max_tokens, on either path, in any
+ * order. Bytes 128..131 are a sticky device error word
  * (either path may set bits; the caller clears it): bits 0..3 a decode
  * workgroup's bounded wait for another expired, bit 16 an invalid hash-routing
  * input. Results of a call that set it are not valid. stream: hipStream_t
@@ -286,8 +297,24 @@ moe_status moe_forward_ep_partial(const moe_cfg* cfg, const moe_router* router,
                                   size_t workspace_bytes, void* stream,
                                   const moe_trace* trace);
 
+/* The name of a status code ("MOE_OK", "MOE_ERR_WORKSPACE", ...; unknown
+ * codes give "MOE_ERR_UNKNOWN"). A refused call is refused by name rather
+ * than served by a silent fallback, as the pages' forward functions do
+ * ("forward_k3.rs", MoeLayer::forward_k3: the zero-expert guard and the E8M0
+ * guard each bail with a named error). Static storage; never NULL. */
 const char* moe_status_str(moe_status status);
+
+/* The detail of the last refusal on the calling thread (the need/have
+ * figures of a workspace refusal, the argument and the limit of an invalid
+ * one; "forward_atomic_c4.rs", the scratch size check, and "forward_k3.rs",
+ * the E8M0 guard, name what they refuse and why). Thread-local storage valid
+ * until the thread's next call into the library; "" after a call that
+ * succeeded. Never NULL. */
 const char* moe_last_error(void);
+
+/* MOE_ABI_VERSION of the built library, so that a caller can refuse a
+ * library whose structs differ from its header instead of calling it with
+ * mismatched arguments (the same refuse-by-name habit as moe_status_str). */
 int32_t moe_abi_version(void);
 
 #ifdef __cplusplus

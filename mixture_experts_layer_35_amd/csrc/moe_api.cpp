@@ -220,10 +220,19 @@ GPlan gplan(const moe_cfg* c, int n, bool gated) {
   return g;
 }
 
-// Workspace layout. The head (decode-path counters and, in atomic mode, the
-// decode FP32 accumulator) has a fixed size for a given cfg and must be zero
-// at rest; every decode call leaves it zero and the grouped path does not
-// touch it. The per-call buffers after it depend on the path and on N.
+// Workspace layout, three regions in this order:
+//   head     decode-path counters and the decode FP32 accumulator; fixed size
+//            for a given cfg, zero at rest (every decode call leaves it zero;
+//            the grouped path only ever sets bits of the error word in it)
+//   decode   the decode path's tagged hand-off words (activations, slot-mode
+//            down rows), always sized for kNmax tokens in slot mode, so that
+//            its offsets do not depend on N or on the accumulation mode
+//   grouped  the grouped path's per-call buffers (their size depends on N)
+// The decode region holds nothing but tagged words of decode calls: a
+// grouped call never writes there, so no word of it can carry a value a
+// later decode call would take for its own tag (a grouped buffer holds small
+// integers such as expert ids and counts, and tags are small integers too).
+// The grouped path writes every buffer it reads within the same call.
 struct Layout {
   size_t head_bytes = 0;
   size_t total = 0;
@@ -238,7 +247,7 @@ struct Layout {
 Layout layout(const moe_cfg* c, int32_t n, int path, bool gated) {
   Layout L;
   const size_t N = n, k = c->top_k, H = c->hidden, I = c->inter, Is = c->shared_inter,
-               E = c->num_experts;
+               E = c->num_experts, Nd = moe::kNmax;
   const bool atomic = c->accum_mode == MOE_ACCUM_ATOMIC_F32;
   size_t off = sizeof(moe::Ctl);
   auto take = [&](size_t bytes) {
@@ -249,14 +258,14 @@ Layout layout(const moe_cfg* c, int32_t n, int path, bool gated) {
   L.blend_ctr = take((H + 3) / 4 * moe::kLineWords * 4);
   // the decode accumulator is part of the head in both modes, so that calls
   // of either mode can share a workspace (it is zero at rest)
-  L.acc = take((size_t)moe::kNmax * H * 4);
+  L.acc = take(Nd * H * 4);
   L.head_bytes = off;
-  if (path == MOE_PATH_DECODE) {
-    // tagged BF16 pairs: one 8-byte word per two activations
-    L.a_routed = take(N * k * I / 2 * 8);
-    L.a_shared = take(N * (Is ? Is : 2) / 2 * 8);
-    if (!atomic) L.dbuf = take((N * k + N) * H * 8);
-  } else {
+  // decode region: tagged BF16 pairs (one 8-byte word per two activations)
+  // and tagged FP32 slot-mode down rows, sized for the largest decode call
+  L.a_routed = take(Nd * k * I / 2 * 8);
+  L.a_shared = take(Nd * (Is ? Is : 2) / 2 * 8);
+  L.dbuf = take((Nd * k + Nd) * H * 8);
+  if (path == MOE_PATH_GROUPED) {
     const GPlan g = gplan(c, n, gated);
     L.g_mask = take(E * g.W * 4);
     L.g_ticket = take(4);

@@ -354,6 +354,15 @@ def moe_forward(cfg: dict, layer: dict, x_bits, rows=None, expert_range=None,
     ``tid2eid`` table routes by the tokens' ``token_ids`` (R15).
 
     y[t] = sum_j w[t, j] * d_{idx[t, j]}(x_t) + gamma[t] * s(x_t)   (R12)
+
+    Besides y, the result holds ``y_sq``: for every output element, the sum
+    of the squares of the terms it adds up, w[t, j] * Wd[r, i] * a_i over the
+    routed slots and gamma[t] * Wsd[r, i] * as_i for the shared expert. It is
+    not part of the layer; it sizes an error. Were every intermediate
+    activation a_i (and as_i) scaled by its own independent factor
+    (1 + delta_i) with mean 0 and variance v, y[r] would move by a zero-mean
+    amount of variance v * y_sq[r] (a sum of independent terms), which is what
+    storing the activations in a narrower format does.
     """
     x = bf16_to_f64(np.asarray(x_bits))
     n, h = x.shape
@@ -373,6 +382,7 @@ def moe_forward(cfg: dict, layer: dict, x_bits, rows=None, expert_range=None,
     ex = layer["experts"]
     a_slots = np.zeros((n, k, cfg["I"]), dtype=np.float64)
     d_slots = np.zeros((n, k, out_rows.size), dtype=np.float64)
+    sq_slots = np.zeros((n, k, out_rows.size), dtype=np.float64)
     # one expert's weights at a time (dequantised once for all of its slots)
     lo, hi = (0, cfg["E"]) if expert_range is None else expert_range
     for e in np.unique(idx):
@@ -384,9 +394,12 @@ def moe_forward(cfg: dict, layer: dict, x_bits, rows=None, expert_range=None,
         _, _, a, d = swiglu_expert(wg, wu, wd, x[ts])
         a_slots[ts, js] = a
         d_slots[ts, js] = d
+        sq_slots[ts, js] = (a * a) @ (wd * wd).T  # sum_i (Wd[r, i] a_i)^2
     y = np.zeros((n, out_rows.size), dtype=np.float64)
+    y_sq = np.zeros((n, out_rows.size), dtype=np.float64)
     for j in range(k):
         y += w[:, j:j + 1] * d_slots[:, j]
+        y_sq += (w[:, j:j + 1] ** 2) * sq_slots[:, j]
     s_out = None
     gamma = None
     if expert_range is None and layer.get("shared") is not None and cfg.get("I_s", 0) > 0:
@@ -394,11 +407,12 @@ def moe_forward(cfg: dict, layer: dict, x_bits, rows=None, expert_range=None,
         wg = dequant(sh["gate"], 0)
         wu = dequant(sh["up"], 0)
         wd = dequant(sh["down"], 0, rows=out_rows)
-        _, _, _, s_out = swiglu_expert(wg, wu, wd, x)
+        _, _, a_s, s_out = swiglu_expert(wg, wu, wd, x)
         gamma = shared_gate_weight(x, None if layer["router"].get("shared_gate") is None
                                    else bf16_to_f64(layer["router"]["shared_gate"]))
         y = y + gamma[:, None] * s_out
-    return {"y": y, "z": z, "idx": idx, "w": w, "a": a_slots,
+        y_sq = y_sq + (gamma[:, None] ** 2) * ((a_s * a_s) @ (wd * wd).T)
+    return {"y": y, "y_sq": y_sq, "z": z, "idx": idx, "w": w, "a": a_slots,
             "shared": s_out, "gamma": gamma, "rows": out_rows}
 
 

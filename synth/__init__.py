@@ -166,23 +166,41 @@ def _quantize(w: torch.Tensor, fmt: str) -> dict:
     raise ValueError(fmt)
 
 
+def _packed_shapes(fmt: str, count: int, rows: int, cols: int) -> dict:
+    """Shapes and dtypes of a packed projection's arrays (None: absent)."""
+    if fmt == "bf16":
+        return {"data": ((count, rows, cols), torch.bfloat16), "scales": None,
+                "tensor_scale": None}
+    if fmt == "fp8_rowscale":
+        return {"data": ((count, rows, cols), torch.uint8),
+                "scales": ((count, rows), torch.float32), "tensor_scale": None}
+    if fmt == "mxfp4":
+        return {"data": ((count, rows, cols // 2), torch.uint8),
+                "scales": ((count, rows, cols // 32), torch.uint8), "tensor_scale": None}
+    if fmt == "nvfp4":
+        return {"data": ((count, rows, cols // 2), torch.uint8),
+                "scales": ((count, rows, cols // 16), torch.uint8),
+                "tensor_scale": ((count,), torch.float32)}
+    raise ValueError(fmt)
+
+
 def _projection(cfg, device, tag: str, fmt: str, count: int, rows: int, cols: int,
-                std: float, chunk_bytes: int = 1 << 28) -> dict:
-    """Draw N(0, std) float32 weights expert by expert and pack them."""
-    parts = []
-    per = max(1, min(count, chunk_bytes // max(1, rows * cols * 4)))
-    for e0 in range(0, count, per):
-        e1 = min(count, e0 + per)
-        blk = []
-        for e in range(e0, e1):
-            g = _gen(device, cfg["cfg_id"], _TENSOR_IDS[tag], e)
-            blk.append(torch.randn((rows, cols), generator=g, device=device,
-                                   dtype=torch.float32) * std)
-        parts.append(_quantize(torch.stack(blk), fmt))
+                std: float) -> dict:
+    """Draw N(0, std) float32 weights expert by expert and pack each one
+    straight into its slice of preallocated arrays (every scale of every
+    format lies within one expert, so packing per expert gives the same bytes
+    as packing all experts at once)."""
     out = {"format": fmt, "rows": rows, "cols": cols, "count": count}
-    for key in ("data", "scales", "tensor_scale"):
-        vals = [p[key] for p in parts]
-        out[key] = None if vals[0] is None else torch.cat(vals, dim=0).contiguous()
+    for key, spec in _packed_shapes(fmt, count, rows, cols).items():
+        out[key] = None if spec is None else torch.empty(spec[0], dtype=spec[1], device=device)
+    w = torch.empty((rows, cols), dtype=torch.float32, device=device)
+    for e in range(count):
+        g = _gen(device, cfg["cfg_id"], _TENSOR_IDS[tag], e)
+        torch.randn((rows, cols), generator=g, device=device, dtype=torch.float32, out=w)
+        q = _quantize((w * std).unsqueeze(0), fmt)
+        for key in ("data", "scales", "tensor_scale"):
+            if out[key] is not None:
+                out[key][e].copy_(q[key][0])
     return out
 
 
@@ -247,10 +265,9 @@ def make_tokens(layer: dict, n: int, batch_seed: int = 0, accept=None,
     cfg = layer["cfg"]
     H = cfg["H"]
     device = layer["experts"]["gate"]["data"].device
-    rows = []
+    x = torch.empty((n, H), dtype=torch.bfloat16, device=device)
     for t in range(n):
-        rows.append(_draw_token(cfg, device, n, batch_seed, t, 0))
-    x = torch.stack(rows)
+        x[t].copy_(_draw_token(cfg, device, n, batch_seed, t, 0))
     if accept is not None:
         attempt = 0
         while True:

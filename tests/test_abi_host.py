@@ -90,9 +90,16 @@ def test_workspace_too_small_names_need_and_have():
     assert B.validate(c, r, ex, sh, 4, need) == B.MOE_OK
 
 
-def test_workspace_grows_with_tokens():
+def test_workspace_regions():
     c, *_ = _c3()
-    assert B.workspace_bytes(c, 1) < B.workspace_bytes(c, 4)
+    # the decode region is sized for the largest decode call: one size
+    # serves 1..4 tokens
+    assert B.workspace_bytes(c, 1) == B.workspace_bytes(c, 4)
+    # the grouped region comes after it and grows with the tokens
+    assert B.workspace_bytes(c, 4) < B.workspace_bytes(c, 16) < B.workspace_bytes(c, 512)
+    for n in (5, 16, 512):
+        v = B.group_layout(c, n)
+        assert min(v.info, v.perm_tok, v.perm_slot, v.inv) >= B.workspace_bytes(c, 4)
 
 
 def test_scale_byte_count_mismatch_refused():

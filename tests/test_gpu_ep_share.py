@@ -6,8 +6,10 @@ its own against the oracle's share (routing over all experts, only the
 share's experts computed, FP32 output), and the sum of the G shares plus
 the shared expert's term, added once, against the oracle's whole layer.
 Bar: routing bit-exact / within 1e-5 as for moe_forward, the share's
-grouping bit-exact on the grouped path, per-token relative L2 within 1e-2,
-and exact zeros for tokens none of whose experts is in the share.
+grouping bit-exact on the grouped path, every element within the element-wise
+bound of parity_util (FP32 partials: the activations' BF16 hand-off only),
+per-token relative L2 within 1e-2, and exact zeros for tokens none of whose
+experts is in the share.
 """
 
 import numpy as np
@@ -16,8 +18,8 @@ import torch
 
 import synth
 from oracle import bf16_to_f64, moe_forward
-from parity_util import (OUT_RTOL, W_RTOL, bits, check_grouping, device_error,
-                         rel_l2_per_token, tie_free_filter)
+from parity_util import (OUT_RTOL, W_RTOL, assert_elementwise, bits, check_grouping,
+                         device_error, rel_l2_per_token, tie_free_filter)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,14 +65,20 @@ def _run_shares(cfg_or_name, n, seed, ranges, carrier=None, accum=None, path="au
         assert np.isfinite(got).all(), f"{label}: share {g} left rows unwritten"
         local_npl = dict(npl)
         local_npl["experts"] = {k: _slice(v, lo, hi) for k, v in npl["experts"].items()}
-        ref = moe_forward(cfg, local_npl, xb, expert_range=(lo, hi))["y"]
+        loc = moe_forward(cfg, local_npl, xb, expert_range=(lo, hi))
+        ref, ref_sq = loc["y"], loc["y_sq"]
         if with_shared:
             ref = ref + full["gamma"][:, None] * full["shared"]
+            # the shared term's squares are among the whole layer's
+            ref_sq = ref_sq + full["y_sq"]
         touched = ((full["idx"] >= lo) & (full["idx"] < hi)).any(axis=1) | with_shared
         assert (got[~touched] == 0).all(), f"{label}: share {g} wrote to untouched tokens"
         if touched.any():
             err = rel_l2_per_token(got[touched], ref[touched])
             assert err.max() <= OUT_RTOL, f"{label}: share {g} rel L2 {err}"
+            # an FP32 partial: only the activations' BF16 hand-off rounds
+            assert_elementwise(got[touched], ref[touched], ref_sq[touched],
+                               f"{label}: share {g}", rounded_output=False)
         total += got
     covered = sorted(ranges) == ranges and ranges[0][0] == 0 and ranges[-1][1] == cfg["E"] and \
         all(a[1] == b[0] for a, b in zip(ranges, ranges[1:]))
@@ -79,6 +87,8 @@ def _run_shares(cfg_or_name, n, seed, ranges, carrier=None, accum=None, path="au
             total += full["gamma"][:, None] * full["shared"]
         err = rel_l2_per_token(total, full["y"])
         assert err.max() <= OUT_RTOL, f"{label}: sum of shares rel L2 {err}"
+        assert_elementwise(total, full["y"], full["y_sq"], f"{label}: sum of shares",
+                           rounded_output=False)
         print(f"[share] {label}: sum rel L2 {err.max():.2e}", flush=True)
     return L
 
@@ -158,7 +168,10 @@ def test_grouped_share_then_whole_layer_on_one_workspace():
     full = moe_forward(npl["cfg"], npl, bits(x))
     err = rel_l2_per_token(bf16_to_f64(bits(out)), full["y"])
     assert err.max() <= OUT_RTOL
+    assert_elementwise(bf16_to_f64(bits(out)), full["y"], full["y_sq"], "whole layer")
     part = L.forward_share(x, 0, 8, with_shared=True)
     torch.cuda.synchronize()
     err = rel_l2_per_token(part.cpu().numpy(), full["y"])
     assert err.max() <= OUT_RTOL
+    assert_elementwise(part.cpu().numpy(), full["y"], full["y_sq"], "share of all experts",
+                       rounded_output=False)

@@ -12,7 +12,8 @@ import torch
 
 import synth
 from oracle import bf16_to_f64, moe_forward
-from parity_util import OUT_RTOL, bits, device_error, rel_l2_per_token, tie_free_filter
+from parity_util import (OUT_RTOL, assert_elementwise, bits, device_error, rel_l2_per_token,
+                         tie_free_filter)
 
 pytestmark = pytest.mark.gpu
 
@@ -62,3 +63,4 @@ def test_graph_replays_match_eager(name, n, path, accum):
         ref = moe_forward(npl["cfg"], npl, bits(x))
         err = rel_l2_per_token(bf16_to_f64(bits(got)), ref["y"])
         assert err.max() <= OUT_RTOL, f"replay {i}: rel L2 {err}"
+        assert_elementwise(bf16_to_f64(bits(got)), ref["y"], ref["y_sq"], f"replay {i}")

@@ -175,13 +175,12 @@ def test_nvfp4_router_gated_grouped():
     _case(QR_GATED, 33, 745, path="grouped")
 
 
-def test_nvfp4_router_deepseek_v3_full_sampled_rows():
-    # the DeepSeek-V3 shape with its router in NVFP4 too, N = 4, output
-    # checked on 128 sampled rows
+def test_nvfp4_router_deepseek_v3_full():
+    # the DeepSeek-V3 shape with its router in NVFP4 too, N = 4, every
+    # output row checked
     cfg = synth.reduced("deepseek_v3_nvfp4", router_fmt="nvfp4", name="ds_v3_nvfp4_router")
     layer = synth.make_layer(cfg, device=DEV)
     npl = synth.as_numpy(layer)
     x = synth.make_tokens(layer, 4, 746, accept=tie_free_filter(npl))
-    rows = np.sort(np.random.default_rng(746).choice(7168, size=128, replace=False))
     print("[variant] ds_v3_nvfp4_router n=4", flush=True)
-    check_against_oracle(layer, x, rows=rows, label="ds_v3 nvfp4 router")
+    check_against_oracle(layer, x, label="ds_v3 nvfp4 router")

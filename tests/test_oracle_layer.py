@@ -134,6 +134,34 @@ def test_linear_in_down_weights():
     np.testing.assert_allclose(out["y"], 2 * ref["y"], rtol=1e-14, atol=1e-300)
 
 
+def test_squared_terms_single_expert_closed_form():
+    # one expert, k = 1, weight 1: y_sq[r] = sum_i (Wd[r, i] a_i)^2, which is
+    # never below y[r]^2 / I (Cauchy-Schwarz) nor above (sum_i |Wd a|)^2
+    layer, npl = _layer(dict(H=32, I=16, E=1, k=1, I_s=0))
+    x = _bf16_bits(synth.make_tokens(layer, 2, 12))
+    out = moe_forward(npl["cfg"], npl, x)
+    ex = npl["experts"]
+    xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    wd = dequant(ex["down"], 0)
+    for t in range(2):
+        _, _, a, d = swiglu_expert(dequant(ex["gate"], 0), dequant(ex["up"], 0), wd, xf[t])
+        terms = wd * a[None, :]
+        np.testing.assert_allclose(out["y_sq"][t], (terms ** 2).sum(axis=1), rtol=1e-12)
+        assert np.all(out["y_sq"][t] * 16 >= d ** 2 * (1 - 1e-12))
+        assert np.all(out["y_sq"][t] <= np.abs(terms).sum(axis=1) ** 2 * (1 + 1e-12))
+
+
+def test_squared_terms_scale_with_the_weights():
+    # doubling every routed down matrix (exact in BF16) quadruples y_sq
+    layer, npl = _layer(dict(H=64, I=32, E=6, k=2, I_s=0))
+    x = _bf16_bits(synth.make_tokens(layer, 3, 13))
+    ref = moe_forward(npl["cfg"], npl, x)
+    d = layer["experts"]["down"]["data"] * 2
+    npl["experts"]["down"] = dict(npl["experts"]["down"], data=_bf16_bits(d))
+    out = moe_forward(npl["cfg"], npl, x)
+    np.testing.assert_allclose(out["y_sq"], 4 * ref["y_sq"], rtol=1e-14, atol=1e-300)
+
+
 def test_rows_subset_matches_full():
     layer, npl = _layer(dict(H=64, I=32, E=6, k=2, I_s=16, routed_fmt="nvfp4"))
     x = _bf16_bits(synth.make_tokens(layer, 2, 7))
@@ -141,6 +169,7 @@ def test_rows_subset_matches_full():
     rows = np.array([63, 0, 17, 5])
     sub = moe_forward(npl["cfg"], npl, x, rows=rows)
     np.testing.assert_allclose(sub["y"], full["y"][:, rows], rtol=1e-12, atol=1e-18)
+    np.testing.assert_allclose(sub["y_sq"], full["y_sq"][:, rows], rtol=1e-12, atol=1e-300)
 
 
 # ---- brute force --------------------------------------------------------
@@ -179,7 +208,7 @@ def _brute_layer(layer, x):
     wr = layer["router"]["weight"].double().tolist()
     bias = layer["router"]["bias"]
     xs = x.double().tolist()
-    ys = []
+    ys, sqs = [], []
     for xt in xs:
         z = [sum(wr[e][h] * xt[h] for h in range(H)) for e in range(E)]
         if cfg["scoring"] == "softmax":
@@ -198,24 +227,29 @@ def _brute_layer(layer, x):
             w = [v / tot for v in w]
         w = [v * cfg["rsf"] for v in w]
         y = [0.0] * H
+        sq = [0.0] * H
 
-        def ffn(wg, wu, wd):
+        def ffn(wg, wu, wd, scale):
+            # every term scale * wd[r][i] * a[i] of the output, listed
             inter = len(wg)
             g = [sum(wg[i][h] * xt[h] for h in range(H)) for i in range(inter)]
             u = [sum(wu[i][h] * xt[h] for h in range(H)) for i in range(inter)]
             a = [g[i] / (1 + math.exp(-g[i])) * u[i] for i in range(inter)]
-            return [sum(wd[r][i] * a[i] for i in range(inter)) for r in range(H)]
+            return [[scale * wd[r][i] * a[i] for i in range(inter)] for r in range(H)]
 
         ex = layer["experts"]
-        for e, we in zip(sel, w):
-            d = ffn(_tdq(ex["gate"], e), _tdq(ex["up"], e), _tdq(ex["down"], e))
-            y = [y[r] + we * d[r] for r in range(H)]
+        terms = [ffn(_tdq(ex["gate"], e), _tdq(ex["up"], e), _tdq(ex["down"], e), we)
+                 for e, we in zip(sel, w)]
         if layer["shared"] is not None:
             sh = layer["shared"]
-            d = ffn(_tdq(sh["gate"], 0), _tdq(sh["up"], 0), _tdq(sh["down"], 0))
-            y = [y[r] + d[r] for r in range(H)]
+            terms.append(ffn(_tdq(sh["gate"], 0), _tdq(sh["up"], 0), _tdq(sh["down"], 0), 1.0))
+        for tr in terms:
+            for r in range(H):
+                y[r] += sum(tr[r])
+                sq[r] += sum(v * v for v in tr[r])
         ys.append(y)
-    return np.array(ys)
+        sqs.append(sq)
+    return np.array(ys), np.array(sqs)
 
 
 @pytest.mark.parametrize("fmt,shared_fmt,scoring", [
@@ -231,9 +265,11 @@ def test_layer_matches_pure_python_brute_force(fmt, shared_fmt, scoring):
                 rsf=2.5 if scoring == "sigmoid" else 1.0)
     layer, npl = _layer(over)
     x = synth.make_tokens(layer, 2, 8)
-    got = moe_forward(npl["cfg"], npl, _bf16_bits(x))["y"]
-    want = _brute_layer(layer, x)
-    np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-13)
+    got = moe_forward(npl["cfg"], npl, _bf16_bits(x))
+    want, want_sq = _brute_layer(layer, x)
+    np.testing.assert_allclose(got["y"], want, rtol=1e-11, atol=1e-13)
+    # the sum of the squared terms of each output element
+    np.testing.assert_allclose(got["y_sq"], want_sq, rtol=1e-11, atol=1e-300)
 
 
 # ---- shared-expert gate and expert-parallel shares ----------------------
@@ -266,6 +302,20 @@ def test_zero_gate_vector_halves_the_shared_expert():
     ref = moe_forward(npl["cfg"], plain, x)
     assert np.array_equal(gated["gamma"], np.full(3, 0.5))
     np.testing.assert_allclose(gated["y"], ref["y"] - 0.5 * ref["shared"], rtol=1e-12, atol=1e-15)
+
+
+def test_gated_shared_squared_terms():
+    # with zero routed down weights only the shared expert's terms remain;
+    # a zero gate vector weights them by sigmoid(0) = 1/2, so y_sq by 1/4
+    layer, npl = _gated_layer(dict(H=64, I=32, E=6, k=2, I_s=16))
+    x = _bf16_bits(synth.make_tokens(layer, 3, 14))
+    npl["experts"]["down"] = dict(npl["experts"]["down"],
+                                  data=np.zeros_like(npl["experts"]["down"]["data"]))
+    npl["router"]["shared_gate"] = np.zeros_like(npl["router"]["shared_gate"])
+    gated = moe_forward(npl["cfg"], npl, x)
+    plain = moe_forward(npl["cfg"], dict(npl, router=dict(npl["router"], shared_gate=None)), x)
+    assert plain["y_sq"].min() > 0
+    np.testing.assert_allclose(gated["y_sq"], 0.25 * plain["y_sq"], rtol=1e-14, atol=1e-300)
 
 
 def test_gate_brute_force_per_token():
