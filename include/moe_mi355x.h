@@ -297,6 +297,33 @@ moe_status moe_forward_ep_partial(const moe_cfg* cfg, const moe_router* router,
                                   size_t workspace_bytes, void* stream,
                                   const moe_trace* trace);
 
+/* moe_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Its scratch is a static device array
+ * inside the library, 16 MiB per device, held from the library's first use
+ * on a device until the process ends; the call itself allocates nothing and
+ * frees nothing. Arguments, results, ownership and errors are those of
+ * moe_forward, with these differences:
+ *   - a call whose scratch need exceeds 16 MiB is refused with
+ *     MOE_ERR_WORKSPACE before anything is enqueued (every decode-path call
+ *     fits, at most 7 MiB; grouped-path calls fit up to a few dozen tokens,
+ *     depending on the layer);
+ *   - every call on one device shares that device's array, whatever its
+ *     layer: calls that overlap on one device (different streams or threads
+ *     without ordering) race and give wrong results, and must be ordered;
+ *   - the first call on a device looks the array up and, unless its stream
+ *     is being captured into a graph, enqueues a fill kernel that zeroes it
+ *     ahead of the call (the loader has zeroed it already);
+ *   - the sticky device error word lives in the static array, so device-side
+ *     errors (an expired wait, an invalid hash-routing input) are not visible
+ *     to the caller; use moe_forward to observe them.
+ * stream: hipStream_t of the current device (NULL = default stream). */
+moe_status moe_forward_no_alloc(const moe_cfg* cfg, const moe_router* router,
+                                const moe_experts* experts, const moe_experts* shared,
+                                const void* x, int32_t n_tokens, void* out,
+                                const moe_topk_out* topk, void* stream,
+                                const moe_trace* trace);
+
 /* The name of a status code ("MOE_OK", "MOE_ERR_WORKSPACE", ...; unknown
  * codes give "MOE_ERR_UNKNOWN"). A refused call is refused by name rather
  * than served by a silent fallback, as the pages' forward functions do

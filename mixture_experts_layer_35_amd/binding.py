@@ -21,7 +21,7 @@ FORMAT = {"bf16": 0, "fp8_rowscale": 1, "mxfp4": 2, "nvfp4": 3}
 
 EXPORTED = ("moe_abi_version", "moe_last_error", "moe_status_str", "moe_workspace_bytes",
             "moe_validate", "moe_num_launches", "moe_group_layout", "moe_forward",
-            "moe_forward_ep_partial")
+            "moe_forward_ep_partial", "moe_forward_no_alloc")
 
 
 class MoeCfg(ctypes.Structure):
@@ -115,6 +115,11 @@ def lib() -> ctypes.CDLL:
             ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(MoeExperts), ctypes.c_void_p,
             ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(MoeTopkOut), ctypes.c_void_p,
             ctypes.c_size_t, ctypes.c_void_p, ctypes.POINTER(MoeTrace)]
+        L.moe_forward_no_alloc.restype = ctypes.c_int
+        L.moe_forward_no_alloc.argtypes = [
+            ctypes.POINTER(MoeCfg), ctypes.POINTER(MoeRouter), ctypes.POINTER(MoeExperts),
+            ctypes.POINTER(MoeExperts), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+            ctypes.POINTER(MoeTopkOut), ctypes.c_void_p, ctypes.POINTER(MoeTrace)]
         _lib = L
     return _lib
 
@@ -310,6 +315,31 @@ class Layer:
                 raise MoeError(st, last_error())
             return keep
         return call
+
+    def forward_no_alloc(self, x, out=None, idx=None, weights=None, logits=None, stream=None,
+                         token_ids=None):
+        """The layer forward through moe_forward_no_alloc: the library's static
+        device scratch instead of this object's workspace."""
+        import torch
+        if out is None:
+            out = torch.empty_like(x)
+        topk = None
+        if idx is not None or weights is not None or logits is not None:
+            topk = MoeTopkOut(_ptr(idx), _ptr(weights), _ptr(logits))
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+        router = self.router
+        if token_ids is not None:
+            router = MoeRouter.from_buffer_copy(self.router)
+            router.token_ids = _ptr(token_ids)
+        st = lib().moe_forward_no_alloc(ctypes.byref(self.cfg), ctypes.byref(router),
+                                        _ref(self.experts), _ref(self.shared),
+                                        ctypes.c_void_p(x.data_ptr()), ctypes.c_int32(x.shape[0]),
+                                        ctypes.c_void_p(out.data_ptr()), _ref(topk),
+                                        ctypes.c_void_p(stream), None)
+        if st != MOE_OK:
+            raise MoeError(st, last_error())
+        return out
 
     def num_launches(self, n_tokens: int) -> int:
         return num_launches(self.cfg, n_tokens)

@@ -12,6 +12,7 @@
 
 #include <cmath>
 #include <cstddef>
+#include <mutex>
 
 #include "../../include/moe_mi355x.h"
 #include "moe_internal.h"
@@ -244,27 +245,43 @@ struct Layout {
          g_inv = 0, g_aperm = 0, g_ashared = 0, g_dperm = 0, g_dshared = 0, g_acc = 0;
 };
 
-Layout layout(const moe_cfg* c, int32_t n, int path, bool gated) {
+// Largest decode-path widths (the decode path stages kNmax rows of each in
+// 64 KiB of LDS) and top-k: the universal layout sizes its head and decode
+// region for them.
+constexpr size_t kDecodeMaxWidth = 8192;
+constexpr size_t kUniversalTopk = MOE_MAX_TOPK;
+
+// universal: the layout of the allocation-free entry point's static scratch,
+// which every layer on a device shares. Its head and decode region are sized
+// for the largest decode call of any cfg, so that their offsets do not depend
+// on the cfg either: the zero-at-rest head of one layer never lies where
+// another layer's tagged words are, and no layer's grouped buffers lie where
+// any layer's decode words are.
+Layout layout(const moe_cfg* c, int32_t n, int path, bool gated, bool universal = false) {
   Layout L;
   const size_t N = n, k = c->top_k, H = c->hidden, I = c->inter, Is = c->shared_inter,
                E = c->num_experts, Nd = moe::kNmax;
   const bool atomic = c->accum_mode == MOE_ACCUM_ATOMIC_F32;
+  const size_t Hh = universal ? kDecodeMaxWidth : H;  // head and decode region sizes
+  const size_t Ih = universal ? kDecodeMaxWidth : I;
+  const size_t Ish = universal ? kDecodeMaxWidth : Is;
+  const size_t kh = universal ? kUniversalTopk : k;
   size_t off = sizeof(moe::Ctl);
   auto take = [&](size_t bytes) {
     size_t o = off;
     off = align_up(off + bytes, 256);
     return o;
   };
-  L.blend_ctr = take((H + 3) / 4 * moe::kLineWords * 4);
+  L.blend_ctr = take((Hh + 3) / 4 * moe::kLineWords * 4);
   // the decode accumulator is part of the head in both modes, so that calls
   // of either mode can share a workspace (it is zero at rest)
-  L.acc = take(Nd * H * 4);
+  L.acc = take(Nd * Hh * 4);
   L.head_bytes = off;
   // decode region: tagged BF16 pairs (one 8-byte word per two activations)
   // and tagged FP32 slot-mode down rows, sized for the largest decode call
-  L.a_routed = take(Nd * k * I / 2 * 8);
-  L.a_shared = take(Nd * (Is ? Is : 2) / 2 * 8);
-  L.dbuf = take((Nd * k + Nd) * H * 8);
+  L.a_routed = take(Nd * kh * Ih / 2 * 8);
+  L.a_shared = take(Nd * (Ish ? Ish : 2) / 2 * 8);
+  L.dbuf = take((Nd * kh + Nd) * Hh * 8);
   if (path == MOE_PATH_GROUPED) {
     const GPlan g = gplan(c, n, gated);
     L.g_mask = take(E * g.W * 4);
@@ -379,7 +396,7 @@ moe::DevProj to_dev(const moe_weight& w) {
 moe_status forward_grouped(const moe_cfg* cfg, const moe_router* router,
                            const moe_experts* experts, const moe_experts* shared, const void* x,
                            int32_t n, void* out, const moe_topk_out* topk, void* workspace,
-                           hipStream_t hs, hipEvent_t* ev, const Share& sh) {
+                           hipStream_t hs, hipEvent_t* ev, const Share& sh, bool universal) {
   moe::GroupedArgs a{};
   a.N = n;
   a.H = cfg->hidden;
@@ -442,7 +459,7 @@ moe_status forward_grouped(const moe_cfg* cfg, const moe_router* router,
   a.dn_r = g.dn_r;
   if (a.I_s == 0) a.s_tg = a.gu_s = a.dn_s = 0;  // a share without the shared expert
   char* base = static_cast<char*>(workspace);
-  const Layout L = layout(cfg, n, MOE_PATH_GROUPED, gated);
+  const Layout L = layout(cfg, n, MOE_PATH_GROUPED, gated, universal);
   a.zpart = reinterpret_cast<float*>(base + L.g_zpart);
   a.gamma = reinterpret_cast<float*>(base + L.g_gamma);
   a.mask = reinterpret_cast<uint32_t*>(base + L.g_mask);
@@ -471,7 +488,7 @@ moe_status forward_grouped(const moe_cfg* cfg, const moe_router* router,
 
 moe_status validate_impl(const moe_cfg* cfg, const moe_router* router,
                          const moe_experts* experts, const moe_experts* shared, int32_t n_tokens,
-                         size_t workspace_bytes, const Share& sh) {
+                         size_t workspace_bytes, const Share& sh, bool universal = false) {
   g_err[0] = 0;
   moe_status st = check_cfg(cfg);
   if (st) return st;
@@ -529,18 +546,26 @@ moe_status validate_impl(const moe_cfg* cfg, const moe_router* router,
     return fail(MOE_ERR_INVALID_ARG, "shared is given but shared_inter == 0");
   }
   const size_t need =
-      layout(cfg, n_tokens, path, router->shared_gate != nullptr && with_shared).total;
-  if (workspace_bytes < need)
+      layout(cfg, n_tokens, path, router->shared_gate != nullptr && with_shared, universal).total;
+  if (workspace_bytes < need) {
+    if (universal)
+      return fail(MOE_ERR_WORKSPACE,
+                  "the static scratch holds %zu bytes and this call needs %zu (fewer tokens, "
+                  "or moe_forward with a workspace of its own)",
+                  workspace_bytes, need);
     return fail(MOE_ERR_WORKSPACE, "workspace too small: need %zu bytes, have %zu", need,
                 workspace_bytes);
+  }
   return MOE_OK;
 }
 
 moe_status forward_impl(const moe_cfg* cfg, const moe_router* router, const moe_experts* experts,
                         const moe_experts* shared, const void* x, int32_t n_tokens, void* out,
                         const moe_topk_out* topk, void* workspace, size_t workspace_bytes,
-                        void* stream, const moe_trace* trace, const Share& sh) {
-  moe_status st = validate_impl(cfg, router, experts, shared, n_tokens, workspace_bytes, sh);
+                        void* stream, const moe_trace* trace, const Share& sh,
+                        bool universal = false) {
+  moe_status st =
+      validate_impl(cfg, router, experts, shared, n_tokens, workspace_bytes, sh, universal);
   if (st) return st;
   if (!x || !aligned(x, 16)) return fail(MOE_ERR_INVALID_ARG, "x null or not 16-byte aligned");
   if (!out || !aligned(out, 16))
@@ -560,8 +585,9 @@ moe_status forward_impl(const moe_cfg* cfg, const moe_router* router, const moe_
                 2 * launches, trace ? trace->count : 0);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipEvent_t* ev = trace ? reinterpret_cast<hipEvent_t*>(trace->events) : nullptr;
-  if (path == MOE_PATH_GROUPED) return forward_grouped(cfg, router, experts, shared, x, n_tokens,
-                                                       out, topk, workspace, hs, ev, sh);
+  if (path == MOE_PATH_GROUPED)
+    return forward_grouped(cfg, router, experts, shared, x, n_tokens, out, topk, workspace, hs,
+                           ev, sh, universal);
 
   moe::DecodeArgs a{};
   a.N = n_tokens;
@@ -638,7 +664,7 @@ moe_status forward_impl(const moe_cfg* cfg, const moe_router* router, const moe_
   char* base = static_cast<char*>(workspace);
   moe_cfg cc = *cfg;
   cc.accum_mode = a.atomic ? MOE_ACCUM_ATOMIC_F32 : MOE_ACCUM_SLOT;
-  const Layout L = layout(&cc, n_tokens, MOE_PATH_DECODE, false);
+  const Layout L = layout(&cc, n_tokens, MOE_PATH_DECODE, false, universal);
   a.ctl = reinterpret_cast<moe::Ctl*>(base);
   a.blend_ctr = reinterpret_cast<unsigned*>(base + L.blend_ctr);
   a.acc = a.atomic ? reinterpret_cast<float*>(base + L.acc) : nullptr;
@@ -655,6 +681,76 @@ moe_status forward_impl(const moe_cfg* cfg, const moe_router* router, const moe_
                                       ev ? ev[1] : nullptr);
   if (err != hipSuccess)
     return fail(MOE_ERR_HIP, "launch failed: %s", hipGetErrorString(err));
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point (moe_forward_no_alloc): a device
+// global, so the library never allocates it at call time. Each device that
+// runs the library holds one copy, from module load until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory: the
+// device address comes from hipGetSymbolAddress, once per device, and only
+// that address is ever handed to a kernel.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];      // device address of `scratch` per device
+bool g_scratch_cleared[kMaxDevices];   // the first-use clear was enqueued
+
+// Zero n16 16-byte units from p (grid-stride).
+__global__ void k_zero16(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The current device's scratch address (looked up on the device's first
+// call). On that first call, unless the stream is being captured into a
+// graph, a fill kernel on the caller's stream also zeroes the head and the
+// decode region ahead of the call's own kernels: the head must start at zero
+// (its counters, error word and accumulator) and a decode word must not carry
+// a tag by chance. The code object loader zero-fills the array already; the
+// clear makes that explicit. It is not enqueued under capture, where a graph
+// replay would clear the call counter again and let words of an earlier
+// replay pass for the current call's.
+moe_status static_scratch(const moe_cfg* cfg, hipStream_t hs, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  if (!g_scratch_cleared[dev]) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(hs, &cs);
+    if (e != hipSuccess)
+      return fail(MOE_ERR_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
+    if (cs == hipStreamCaptureStatusNone) {
+      // the head and the decode region of the universal layout (both of
+      // fixed size); the grouped buffers need no clearing
+      const size_t bytes = layout(cfg, 1, MOE_PATH_DECODE, false, true).total;
+      const size_t n16 = (bytes + 15) / 16;
+      hipLaunchKernelGGL(k_zero16, dim3(256), dim3(256), 0, hs,
+                         static_cast<uint4*>(g_scratch_ptr[dev]), n16);
+      e = hipGetLastError();
+      if (e != hipSuccess)
+        return fail(MOE_ERR_HIP, "clearing the static scratch: %s", hipGetErrorString(e));
+    }
+    g_scratch_cleared[dev] = true;
+  }
+  *out = g_scratch_ptr[dev];
   return MOE_OK;
 }
 
@@ -733,6 +829,25 @@ moe_status moe_forward(const moe_cfg* cfg, const moe_router* router, const moe_e
   sh.hi = cfg ? cfg->num_experts : 0;
   return forward_impl(cfg, router, experts, shared, x, n_tokens, out, topk, workspace,
                       workspace_bytes, stream, trace, sh);
+}
+
+moe_status moe_forward_no_alloc(const moe_cfg* cfg, const moe_router* router,
+                                const moe_experts* experts, const moe_experts* shared,
+                                const void* x, int32_t n_tokens, void* out,
+                                const moe_topk_out* topk, void* stream,
+                                const moe_trace* trace) {
+  Share sh;
+  sh.hi = cfg ? cfg->num_experts : 0;
+  g_err[0] = 0;
+  // refuse what does not fit before touching the device
+  moe_status st = validate_impl(cfg, router, experts, shared, n_tokens, kStaticScratchBytes, sh,
+                                true);
+  if (st) return st;
+  void* ws = nullptr;
+  st = static_scratch(cfg, static_cast<hipStream_t>(stream), &ws);
+  if (st) return st;
+  return forward_impl(cfg, router, experts, shared, x, n_tokens, out, topk, ws,
+                      kStaticScratchBytes, stream, trace, sh, true);
 }
 
 moe_status moe_forward_ep_partial(const moe_cfg* cfg, const moe_router* router,

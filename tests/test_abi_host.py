@@ -380,3 +380,22 @@ def test_nvfp4_router_arguments():
     assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_UNSUPPORTED
     r.weight_q = None
     assert B.validate(c, r, ex, sh, 4, 1 << 40) == B.MOE_ERR_INVALID_ARG
+
+
+def test_no_alloc_refuses_calls_beyond_the_static_scratch():
+    # the allocation-free entry point checks its need against the 16 MiB
+    # static scratch before it looks the scratch up or enqueues anything, so
+    # an oversized call is refused by name here, without a device
+    c, r, ex, sh = _c3()
+    c.path = B.PATH["grouped"]
+    lib = moe.lib()
+    st = lib.moe_forward_no_alloc(ctypes.byref(c), ctypes.byref(r), ctypes.byref(ex),
+                                  ctypes.byref(sh), FAKE, 512, FAKE, None, None, None)
+    assert st == B.MOE_ERR_WORKSPACE
+    msg = B.last_error()
+    m = re.search(r"static scratch holds (\d+) bytes and this call needs (\d+)", msg)
+    assert m and int(m.group(1)) == 16 << 20 and int(m.group(2)) > 16 << 20, msg
+    # invalid arguments are refused the same way as by moe_forward
+    st = lib.moe_forward_no_alloc(ctypes.byref(c), ctypes.byref(r), ctypes.byref(ex),
+                                  ctypes.byref(sh), FAKE, 0, FAKE, None, None, None)
+    assert st == B.MOE_ERR_INVALID_ARG and "n_tokens=0" in B.last_error()

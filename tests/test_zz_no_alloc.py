@@ -1,0 +1,114 @@
+"""The allocation-free entry point (moe_forward_no_alloc) against the
+workspace entry point (moe_forward), through the C ABI.
+
+Both run the same kernels; the no-alloc call keeps its scratch in the
+library's static device array, which every layer on the device shares. Each
+case makes two calls in a row, the second with fewer tokens, and checks each
+against moe_forward on the same input: top-k indices and weights equal, the
+output bit for bit in slot mode (a fixed summation order) and within one BF16
+step in FP32-atomic mode; and each against the FP64 oracle with the parity
+bar (indices bit-exact, every element within the element-wise bound).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import moe_forward
+from parity_util import OUT_RTOL, assert_elementwise, bits, tie_free_filter
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _pair(L, layer, x, accum, label):
+    n, k = x.shape[0], layer["cfg"]["k"]
+    idx_a = torch.full((n, k), -1, dtype=torch.int32, device=DEV)
+    idx_b = torch.full((n, k), -2, dtype=torch.int32, device=DEV)
+    w_a = torch.full((n, k), float("nan"), device=DEV)
+    w_b = torch.full((n, k), float("nan"), device=DEV)
+    ref = L.forward(x, out=torch.full_like(x, float("nan")), idx=idx_a, weights=w_a)
+    got = L.forward_no_alloc(x, out=torch.full_like(x, float("nan")), idx=idx_b, weights=w_b)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_a, idx_b), label
+    assert torch.equal(w_a, w_b), label
+    if accum == "slot":
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), label
+    else:
+        a, b = got.double(), ref.double()
+        step = torch.maximum(a.abs(), b.abs()) * 2.0 ** -7 + 1e-30  # one BF16 step
+        assert ((a - b).abs() <= step).all(), label
+    npl = synth.as_numpy(layer)
+    want = moe_forward(npl["cfg"], npl, bits(x))
+    assert np.array_equal(idx_b.cpu().numpy().astype(np.int64), want["idx"]), label
+    o = got.double().cpu().numpy()
+    err = np.linalg.norm(o - want["y"], axis=1) / np.linalg.norm(want["y"], axis=1)
+    assert err.max() <= OUT_RTOL, (label, err)
+    assert_elementwise(o, want["y"], want["y_sq"], label)
+
+
+@pytest.mark.parametrize("accum", ["slot", "atomic"])
+def test_no_alloc_decode_full_qwen3(accum):
+    from mixture_experts_layer_35_amd import Layer
+    print(f"[no-alloc] qwen3 decode {accum}", flush=True)
+    layer = synth.make_layer("qwen3_30b_a3b_mxfp4", device=DEV)
+    acc = tie_free_filter(synth.as_numpy(layer))
+    L = Layer(layer, 3, accum=accum)
+    for seed, n in ((800, 3), (801, 1)):  # the second call is smaller
+        x = synth.make_tokens(layer, n, seed, accept=acc)
+        _pair(L, layer, x, accum, f"qwen3 n={n} {accum}")
+
+
+@pytest.mark.parametrize("accum", ["slot", "atomic"])
+def test_no_alloc_grouped_tiny(accum):
+    from mixture_experts_layer_35_amd import Layer
+    print(f"[no-alloc] tiny grouped {accum}", flush=True)
+    layer = synth.make_layer("tiny_bf16", device=DEV)
+    acc = tie_free_filter(synth.as_numpy(layer))
+    L = Layer(layer, 17, accum=accum, path="grouped")
+    for seed, n in ((810, 17), (811, 5)):
+        x = synth.make_tokens(layer, n, seed, accept=acc)
+        assert L.num_launches(n) > 1
+        _pair(L, layer, x, accum, f"tiny grouped n={n} {accum}")
+
+
+def test_no_alloc_layers_share_the_scratch():
+    # layers of different shapes in turn on the one static array: none may
+    # see another's state
+    from mixture_experts_layer_35_amd import Layer
+    print("[no-alloc] mixed layers", flush=True)
+    big = synth.make_layer("qwen3_30b_a3b_mxfp4", device=DEV)
+    small_cfg = synth.reduced("deepseek_v3_nvfp4", H=1024, I=256, E=32, k=8, I_s=384,
+                              name="nvfp4_h1024_shared_bf16")
+    small = synth.make_layer(small_cfg, device=DEV)
+    Lb = Layer(big, 4, accum="atomic")
+    Ls = Layer(small, 20, accum="slot")
+    Lg = Layer(small, 20, accum="atomic", path="grouped")
+    acc_b = tie_free_filter(synth.as_numpy(big))
+    acc_s = tie_free_filter(synth.as_numpy(small))
+    for i, (L, lay, acc, n, accum) in enumerate(((Lb, big, acc_b, 4, "atomic"),
+                                                 (Ls, small, acc_s, 3, "slot"),
+                                                 (Lg, small, acc_s, 20, "atomic"),
+                                                 (Lb, big, acc_b, 2, "atomic"),
+                                                 (Ls, small, acc_s, 1, "slot"))):
+        x = synth.make_tokens(lay, n, 820 + i, accept=acc)
+        _pair(L, lay, x, accum, f"mixed call {i} n={n}")
+
+
+def test_no_alloc_refuses_calls_that_do_not_fit():
+    from mixture_experts_layer_35_amd import Layer
+    from mixture_experts_layer_35_amd.binding import MOE_ERR_WORKSPACE, MoeError
+    print("[no-alloc] refusal", flush=True)
+    cfg = synth.reduced("prefill_bf16_h4096", E=16, name="bf16_h4096_e16")
+    layer = synth.make_layer(cfg, device=DEV)
+    L = Layer(layer, 512)
+    x = synth.make_tokens(layer, 512, 830)
+    out = torch.full_like(x, float("nan"))
+    with pytest.raises(MoeError) as e:
+        L.forward_no_alloc(x, out=out)
+    assert e.value.status == MOE_ERR_WORKSPACE
+    assert "static scratch holds 16777216 bytes" in str(e.value)
+    torch.cuda.synchronize()
+    assert torch.isnan(out.float()).all()  # nothing was enqueued
