@@ -645,11 +645,11 @@ moe_status forward_impl(const moe_cfg* cfg, const moe_router* router, const moe_
     a.gs = gate_up_geom(fs, a.H, a.I_s, rpl, a.N, 1, 256);
     a.ds = down_geom(fs, a.I_s, a.H, rpl_down, a.N, 1, 64);
   }
-  // router: up to four waves per row, so that each wave covers its part of a
-  // row in one round of IT loads per lane (+ one row for the shared gate)
-  const int rcpr = a.H / 8;
+  // router: up to four waves per row, enough that each lane holds about one
+  // 16-byte chunk of the row (+ one row for the shared gate)
+  const int rcpr = a.H / (router->weight_q ? 32 : 8);
   a.r_wpr = 1;
-  while (a.r_wpr < 4 && a.r_wpr * 64 * 4 < rcpr) a.r_wpr <<= 1;
+  while (a.r_wpr < 4 && a.r_wpr * 64 < rcpr) a.r_wpr <<= 1;
   const int rrows = a.EW + (a.shared_gate ? 1 : 0);
   const int rows_per_wg = 4 / a.r_wpr;
   a.nR = (rrows + rows_per_wg - 1) / rows_per_wg;

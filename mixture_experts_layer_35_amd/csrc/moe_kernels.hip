@@ -88,6 +88,14 @@ __device__ __forceinline__ float tag_value(u64 w) {
   return __builtin_bit_cast(float, (unsigned)(w >> 32));
 }
 
+// This call's tag: the workspace call counter + 1 (never 0, the value of
+// zero-filled memory); stable until the last workgroup has finished. Each
+// phase reads it together with its own first loads, so that the read costs
+// no round trip of its own.
+__device__ __forceinline__ unsigned call_tag(const DecodeArgs& a) {
+  return ld_coh(&a.ctl->epoch) + 1u;
+}
+
 __device__ __forceinline__ void set_error(const DecodeArgs& a, unsigned code) {
   __hip_atomic_fetch_or(&a.ctl->error, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -421,19 +429,19 @@ __device__ __forceinline__ void topk_and_plan(const DecodeArgs& a, TopkScratch* 
   }
   __syncthreads();
   // publish two tagged words per (unit, token): the plan info and the weight
-  for (int i = tid; i < a.maxu * kNmax; i += kThreads) {
-    const int u = i / kNmax;
-    const int t = i - u * kNmax;
+  for (int ut = tid; ut < a.maxu * kNmax; ut += kThreads) {
+    const int u = ut / kNmax;
+    const int t = ut - u * kNmax;
     unsigned info = 0u;
     float wt = 0.f;
     if (u >= nu) {
       info = kPlanAbsent;
     } else {
       info = (unsigned)s->uexp[u] << 16;
-      const int j = s->jpos[i];
+      const int j = s->jpos[ut];
       if (j >= 0) {
         info |= kPlanPresent | (unsigned)j;
-        wt = s->uw[i];
+        wt = s->uw[ut];
       }
     }
     u64* p = a.ctl->plan + u * kPlanStride + 2 * t;
@@ -442,59 +450,71 @@ __device__ __forceinline__ void topk_and_plan(const DecodeArgs& a, TopkScratch* 
   }
 }
 
-// This wave's part (chunks q*64*ITR + ..., stride wpr*64*ITR) of one router
-// row's dot products with the N tokens, format RF: BF16 (8 values per chunk,
-// ITR = 4 chunks per lane per round) or NVFP4 (32 values per chunk with two
-// E4M3 block scales, ITR = 1, so that the matching 64 bytes of x per token
-// stay few registers). x is read from global memory (L2).
+// This wave's part of one router row's dot products with the N tokens,
+// format RF: BF16 (8 values per 16-byte chunk) or NVFP4 (32 values per chunk
+// with two E4M3 block scales). The row's chunks are dealt to the wpr waves of
+// the row and their 64 lanes in turn (lane l of wave q takes chunks
+// q * 64 + l + j * wpr * 64), RPR chunks per lane per round, all of a round's
+// row and token loads in flight together; x is read from global memory
+// (L2). Only the N real tokens are loaded and multiplied. The call's tag is
+// read into `tag` right after the first round's loads are issued, so that
+// both are in flight together; returns false if this wave had no chunk of the
+// row (and so did not read the tag).
 template <int RF>
-__device__ __forceinline__ void router_row(const DecodeArgs& a, const uint8_t* wrow,
+__device__ __forceinline__ bool router_row(const DecodeArgs& a, const uint8_t* wrow,
                                            const uint8_t* srow, int q, int wpr, int lane,
-                                           float (&acc)[kNmax]) {
+                                           float (&acc)[kNmax], unsigned& tag) {
+  bool have_tag = false;
   constexpr int VPC = Fmt<RF>::VPC;
   constexpr int XU = VPC / 8;  // 16-byte x loads per token and chunk
-  constexpr int ITR = RF == FMT_BF16 ? IT : 1;
+  constexpr int RPR = RF == FMT_BF16 ? 4 : 1;
   const int cpr = a.H / VPC;
+  const int stride = wpr * 64;
   const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.x);
-  for (int c0 = q * 64 * ITR; c0 < cpr; c0 += wpr * 64 * ITR) {
-    // router and token loads go out together
-    uint4 wq[ITR], xq[ITR][kNmax][XU];
-    uint32_t sc[ITR];
+  for (int c0 = q * 64 + lane; c0 - lane < cpr; c0 += stride * RPR) {
+    uint4 wq[RPR], xq[RPR][kNmax][XU];
+    uint32_t sc[RPR];
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-    for (int it = 0; it < ITR; ++it) {
-      const int c = c0 + it * 64 + lane;
+    for (int r = 0; r < RPR; ++r) {
+      const int c = c0 + r * stride;
       const bool in = c < cpr;
-      wq[it] = in ? ldg16(wrow + (size_t)c * 16) : z;
-      sc[it] = (RF != FMT_BF16 && in) ? load_chunk_scale<RF>(srow, c) : 0u;
+      wq[r] = in ? ldg16(wrow + (size_t)c * 16) : z;
+      sc[r] = (RF != FMT_BF16 && in) ? load_chunk_scale<RF>(srow, c) : 0u;
 #pragma unroll
       for (int t = 0; t < kNmax; ++t)
 #pragma unroll
         for (int u = 0; u < XU; ++u)
-          xq[it][t][u] = (in && t < a.N)
-                             ? ldg16(xb + (size_t)t * a.H * 2 + (size_t)c * VPC * 2 + u * 16)
-                             : z;
+          xq[r][t][u] = (in && t < a.N)
+                            ? ldg16(xb + (size_t)t * a.H * 2 + (size_t)c * VPC * 2 + u * 16)
+                            : z;
+    }
+    if (!have_tag) {  // the first round: the call's tag joins its loads
+      tag = call_tag(a);
+      have_tag = true;
     }
 #pragma unroll
-    for (int it = 0; it < ITR; ++it) {
+    for (int r = 0; r < RPR; ++r) {
 #pragma unroll
       for (int t = 0; t < kNmax; ++t) {
+        if (t >= a.N) continue;
         uint32_t xv[VPC / 2];
 #pragma unroll
         for (int u = 0; u < XU; ++u) {
-          xv[4 * u + 0] = xq[it][t][u].x;
-          xv[4 * u + 1] = xq[it][t][u].y;
-          xv[4 * u + 2] = xq[it][t][u].z;
-          xv[4 * u + 3] = xq[it][t][u].w;
+          xv[4 * u + 0] = xq[r][t][u].x;
+          xv[4 * u + 1] = xq[r][t][u].y;
+          xv[4 * u + 2] = xq[r][t][u].z;
+          xv[4 * u + 3] = xq[r][t][u].w;
         }
-        acc[t] += chunk_dot<RF>(wq[it], sc[it], xv);
+        acc[t] += chunk_dot<RF>(wq[r], sc[r], xv);
       }
     }
   }
+  return have_tag;
 }
 
 __device__ __forceinline__ void router_phase(const DecodeArgs& a, int wg, uint4* smem,
-                                             float* s_part, unsigned tag) {
+                                             float* s_part, unsigned& tag) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   // a.r_wpr waves share one router row (K split), so that a long row is one
@@ -506,22 +526,28 @@ __device__ __forceinline__ void router_phase(const DecodeArgs& a, int wg, uint4*
   // gate): w_sg, BF16
   const bool has_row = e < a.EW + (a.shared_gate ? 1 : 0);
   float acc[kNmax] = {0.f, 0.f, 0.f, 0.f};
+  // the call's tag, read after the row's first loads, while they are in
+  // flight (router_row reads it; a wave without a chunk of a row, here)
+  bool have_tag = false;
   if (has_row) {
     if (e < a.EW && a.router_fmt == FMT_NVFP4) {
       const MatView m = view_of(a.router_q, 0);
-      router_row<FMT_NVFP4>(a, m.data + (size_t)e * m.row_bytes,
-                            m.scales + (size_t)e * m.scale_row_bytes, q, wpr, lane, acc);
+      have_tag = router_row<FMT_NVFP4>(a, m.data + (size_t)e * m.row_bytes,
+                                       m.scales + (size_t)e * m.scale_row_bytes, q, wpr, lane,
+                                       acc, tag);
 #pragma unroll
       for (int t = 0; t < kNmax; ++t) acc[t] *= m.tensor_scale;
     } else {
       const uint8_t* wrow = e < a.EW
                                 ? reinterpret_cast<const uint8_t*>(a.router_w) + (size_t)e * a.H * 2
                                 : reinterpret_cast<const uint8_t*>(a.shared_gate);
-      router_row<FMT_BF16>(a, wrow, nullptr, q, wpr, lane, acc);
+      have_tag = router_row<FMT_BF16>(a, wrow, nullptr, q, wpr, lane, acc, tag);
     }
 #pragma unroll
-    for (int t = 0; t < kNmax; ++t) acc[t] = wave_sum_dpp(acc[t]);
+    for (int t = 0; t < kNmax; ++t)
+      if (t < a.N) acc[t] = wave_sum_dpp(acc[t]);
   }
+  if (!have_tag) tag = call_tag(a);
   if (wpr > 1) {
     // the row's partial sums meet in LDS; the row's first wave adds them in
     // a fixed order
@@ -549,19 +575,23 @@ __device__ __forceinline__ void router_phase(const DecodeArgs& a, int wg, uint4*
   topk_and_plan(a, reinterpret_cast<TopkScratch*>(smem), tag);
 }
 
-// Unit u's plan (polling its tagged words). Returns false if the unit is
+// Unit u's plan (polling its tagged words); also reads the call's tag, in
+// flight together with the first plan load. Returns false if the unit is
 // absent. slots[t] = t*k + j for tokens routed to the unit, else -1.
-__device__ __forceinline__ bool read_plan(const DecodeArgs& a, int u, unsigned tag, int& expert,
+__device__ __forceinline__ bool read_plan(const DecodeArgs& a, int u, unsigned& tag, int& expert,
                                           int (&slots)[kNmax], float (&wt)[kNmax],
                                           uint32_t& mask, u64* s_words) {
+  const u64* p = a.ctl->plan + u * kPlanStride + (threadIdx.x & (2 * kNmax - 1));
+  // first a plain load, which a workgroup starting after the plan was
+  // published usually serves from its XCD's L2 (another workgroup of the
+  // unit brought the line in); a word with another call's tag is read again
+  // coherently, from memory. A word carries its tag, so a line cached before
+  // the plan was written is never taken for it.
+  // every lane loads a word (lanes past the plan's words repeat them), so the
+  // loads and the tag's need no branch and share one wait
+  u64 v = *p;
+  tag = call_tag(a);
   if (threadIdx.x < 2 * kNmax) {
-    const u64* p = a.ctl->plan + u * kPlanStride + threadIdx.x;
-    // first a plain load, which a workgroup starting after the plan was
-    // published usually serves from its XCD's L2 (another workgroup of the
-    // unit brought the line in); a word with another call's tag is read
-    // again coherently, from memory. A word carries its tag, so a line
-    // cached before the plan was written is never taken for it.
-    u64 v = *p;
     unsigned spins = 0;
     while ((unsigned)v != tag) {
       v = ld_coh64(p);
@@ -686,7 +716,7 @@ __device__ __forceinline__ void gate_up_tile(const DecodeArgs& a, const DevProj&
 
 template <int FR, int FS, int RPL>
 __device__ __forceinline__ void gate_up_phase(const DecodeArgs& a, int wg, uint4* smem,
-                                              float* s_rows, u64* s_words, unsigned tag) {
+                                              float* s_rows, u64* s_words, unsigned& tag) {
   int slots[kNmax];
   uint32_t mask = 0;
   // x does not depend on the routing: stage every token now, while the
@@ -694,6 +724,7 @@ __device__ __forceinline__ void gate_up_phase(const DecodeArgs& a, int wg, uint4
   const uint32_t all = (1u << a.N) - 1u;
   stage_x_async(smem, a.x, a.N, a.H);
   if (wg < a.nGs) {
+    tag = call_tag(a);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if constexpr (FS != FMT_NONE) {
@@ -756,23 +787,41 @@ __device__ __forceinline__ void blend_block(const DecodeArgs& a, int bt, unsigne
     } else {
       // slots in order, then the shared expert; a slot whose expert no
       // workgroup of this call computes (a zero expert, another share's
-      // expert) has no words and adds nothing
+      // expert) has no words and adds nothing. The words are requested four
+      // slots at a time before any of them is waited for (those without this
+      // call's tag are read again), so the reads cost a round trip per four
+      // slots, not per slot.
+      constexpr int G = 4;
       const int ns = a.k + (a.I_s > 0 ? 1 : 0);
-      for (int j = 0; j < ns; ++j) {
-        const int slot = j < a.k ? t * a.k + j : a.N * a.k + t;
-        if (j < a.k && a.slot_flags && !s_real[slot]) continue;
-        const u64* p = a.dbuf + (size_t)slot * a.H + r;
-        u64 v = ld_coh64(p);
+      for (int j0 = 0; j0 < ns; j0 += G) {
+        u64 v[G];
+        const u64* p[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const int j = j0 + g;
+          const int slot = j < a.k ? t * a.k + j : a.N * a.k + t;
+          const bool need = j < ns && (j >= a.k || !a.slot_flags || s_real[slot]);
+          p[g] = need ? a.dbuf + (size_t)slot * a.H + r : nullptr;
+          v[g] = need ? ld_coh64(p[g]) : (u64)tag;
+        }
         unsigned spins = 0;
-        while ((unsigned)v != tag) {
+        for (;;) {
+          bool all = true;
+#pragma unroll
+          for (int g = 0; g < G; ++g) all = all && (unsigned)v[g] == tag;
+          if (all) break;
           __builtin_amdgcn_s_sleep(1);
           if (++spins > a.spin_limit) {
             set_error(a, 8u);
             break;
           }
-          v = ld_coh64(p);
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            if ((unsigned)v[g] != tag) v[g] = ld_coh64(p[g]);
         }
-        y += tag_value(v);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          if (p[g]) y += tag_value(v[g]);
       }
     }
     if (a.out_f32)
@@ -863,7 +912,7 @@ constexpr int kDownRpl = RPL == 2 ? 4 : RPL;
 
 template <int FR, int FS, int RPL>
 __device__ __forceinline__ void down_phase(const DecodeArgs& a, int wg, uint4* smem, unsigned* s_tmp,
-                           u64* s_words, unsigned tag) {
+                           u64* s_words, unsigned& tag) {
   int slots[kNmax];
   float wt[kNmax];
   uint32_t mask = 0;
@@ -881,9 +930,10 @@ __device__ __forceinline__ void down_phase(const DecodeArgs& a, int wg, uint4* s
       if (a.shared_gate) {
         // the shared output's weight sigmoid(x . w_sg): the gate logits come
         // from the router phase (tagged)
+        const u64* p = a.ctl->glog + (threadIdx.x & (kNmax - 1));
+        u64 v = ld_coh64(p);  // every lane (past N: a repeat), no branch
+        tag = call_tag(a);
         if (threadIdx.x < a.N) {
-          const u64* p = a.ctl->glog + threadIdx.x;
-          u64 v = ld_coh64(p);
           unsigned spins = 0;
           while ((unsigned)v != tag) {
             __builtin_amdgcn_s_sleep(1);
@@ -899,6 +949,8 @@ __device__ __forceinline__ void down_phase(const DecodeArgs& a, int wg, uint4* s
 #pragma unroll
         for (int t = 0; t < kNmax; ++t)
           if (t < a.N) wt[t] = 1.0f / (1.0f + expf(-tag_value(s_words[t])));
+      } else {
+        tag = call_tag(a);
       }
       row0 = wg * a.ds.rows_per_wg;
       down_tile<FS, kDownRpl<RPL>>(a, a.sdown, 0, wg, a.ds, a.I_s, smem, mask, slots, wt, a.a_shared, true,
@@ -946,9 +998,7 @@ __global__ __launch_bounds__(kThreads, RPL == 1 ? 4 : 2) void k_moe_decode(Decod
   __shared__ u64 s_words[2 * kNmax];
   __shared__ float s_rows[kBlockRowsMax * kNmax];
   const int bid = blockIdx.x;
-  // this call's tag: the workspace call counter + 1 (never 0, the value of
-  // zero-filled memory); stable until the last workgroup has finished
-  const unsigned tag = ld_coh(&a.ctl->epoch) + 1u;
+  unsigned tag;  // this call's tag, read by each phase with its first loads
   if (bid < a.nR) {
     router_phase(a, bid, smem, s_rows, tag);
   } else if (bid < a.nR + a.nGs + a.nGr) {

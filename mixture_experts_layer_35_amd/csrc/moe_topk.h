@@ -120,6 +120,24 @@ __device__ __forceinline__ int topk_exact(const uint32_t hi_in[4], int E, int k,
   return my_e;
 }
 
+// e^x from the hardware base-2 exponential: t = x log2(e) rounded to FP32,
+// 2^t, times 1 + (x log2(e) - t) ln 2 for the part the rounding of t lost (an
+// FMA gives it exactly but for the tail of log2(e)), so the error is the
+// hardware exponential's, a few ulp, at any |x|. And the logistic function
+// with the hardware reciprocal. The routing needs no more: the selection
+// margins of its inputs are orders of magnitude wider, and equal inputs still
+// give equal outputs, so exact ties stay ties.
+__device__ __forceinline__ float fast_exp(float x) {
+  const float l2e_hi = 1.44269502162933350f;  // log2(e) to FP32
+  const float l2e_lo = 1.92596299112661746e-08f;  // log2(e) - l2e_hi
+  const float t = x * l2e_hi;
+  const float lost = fmaf(x, l2e_hi, -t) + x * l2e_lo;
+  return __builtin_amdgcn_exp2f(t) * fmaf(lost, 0.693147180559945f, 1.0f);
+}
+__device__ __forceinline__ float fast_sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + fast_exp(-x));
+}
+
 // Top-k routing of one token by one wave ("forward_k3.rs",
 // MoeLayer::forward_k3, step 2; "forward_batched.rs", the routing step and
 // its softmax+bias arm). The router logits sit four per lane: expert lane +
@@ -132,26 +150,32 @@ __device__ __forceinline__ int topk_exact(const uint32_t hi_in[4], int E, int k,
 //
 // Selection packs each key into 32 bits: the score's top 24 ordered bits,
 // then 255 - expert. These keys are distinct, so each of k + 1 rounds is one
-// wave maximum, and the winner's lane (expert % 64) pops its head with no
-// tie handling. The packed order equals the true order wherever two keys
-// differ in their top 24 bits; if none of the k + 1 largest packed keys
-// shares its top 24 bits with the next one, the first k are exactly the true
-// top k in order (any other key is below the (k+1)-th in its top bits).
-// Otherwise the exact rounds of topk_exact decide. Weights: softmax over all
-// E logits or the plain sigmoid of the chosen logits (no bias), optionally
-// divided by their sum, then times the routed scaling factor. Lane j < k
-// returns the j-th choice and its weight.
+// wave maximum, and the winner's lane (expert % 64) pops its head; the pops
+// are selects, with no branch. The packed order equals the true order
+// wherever two keys differ in their top 24 bits; if none of the k + 1
+// largest packed keys shares its top 24 bits with the next one, the first k
+// are exactly the true top k in order (any other key is below the (k+1)-th
+// in its top bits). Otherwise the exact rounds of topk_exact decide.
+//
+// Weights: softmax over all E logits or the plain sigmoid of the chosen
+// logits (no bias), optionally divided by their sum, then times the routed
+// scaling factor. With renormalisation the softmax denominator cancels:
+// w_j = exp(z_j - z_1) / sum over the chosen i of exp(z_i - z_1), z_1 the
+// largest logit (the first choice), so the sum over all E is formed only to
+// score with a bias or to weight without renormalisation. Lane j < k returns
+// the j-th choice and its weight.
 __device__ __forceinline__ void topk_wave(const float zv[4], const float bv[4], bool has_bias,
                                           int E, int k, int scoring, int renorm, float rsf,
                                           int lane, int& my_e, float& my_w) {
-  float zmax = 0.f, zsum = 1.f;
-  if (scoring == 0) {
+  const bool full_softmax = scoring == 0 && (has_bias || !renorm);
+  float zmax = 0.f, rzsum = 1.f;
+  if (full_softmax) {
     zmax = wave_max_dpp(fmaxf(fmaxf(zv[0], zv[1]), fmaxf(zv[2], zv[3])));
     float p = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i < E) p += expf(zv[i] - zmax);
-    zsum = wave_sum_dpp(p);
+      if (lane + 64 * i < E) p += fast_exp(zv[i] - zmax);
+    rzsum = __builtin_amdgcn_rcpf(wave_sum_dpp(p));
   }
   uint32_t hi[4], key[4];
 #pragma unroll
@@ -160,9 +184,9 @@ __device__ __forceinline__ void topk_wave(const float zv[4], const float bv[4], 
     const bool in = e < E;
     float sc = zv[i];
     if (scoring == 1)
-      sc = 1.0f / (1.0f + expf(-zv[i])) + bv[i];
+      sc = fast_sigmoid(zv[i]) + bv[i];
     else if (has_bias)
-      sc = expf(zv[i] - zmax) / zsum + bv[i];
+      sc = fast_exp(zv[i] - zmax) * rzsum + bv[i];
     hi[i] = in ? ordered_bits(sc) : 0u;
     key[i] = in ? ((hi[i] & 0xffffff00u) | (255u - (uint32_t)e)) : 0u;
   }
@@ -180,14 +204,12 @@ __device__ __forceinline__ void topk_wave(const float zv[4], const float bv[4], 
   uint32_t mine = 0u;
   for (int j = 0; j <= k; ++j) {
     const uint32_t m = wave_max_u32(key[0]);
-    const int lw = (int)(255u - (m & 255u)) & 63;  // the winner's lane
-    if (lane == lw) {
-      key[0] = key[1];
-      key[1] = key[2];
-      key[2] = key[3];
-      key[3] = 0u;
-    }
-    if (lane == j) mine = m;
+    const bool win = lane == ((int)(255u - (m & 255u)) & 63);  // the winner's lane
+    key[0] = win ? key[1] : key[0];
+    key[1] = win ? key[2] : key[1];
+    key[2] = win ? key[3] : key[2];
+    key[3] = win ? 0u : key[3];
+    mine = lane == j ? m : mine;
   }
   const uint32_t next = (uint32_t)__shfl((int)mine, lane + 1 < 64 ? lane + 1 : lane, 64);
   const bool amb = lane < k && (mine >> 8) == (next >> 8);
@@ -201,8 +223,18 @@ __device__ __forceinline__ void topk_wave(const float zv[4], const float bv[4], 
   const float z2 = __shfl(zv[2], src, 64), z3 = __shfl(zv[3], src, 64);
   const float my_z = reg == 0 ? z0 : (reg == 1 ? z1 : (reg == 2 ? z2 : z3));
   float w = 0.f;
-  if (lane < k) w = (scoring == 0) ? expf(my_z - zmax) / zsum : 1.0f / (1.0f + expf(-my_z));
-  if (renorm) w = w / wave_sum_dpp(w);
+  if (scoring == 1) {
+    w = fast_sigmoid(my_z);
+  } else if (full_softmax) {
+    w = fast_exp(my_z - zmax) * rzsum;
+  } else {
+    // renormalised softmax: relative to the first choice's logit, the largest
+    const float z_first = __builtin_bit_cast(
+        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, my_z)));
+    w = fast_exp(my_z - z_first);
+  }
+  w = lane < k ? w : 0.f;
+  if (renorm) w = w * __builtin_amdgcn_rcpf(wave_sum_dpp(w));
   my_w = w * rsf;
 }
 

@@ -111,6 +111,21 @@ def assert_elementwise(got, y, y_sq, label, rounded_output=True):
     return float((diff / np.where(bound > 0, bound, 1.0)).max())
 
 
+def assert_same_up_to_order(a, b, y_sq, label):
+    """Two BF16 outputs of the FP32-atomic mode for the same input. The
+    atomic adds land in a different order each run, so the FP32 sums may
+    differ by reassociation, about sqrt(K) * 2^-24 * sqrt(y_sq) for K terms
+    (y_sq: the oracle's sum of squared terms), and the BF16 rounding may then
+    fall on either side: allowed, one BF16 step of the larger value plus
+    1e-4 * sqrt(y_sq), which is 30 times the reassociation error at K = 2^16."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    tol = np.maximum(np.abs(a), np.abs(b)) * 2.0 ** -7 + 1e-4 * np.sqrt(np.asarray(y_sq))
+    bad = np.abs(a - b) > tol
+    assert not bad.any(), (f"{label}: {int(bad.sum())} elements differ, e.g. "
+                           f"{a[bad][:3]} vs {b[bad][:3]}")
+
+
 def check_grouping(L, n, ref_idx, num_experts, expert_range=None):
     """The grouped path's permutation against the oracle's, bit for bit
     (of one expert-parallel share's experts, with ``expert_range``)."""
