@@ -137,8 +137,17 @@ __device__ __forceinline__ int nth_token(uint32_t mask, int j) {
 // ---------------------------------------------------------------------------
 template <int F, int NM, int RPL>
 struct Stream {
+  // FP4 block scales: BPC bytes per 16-byte chunk. The scale bits of one
+  // pass (lpr * IT chunks of a row) are contiguous, so lane li of a group
+  // fetches 32-bit word li (and lpr + li when SW == 2) of them, one load per
+  // row, and spread() deals each lane the bits of its own IT chunks.
+  static constexpr bool kChunkScales = F == FMT_MXFP4 || F == FMT_NVFP4;
+  static constexpr int BPC = F == FMT_NVFP4 ? 2 : 1;
+  static constexpr int CPW = 4 / BPC;             // chunks per scale word
+  static constexpr int SW = kChunkScales ? IT / CPW : 1;  // scale words per lane per row
   uint4 wq[IT][NM][RPL];
   uint32_t sc[IT][NM][RPL];
+  uint32_t sw[NM][RPL][SW];
   float acc[NM][RPL][kNmax];
 
   __device__ __forceinline__ void zero() {
@@ -150,11 +159,62 @@ struct Stream {
         for (int t = 0; t < kNmax; ++t) acc[m][r][t] = 0.f;
   }
 
+  // the scale words of the pass at chunk c0 (issued ahead of its weights).
+  // Scale rows that are not 4-byte aligned take their bytes one by one.
+  __device__ __forceinline__ void load_scales(const MatView (&mv)[NM], int row_base, int nrows,
+                                              int cpr, int lpr, int li, int c0) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const bool whole = ((mv[m].scale_row_bytes | (int)(uintptr_t)mv[m].scales) & 3) == 0;
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        const int row = row_base + r;
+#pragma unroll
+        for (int w = 0; w < SW; ++w) {
+          const int cw = c0 + (w * lpr + li) * CPW;  // first chunk of the word
+          uint32_t v = 0u;
+          if (row < nrows && cw < cpr) {
+            const uint8_t* p = mv[m].scales + (size_t)row * mv[m].scale_row_bytes + cw * BPC;
+            if (whole) {
+              v = *reinterpret_cast<const uint32_t*>(p);
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                if (cw + j / BPC < cpr) v |= (uint32_t)p[j] << (8 * j);
+            }
+          }
+          sw[m][r][w] = v;
+        }
+      }
+    }
+  }
+
+  // sc[it] = the scale bits of chunk c0 + it*lpr + li: word
+  // (it*lpr + li) / CPW of the pass, i.e. word it / CPW of lane
+  // (it % CPW) * lpr / CPW + li / CPW of the group. Every lane of the wave
+  // takes part (a permute reads zero from an inactive lane).
+  __device__ __forceinline__ void spread(int lpr, int li) {
+    const int lane = threadIdx.x & 63;
+    const int base = lane - li + li / CPW;
+    const int shift = (li % CPW) * 8 * BPC;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int addr = (base + (it % CPW) * (lpr / CPW)) * 4;
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int r = 0; r < RPL; ++r)
+          sc[it][m][r] =
+              (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)sw[m][r][it / CPW]) >> shift;
+    }
+  }
+
   // chunk sets I0 .. I1-1 of one pass (the pipelined loops below fetch the
   // two halves of the next pass while computing the two halves of this one)
   template <int I0, int I1>
   __device__ __forceinline__ void load_its(const MatView (&mv)[NM], int row_base, int nrows,
                                            int cpr, int lpr, int li, int c0) {
+    if constexpr (kChunkScales && I0 == 0) load_scales(mv, row_base, nrows, cpr, lpr, li, c0);
 #pragma unroll
     for (int it = I0; it < I1; ++it) {
       const int c = c0 + it * lpr + li;
@@ -163,14 +223,10 @@ struct Stream {
 #pragma unroll
         for (int r = 0; r < RPL; ++r) {
           const int row = row_base + r;
-          if (c < cpr && row < nrows) {
+          if (c < cpr && row < nrows)
             wq[it][m][r] = ldg16(mv[m].data + (size_t)row * mv[m].row_bytes + (size_t)c * 16);
-            sc[it][m][r] =
-                load_chunk_scale<F>(mv[m].scales + (size_t)row * mv[m].scale_row_bytes, c);
-          } else {
+          else
             wq[it][m][r] = make_uint4(0u, 0u, 0u, 0u);
-            sc[it][m][r] = 0u;
-          }
         }
       }
     }
@@ -185,6 +241,7 @@ struct Stream {
   __device__ __forceinline__ void compute_its(int cpr, int lpr, int li, int c0, const uint32_t* xs,
                                               int xs_tok_words, uint32_t mask) {
     constexpr int XW = Fmt<F>::VPC / 2;  // 32-bit activation words per chunk
+    if constexpr (kChunkScales && I0 == 0) spread(lpr, li);
 #pragma unroll
     for (int it = I0; it < I1; ++it) {
       const int c = c0 + it * lpr + li;
