@@ -57,8 +57,65 @@ struct ARow {
   const uint8_t* scales;  // FP4: start of the row's block scales
 };
 
+// 16 and 12 bytes read with one load from a 4-byte aligned address
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x3_a4 __attribute__((ext_vector_type(3), aligned(4)));
+
+// FP4 block scales of block blk (chunks 4 blk .. 4 blk + 3) of a row. MXFP4
+// keeps one E8M0 byte per 32 values, bytes 4c .. 4c+3 for the four K groups
+// of chunk c; NVFP4 two E4M3 bytes per 32 values, bytes 8c + 2g, 8c + 2g + 1
+// for group g. The block's 16 (MXFP4) or 32 (NVFP4) scale bytes are
+// contiguous, so a "whole" block (all four chunks present, scales 4-byte
+// aligned) is read with wide loads: MXFP4 one 16-byte load (sc[ql] = word
+// ql, group g's byte at bit 8g), NVFP4 two 12-byte loads from word g/2 of
+// each chunk pair (sc[ql] = the word that holds group g's half-word, at bit
+// 16 (g&1)). Any other block is read chunk by chunk (sc[ql] = the bits
+// themselves). Nothing here waits for a load; a_operand finds the bits.
 template <int F>
-__device__ __forceinline__ void load_block(WBlock& b, const ARow& r, int blk, int g, int nchunks) {
+__device__ __forceinline__ void load_block_scales(WBlock& b, const ARow& r, int blk, int g,
+                                                  int nchunks, bool whole) {
+  if constexpr (F == FMT_MXFP4) {
+    if (whole) {
+      const u32x4_a4 s = *reinterpret_cast<const u32x4_a4*>(r.scales + blk * 16);
+      b.sc[0] = s.x;
+      b.sc[1] = s.y;
+      b.sc[2] = s.z;
+      b.sc[3] = s.w;
+    } else {
+#pragma unroll
+      for (int ql = 0; ql < 4; ++ql) {
+        const int c = blk * 4 + ql;
+        b.sc[ql] = c < nchunks ? (uint32_t)r.scales[c * 4 + g] : 0u;
+      }
+    }
+  } else if constexpr (F == FMT_NVFP4) {
+    if (whole) {
+      const uint8_t* p = r.scales + blk * 32 + 4 * (g >> 1);
+      const u32x3_a4 s0 = *reinterpret_cast<const u32x3_a4*>(p);
+      const u32x3_a4 s1 = *reinterpret_cast<const u32x3_a4*>(p + 16);
+      b.sc[0] = s0.x;
+      b.sc[1] = s0.z;
+      b.sc[2] = s1.x;
+      b.sc[3] = s1.z;
+    } else {
+#pragma unroll
+      for (int ql = 0; ql < 4; ++ql) {
+        const int c = blk * 4 + ql;
+        b.sc[ql] =
+            c < nchunks ? (uint32_t)*reinterpret_cast<const uint16_t*>(r.scales + c * 8 + g * 2) : 0u;
+      }
+    }
+  }
+}
+
+// Whether block blk of rows with these scales is read whole (see above).
+__device__ __forceinline__ bool scales_whole(bool aligned4, int blk, int nchunks) {
+  return aligned4 && blk * 4 + 4 <= nchunks;
+}
+
+template <int F>
+__device__ __forceinline__ void load_block(WBlock& b, const ARow& r, int blk, int g, int nchunks,
+                                           bool whole) {
   constexpr int LPC = GF<F>::LPC;
   constexpr int XPB = 4 / LPC;  // chunks per block
 #pragma unroll
@@ -72,16 +129,14 @@ __device__ __forceinline__ void load_block(WBlock& b, const ARow& r, int blk, in
     else if constexpr (F == FMT_FP8) off = c * 128 + q * 64 + g * 16;
     else off = (c * 128 + g * 32) / 2;
     b.q[ql] = *reinterpret_cast<const uint4*>(r.data + off);
-    if constexpr (F == FMT_MXFP4) b.sc[ql] = r.scales[c * 4 + g];
-    else if constexpr (F == FMT_NVFP4)
-      b.sc[ql] = *reinterpret_cast<const uint16_t*>(r.scales + (c * 8 + g * 2));
-    else b.sc[ql] = 0u;
   }
+  if constexpr (F == FMT_MXFP4 || F == FMT_NVFP4)
+    load_block_scales<F>(b, r, blk, g, nchunks, whole);
 }
 
 // The eight BF16 A values of K-step h of load ql.
 template <int F>
-__device__ __forceinline__ bf16x8 a_operand(const WBlock& b, int ql, int h) {
+__device__ __forceinline__ bf16x8 a_operand(const WBlock& b, int ql, int h, int g, bool whole) {
   const uint4 v = b.q[ql];
   if constexpr (F == FMT_BF16) {
     return __builtin_bit_cast(bf16x8, v);
@@ -96,7 +151,7 @@ __device__ __forceinline__ bf16x8 a_operand(const WBlock& b, int ql, int h) {
   } else if constexpr (F == FMT_MXFP4) {
     // the E8M0 block scale is a power of two: the scaled convert applies it
     const uint32_t d = h == 0 ? v.x : (h == 1 ? v.y : (h == 2 ? v.z : v.w));
-    const float s = e8m0_to_f32(b.sc[ql]);
+    const float s = e8m0_to_f32((whole ? b.sc[ql] >> (8 * g) : b.sc[ql]) & 0xffu);
     const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 0);
     const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 1);
     const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 2);
@@ -108,7 +163,8 @@ __device__ __forceinline__ bf16x8 a_operand(const WBlock& b, int ql, int h) {
     // the E4M3 block scale (which has mantissa bits) multiplies in FP32; the
     // product has at most 6 significant bits and converts to BF16 exactly
     const uint32_t d = h == 0 ? v.x : (h == 1 ? v.y : (h == 2 ? v.z : v.w));
-    const f32x2 s2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(b.sc[ql], 1.0f, false);
+    const uint32_t bits = whole ? b.sc[ql] >> (16 * (g & 1)) : b.sc[ql];
+    const f32x2 s2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(bits, 1.0f, false);
     const float s = h < 2 ? s2.x : s2.y;
     const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
     const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
@@ -164,7 +220,7 @@ __device__ __forceinline__ void x_store(uint4* buf, const uint4 (&v)[NT]) {
 // against NT token tiles.
 template <int F, int NA, int NT>
 __device__ __forceinline__ void mma_chunk(f32x4 (&acc)[NA][NT], const WBlock (&w)[NA], int xc,
-                                          const uint4* buf) {
+                                          const uint4* buf, bool whole) {
   constexpr int LPC = GF<F>::LPC, SPL = GF<F>::SPL;
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
@@ -175,7 +231,7 @@ __device__ __forceinline__ void mma_chunk(f32x4 (&acc)[NA][NT], const WBlock (&w
     for (int h = 0; h < SPL; ++h) {
       bf16x8 A[NA];
 #pragma unroll
-      for (int t = 0; t < NA; ++t) A[t] = a_operand<F>(w[t], ql, h);
+      for (int t = 0; t < NA; ++t) A[t] = a_operand<F>(w[t], ql, h, g, whole);
       const int u = 4 * SPL * q + SPL * g + h;
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
@@ -211,14 +267,19 @@ __device__ __forceinline__ void stream_gemm(f32x4 (&acc)[NA][NT], const ARow (&r
   x_store<NT>(buf0, xv);
   const int nblk = (nchunks + XPB - 1) / XPB;
   WBlock cur[NA], nxt[NA];
+  // FP4 scales of one matrix share their alignment (rows and experts are
+  // multiples of 4 bytes apart)
+  const bool al4 = ((uintptr_t)rows[0].scales & 3) == 0;
 #pragma unroll
-  for (int t = 0; t < NA; ++t) load_block<F>(cur[t], rows[t], 0, g, nchunks);
+  for (int t = 0; t < NA; ++t)
+    load_block<F>(cur[t], rows[t], 0, g, nchunks, scales_whole(al4, 0, nchunks));
   __syncthreads();
   for (int blk = 0; blk < nblk; ++blk) {
     // the next block's weights are in flight while this one is multiplied
     if (blk + 1 < nblk) {
 #pragma unroll
-      for (int t = 0; t < NA; ++t) load_block<F>(nxt[t], rows[t], blk + 1, g, nchunks);
+      for (int t = 0; t < NA; ++t)
+        load_block<F>(nxt[t], rows[t], blk + 1, g, nchunks, scales_whole(al4, blk + 1, nchunks));
     }
 #pragma unroll
     for (int xc = 0; xc < XPB; ++xc) {
@@ -226,7 +287,7 @@ __device__ __forceinline__ void stream_gemm(f32x4 (&acc)[NA][NT], const ARow (&r
       if (XPB > 1 && c >= nchunks) break;
       const bool more = c + 1 < nchunks;
       if (more) x_fetch<NT>(xv, xr, x, c + 1);
-      mma_chunk<F, NA, NT>(acc, cur, xc, (c & 1) ? buf1 : buf0);
+      mma_chunk<F, NA, NT>(acc, cur, xc, (c & 1) ? buf1 : buf0, scales_whole(al4, blk, nchunks));
       if (more) x_store<NT>((c & 1) ? buf0 : buf1, xv);
       __syncthreads();
     }
