@@ -412,12 +412,19 @@ __device__ __forceinline__ void topk_and_plan(const DecodeArgs& a, TopkScratch* 
   // the bias does not depend on the logits: read it before waiting for them
   float bv[4];
   load_bias4(a.tid2eid ? nullptr : a.router_bias, a.EW, lane, bv);
-  // wave t routes token t (N <= kNmax waves); lane j < k holds slot (t, j)
+  // wave t routes token t (N <= kNmax waves); lane j < k holds slot (t, j).
+  // The routing's global outputs (logits, indices, weights, slot flags) are
+  // written after the plan is published: the barriers below then wait for
+  // LDS only, not for those stores.
+  static_assert(kThreads / 64 >= kNmax, "one routing wave per token");
+  const int rt = wave;  // the token this wave routes
+  const bool routes = rt < a.N;
   int slot_e = -1;
   float slot_w = 0.f;
-  for (int t = wave; t < a.N; t += kThreads / 64) {
-    const int id = a.tid2eid ? a.token_ids[t] : 0;  // hash routing: the token's id
-    const u64* zrow = a.ctl->zlog + t * 256;
+  float zv[4];
+  if (routes) {
+    const int id = a.tid2eid ? a.token_ids[rt] : 0;  // hash routing: the token's id
+    const u64* zrow = a.ctl->zlog + rt * 256;
     u64 zw[4] = {(u64)tag, (u64)tag, (u64)tag, (u64)tag};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -434,13 +441,8 @@ __device__ __forceinline__ void topk_and_plan(const DecodeArgs& a, TopkScratch* 
       for (int i = 0; i < 4; ++i)
         if ((unsigned)zw[i] != tag) zw[i] = ld_coh64(zrow + lane + 64 * i);
     }
-    float zv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      zv[i] = e < a.EW ? tag_value(zw[i]) : -INFINITY;
-      if (a.out_logits && e < a.EW) a.out_logits[(size_t)t * a.EW + e] = zv[i];
-    }
+    for (int i = 0; i < 4; ++i) zv[i] = lane + 64 * i < a.EW ? tag_value(zw[i]) : -INFINITY;
     int my_e;
     float w;
     if (!route_token(zv, bv, a.router_bias != nullptr, a.tid2eid, a.vocab, id, a.EW, a.k,
@@ -448,11 +450,7 @@ __device__ __forceinline__ void topk_and_plan(const DecodeArgs& a, TopkScratch* 
         lane == 0)
       set_error(a, kErrHashInput);
     if (lane < a.k) {
-      const int sl = t * a.k + lane;
-      if (a.out_idx) a.out_idx[sl] = (uint32_t)my_e;
-      if (a.out_w) a.out_w[sl] = w;
       const bool real = my_e >= a.e_lo && my_e < a.e_hi;
-      if (a.slot_flags) st_coh64(&a.ctl->slot_real[sl], tagged_u(real ? 1u : 0u, tag));
       if (real) atomicOr(&s->bits[my_e >> 5], 1u << (my_e & 31));
       slot_e = my_e;
       slot_w = w;
@@ -479,7 +477,7 @@ __device__ __forceinline__ void topk_and_plan(const DecodeArgs& a, TopkScratch* 
       word = q == wq ? bw[q] : word;
     }
     u += __popc(word & ((1u << (slot_e & 31)) - 1u));
-    const int t = wave, j = lane;
+    const int t = rt, j = lane;
     s->uexp[u] = slot_e;
     s->jpos[u * kNmax + t] = j;
     s->uw[u * kNmax + t] = slot_w;
@@ -504,6 +502,22 @@ __device__ __forceinline__ void topk_and_plan(const DecodeArgs& a, TopkScratch* 
     u64* p = a.ctl->plan + u * kPlanStride + 2 * t;
     st_coh64(p, tagged_u(info, tag));
     st_coh64(p + 1, tagged(wt, tag));
+  }
+  // the routing's outputs
+  if (routes) {
+    if (a.out_logits) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (lane + 64 * i < a.EW) a.out_logits[(size_t)rt * a.EW + lane + 64 * i] = zv[i];
+    }
+    if (lane < a.k) {
+      const int sl = rt * a.k + lane;
+      if (a.out_idx) a.out_idx[sl] = (uint32_t)slot_e;
+      if (a.out_w) a.out_w[sl] = slot_w;
+      if (a.slot_flags)
+        st_coh64(&a.ctl->slot_real[sl],
+                 tagged_u(slot_e >= a.e_lo && slot_e < a.e_hi ? 1u : 0u, tag));
+    }
   }
 }
 
