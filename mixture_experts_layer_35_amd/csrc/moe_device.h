@@ -143,6 +143,16 @@ __device__ __forceinline__ float row_scale(const MatView& m, int row) {
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
 
+// Workgroup barrier that orders LDS accesses only: it waits for this wave's
+// LDS operations, not for its outstanding global stores (a __syncthreads
+// waits for those too). For phases that exchange data through LDS while
+// global results are still being written.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Sum over aligned groups of `width` lanes (width a power of two <= 64).
 __device__ __forceinline__ float group_sum(float v, int width) {
   for (int m = width >> 1; m > 0; m >>= 1) v += __shfl_xor(v, m, 64);

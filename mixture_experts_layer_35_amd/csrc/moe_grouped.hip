@@ -41,9 +41,17 @@ template <int NT>
 __global__ __launch_bounds__(kGThreads) void k_g_router(GroupedArgs a) {
   extern __shared__ uint4 g_lds[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  // clear the token masks (the top-k kernel, launched next, sets them)
+  // clear the token masks (the top-k kernel, launched next, sets them) and,
+  // with FP32 accumulation, the accumulator the down kernel adds into
   for (int i = blockIdx.x * kGThreads + tid; i < a.EL * a.W; i += gridDim.x * kGThreads)
     a.mask[i] = 0u;
+  if (a.atomic) {
+    float4* acc4 = reinterpret_cast<float4*>(a.acc);
+    const int64_t n4 = (int64_t)a.N * a.H / 4;
+    for (int64_t i = (int64_t)blockIdx.x * kGThreads + tid; i < n4;
+         i += (int64_t)gridDim.x * kGThreads)
+      acc4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   if (blockIdx.x == 0 && tid == 0) *a.ticket = 0u;
   const int s = blockIdx.x % a.ksplit;
   const int tg = (blockIdx.x / a.ksplit) % a.r_tg;
@@ -136,6 +144,9 @@ __global__ __launch_bounds__(kGThreads) void k_g_topk(GroupedArgs a) {
   __shared__ int s_last;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kGThreads / 64) + (threadIdx.x >> 6);
+  float zv[4] = {0.f, 0.f, 0.f, 0.f};
+  int my_e = 0;
+  float my_w = 0.f, gate_logit = 0.f;
   if (t < a.N) {
     const int id = a.tid2eid ? a.token_ids[t] : 0;  // hash routing: the token's id
     float bv[4];
@@ -143,7 +154,6 @@ __global__ __launch_bounds__(kGThreads) void k_g_topk(GroupedArgs a) {
     // sum the K-range partials of the lane's four logits in ascending range
     // order; lanes read consecutive experts, 16 ranges at a time
     const int ks = a.ksplit;
-    float zv[4] = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < ks; s0 += 16) {
       float v[4][16];
 #pragma unroll
@@ -161,48 +171,48 @@ __global__ __launch_bounds__(kGThreads) void k_g_topk(GroupedArgs a) {
         for (int q = 0; q < 16; ++q) zv[i] += v[i][q];
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      if (e < a.EW) {
-        if (a.out_logits) a.out_logits[(int64_t)t * a.EW + e] = zv[i];
-      } else {
-        zv[i] = -INFINITY;
-      }
-    }
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i >= a.EW) zv[i] = -INFINITY;
+    float g = 0.f;
     if (a.shared_gate && lane == 0) {
       // the shared-expert weight sigmoid(x . w_sg), from router row EW
-      float g = 0.f;
       for (int q = 0; q < ks; ++q) g += a.zpart[((int64_t)t * ks + q) * a.ER + a.EW];
-      a.gamma[t] = 1.0f / (1.0f + expf(-g));
     }
-    int my_e;
-    float w;
     if (!route_token(zv, bv, a.router_bias != nullptr, a.tid2eid, a.vocab, id, a.EW, a.k,
-                     a.scoring, a.renorm, a.rsf, lane, my_e, w) &&
+                     a.scoring, a.renorm, a.rsf, lane, my_e, my_w) &&
         lane == 0)
       __hip_atomic_fetch_or(a.err, kErrHashInput, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (lane < a.k) {
-      const int sl = t * a.k + lane;
-      st_dev(a.idx + sl, my_e);
-      a.wts[sl] = w;
-      if (a.out_idx) a.out_idx[sl] = (uint32_t)my_e;
-      if (a.out_w) a.out_w[sl] = w;
+      st_dev(a.idx + t * a.k + lane, my_e);
       const int el = my_e - a.e_lo;  // only this call's experts are grouped
       if (el >= 0 && el < a.EL) atomicOr(a.mask + (int64_t)el * a.W + (t >> 5), 1u << (t & 31));
     }
-    if (a.atomic) {
-      float4* row = reinterpret_cast<float4*>(a.acc + (int64_t)t * a.H);
-      for (int i = lane; i < a.H / 4; i += 64) row[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    gate_logit = g;
   }
   // the last workgroup to arrive groups the slots. idx is written with
   // device-coherent stores and mask with device atomics; each workgroup waits
-  // for its own to complete before taking its ticket, and the last one reads
-  // them with device-coherent loads (no cache-wide fence either way)
+  // for those to complete before taking its ticket (the only stores issued
+  // so far), and the last one reads them with device-coherent loads (no
+  // cache-wide fence either way)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) s_last = atomicAdd(a.ticket, 1u) == gridDim.x - 1;
   __syncthreads();
+  // the routing's other results (read by later launches or the caller only)
+  if (t < a.N) {
+    if (a.out_logits) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (lane + 64 * i < a.EW) a.out_logits[(int64_t)t * a.EW + lane + 64 * i] = zv[i];
+    }
+    if (a.shared_gate && lane == 0) a.gamma[t] = 1.0f / (1.0f + expf(-gate_logit));
+    if (lane < a.k) {
+      const int sl = t * a.k + lane;
+      a.wts[sl] = my_w;
+      if (a.out_idx) a.out_idx[sl] = (uint32_t)my_e;
+      if (a.out_w) a.out_w[sl] = my_w;
+    }
+  }
   if (!s_last) return;
   group_slots(a, g_lds);
 }
@@ -239,7 +249,7 @@ __device__ void group_slots(const GroupedArgs& a, uint4* g_lds) {
   const bool staged = E * W <= kMaskLdsWords;
   if (staged)
     for (int i = tid; i < E * W; i += kT) mlds[i] = ld_dev(a.mask + i);
-  __syncthreads();
+  lds_barrier();
   auto mword = [&](int i) { return staged ? mlds[i] : ld_dev(a.mask + i); };
   // tokens per expert: thread e sums its mask words
   if (tid < E) {
@@ -247,7 +257,7 @@ __device__ void group_slots(const GroupedArgs& a, uint4* g_lds) {
     for (int i = 0; i < W; ++i) c += __popc(mword(tid * W + i));
     cnt[tid] = c;
   }
-  __syncthreads();
+  lds_barrier();
   // padded exclusive scan, the unit list and the work items (wave 0, four
   // experts per lane): a unit of c rows has ceil(c / T) items, T = 16 * nt
   // rows per pass of the expert kernels
@@ -301,7 +311,7 @@ __device__ void group_slots(const GroupedArgs& a, uint4* g_lds) {
       base[E] = ip;
     }
   }
-  __syncthreads();
+  lds_barrier();
   // padding rows
   if (tid < E) {
     for (int r = base[tid] + cnt[tid]; r < base[tid + 1]; ++r) {
@@ -321,7 +331,7 @@ __device__ void group_slots(const GroupedArgs& a, uint4* g_lds) {
         run += __popc(mword(tid * W + i));
       }
     }
-    __syncthreads();
+    lds_barrier();
     // eight slots per thread per pass, their loads issued together
     for (int s0 = 0; s0 < nslots; s0 += 8 * kT) {
       int ev[8];
@@ -351,7 +361,7 @@ __device__ void group_slots(const GroupedArgs& a, uint4* g_lds) {
         a.inv[sl] = pos;
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
