@@ -360,7 +360,7 @@ moe::StageGeom gate_up_geom(int fmt, int H, int rows, int rpl, int tokens, int u
 
 // Down geometry: a workgroup stages its unit's activations once (tagged BF16
 // pairs, 4 bytes per value and token) and streams `sub` row blocks, enough
-// that the staged bytes stay under a quarter of the weight bytes, while the
+// that the staged bytes stay under an eighth of the weight bytes, while the
 // grid keeps at least min_wgs workgroups. sub stays a power of two, so that row
 // tiles of the routed and the shared expert nest in the blend blocks.
 moe::StageGeom down_geom(int fmt, int I, int H, int rpl, int tokens, int units, int min_wgs) {
@@ -370,7 +370,7 @@ moe::StageGeom down_geom(int fmt, int I, int H, int rpl, int tokens, int units, 
   const int64_t block_bytes = (int64_t)one.rows_per_wg * (db + sb);
   const int64_t staged = (int64_t)tokens * I * 4;
   int sub = 1;
-  while (sub < 16 && sub * block_bytes < 4 * staged) sub <<= 1;
+  while (sub < 16 && sub * block_bytes < 8 * staged) sub <<= 1;
   auto tiles = [&](int s) { return (H + one.rows_per_wg * s - 1) / (one.rows_per_wg * s); };
   while (sub > 1 && (int64_t)units * tiles(sub) < min_wgs) sub >>= 1;
   return moe::stage_geom(fmt, I, H, rpl, sub);
