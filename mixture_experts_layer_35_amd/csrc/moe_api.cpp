@@ -660,6 +660,21 @@ moe_status forward_impl(const moe_cfg* cfg, const moe_router* router, const moe_
   a.blend_rows = a.dr.rows_per_wg;
   if (a.I_s > 0 && a.ds.rows_per_wg > a.blend_rows) a.blend_rows = a.ds.rows_per_wg;
   a.spin_limit = 1u << 22;
+  // When the whole grid is resident (small calls), the down workgroups read
+  // the plan together with the gate+up workgroups, and their first weight
+  // requests would share the memory system with the gate+up weights that the
+  // chain waits for. They hold back for about as long as those bytes take to
+  // stream at about 6 TB/s (100 MHz ticks; at most 10 us). Below 0.5 us
+  // there is nothing to gain and they start at once.
+  {
+    const double gu = (double)a.maxu * (a.gate.expert_bytes + a.gate.scale_expert_bytes +
+                                        a.up.expert_bytes + a.up.scale_expert_bytes) +
+                      (a.I_s > 0 ? (double)(a.sgate.expert_bytes + a.sgate.scale_expert_bytes +
+                                            a.sup.expert_bytes + a.sup.scale_expert_bytes)
+                                 : 0.0);
+    const double ticks = gu / 6e12 * 1e8;
+    a.d_defer_ticks = ticks < 50.0 ? 0u : (unsigned)(ticks < 1000.0 ? ticks : 1000.0);
+  }
 
   char* base = static_cast<char*>(workspace);
   moe_cfg cc = *cfg;

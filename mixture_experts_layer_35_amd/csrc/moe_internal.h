@@ -99,6 +99,10 @@ struct DecodeArgs {
   StageGeom gr, gs, dr, ds;
   int blend_rows;  // output rows per blend block
   unsigned spin_limit;
+  // routed down workgroups wait this long (100 MHz realtime ticks) after
+  // reading the plan before they request weights; zero unless the call's
+  // whole grid is resident at once (set at launch)
+  unsigned d_defer_ticks;
   // workspace
   Ctl* ctl;
   unsigned* blend_ctr;  // [ceil(H / blend_rows) * kLineWords]

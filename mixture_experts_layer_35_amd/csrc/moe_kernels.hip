@@ -43,6 +43,8 @@
 // converts, then into v_dot2_f32_bf16 against BF16 activations; block scales
 // multiply per-chunk partial sums, row and tensor scales the row result; FP32
 // accumulation throughout.
+#include <mutex>
+
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -1033,9 +1035,16 @@ __device__ __forceinline__ void down_phase(const DecodeArgs& a, int wg, uint4* s
     const int tile = r - unit * a.dr.tiles;
     row0 = tile * a.dr.rows_per_wg;
     int e;
-    if (read_plan(a, unit, tag, e, slots, wt, mask, s_words))
+    const unsigned defer = a.d_defer_ticks;  // (read before the plan's loads)
+    if (read_plan(a, unit, tag, e, slots, wt, mask, s_words)) {
+      if (defer) {
+        // (a resident grid: let the gate+up weights stream first)
+        const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+        while (__builtin_amdgcn_s_memrealtime() - t0 < defer) __builtin_amdgcn_s_sleep(2);
+      }
       down_tile<FR, kDownRpl<RPL>>(a, a.down, e - a.e_lo, tile, a.dr, a.I, smem, mask, slots, wt, a.a_routed,
                          false, tag);
+    }
   }
   const int bt = row0 / a.blend_rows;
   const int rows_bt = min(a.blend_rows, a.H - bt * a.blend_rows);
@@ -1138,6 +1147,34 @@ size_t decode_lds_bytes(int H, int I, int I_s) {
 // With trace events, the launch goes through hipExtLaunchKernel, which
 // stamps the events at the kernel's own start and end (the same interval a
 // kernel trace reports) rather than around the enqueue.
+// Workgroups of kernel fn (kThreads threads, lds bytes of dynamic LDS) that
+// the current device holds at once. Queried once per device, kernel and LDS
+// size, into a fixed table (no allocation: the no-workspace entry point
+// launches through here too).
+static int resident_wgs(const void* fn, size_t lds) {
+  struct Entry {
+    int dev;
+    const void* fn;
+    size_t lds;
+    int v;
+  };
+  static Entry table[128];
+  static int used = 0;
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < used; ++i)
+    if (table[i].dev == dev && table[i].fn == fn && table[i].lds == lds) return table[i].v;
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, kThreads, lds) != hipSuccess) per = 0;
+  const int v = cus * per;  // 0 when unknown: never taken for resident
+  if (used < 128) table[used++] = Entry{dev, fn, lds, v};
+  return v;
+}
+
 template <int FR, int FS>
 static hipError_t launch(const DecodeArgs& a, int rpl, size_t lds, hipStream_t st, hipEvent_t e0,
                          hipEvent_t e1) {
@@ -1145,6 +1182,7 @@ static hipError_t launch(const DecodeArgs& a, int rpl, size_t lds, hipStream_t s
   const void* fn = rpl == 2 ? reinterpret_cast<const void*>(&k_moe_decode<FR, FS, 2>)
                             : reinterpret_cast<const void*>(&k_moe_decode<FR, FS, 1>);
   DecodeArgs copy = a;
+  if (copy.d_defer_ticks && blocks > resident_wgs(fn, lds)) copy.d_defer_ticks = 0;
   void* args[] = {&copy};
   if (e0 || e1)
     return hipExtLaunchKernel(fn, dim3(blocks), dim3(kThreads), args, lds, st, e0, e1, 0);
