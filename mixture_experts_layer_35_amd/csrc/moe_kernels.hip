@@ -114,6 +114,13 @@ __device__ __forceinline__ unsigned wg_signal(unsigned* p, unsigned* s_tmp, bool
   return *s_tmp;
 }
 
+// One workgroup's report to its done group, made by thread 0 after a
+// barrier that followed every wave's read of the call's tag. Returns the
+// count before it, which the workgroup looks at only when it ends.
+__device__ __forceinline__ unsigned arrive_early(unsigned* p) {
+  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <typename T>
 __device__ __forceinline__ T sel4(int i, T v0, T v1, T v2, T v3) {
   return i == 0 ? v0 : (i == 1 ? v1 : (i == 2 ? v2 : v3));
@@ -985,7 +992,8 @@ constexpr int kDownRpl = RPL == 2 ? 4 : RPL;
 
 template <int FR, int FS, int RPL>
 __device__ __forceinline__ void down_phase(const DecodeArgs& a, int wg, uint4* smem, unsigned* s_tmp,
-                           u64* s_words, unsigned& tag) {
+                           u64* s_words, unsigned& tag, unsigned* done_ctr, bool& arrived,
+                           unsigned& done_old) {
   int slots[kNmax];
   float wt[kNmax];
   uint32_t mask = 0;
@@ -1019,6 +1027,8 @@ __device__ __forceinline__ void down_phase(const DecodeArgs& a, int wg, uint4* s
           s_words[threadIdx.x] = v;
         }
         __syncthreads();
+        arrived = true;
+        if (threadIdx.x == 0) done_old = arrive_early(done_ctr);
 #pragma unroll
         for (int t = 0; t < kNmax; ++t)
           if (t < a.N) wt[t] = 1.0f / (1.0f + expf(-tag_value(s_words[t])));
@@ -1036,7 +1046,10 @@ __device__ __forceinline__ void down_phase(const DecodeArgs& a, int wg, uint4* s
     row0 = tile * a.dr.rows_per_wg;
     int e;
     const unsigned defer = a.d_defer_ticks;  // (read before the plan's loads)
-    if (read_plan(a, unit, tag, e, slots, wt, mask, s_words)) {
+    const bool present = read_plan(a, unit, tag, e, slots, wt, mask, s_words);
+    arrived = true;
+    if (threadIdx.x == 0) done_old = arrive_early(done_ctr);
+    if (present) {
       if (defer) {
         // (a resident grid: let the gate+up weights stream first)
         const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
@@ -1079,21 +1092,36 @@ __global__ __launch_bounds__(kThreads, RPL == 1 ? 4 : 2) void k_moe_decode(Decod
   __shared__ float s_rows[kBlockRowsMax * kNmax];
   const int bid = blockIdx.x;
   unsigned tag;  // this call's tag, read by each phase with its first loads
+  // The call counter (the epoch, from which the next call takes its tag)
+  // advances once every workgroup has read this call's tag: each workgroup
+  // reports once, after its tag has reached all of its waves, and whichever
+  // reports last advances it. Reports are counted in two levels (per done
+  // group, then groups) so that no single counter takes an atomic from every
+  // workgroup.
+  const unsigned total = (unsigned)(a.nR + a.nGs + a.nGr + a.nDs + a.nDr);
+  const unsigned g = (unsigned)bid % kDoneGroups;
+  const unsigned in_group = (total - g + kDoneGroups - 1) / kDoneGroups;
+  const unsigned groups = total < (unsigned)kDoneGroups ? total : (unsigned)kDoneGroups;
+  unsigned* done_ctr = &a.ctl->group_done[g * kLineWords];
+  // down workgroups report as soon as they hold the tag (their atomic's
+  // result is looked at only here at the end), so that the last workgroups
+  // to finish, which are down workgroups, end without a counting round trip
+  bool arrived = false;
+  unsigned d = 0;  // thread 0: the group count this workgroup's report met
   if (bid < a.nR) {
     router_phase(a, bid, smem, s_rows, tag);
   } else if (bid < a.nR + a.nGs + a.nGr) {
     gate_up_phase<FR, FS, RPL>(a, bid - a.nR, smem, s_rows, s_words, tag);
   } else {
-    down_phase<FR, FS, RPL>(a, bid - a.nR - a.nGs - a.nGr, smem, &s_tmp, s_words, tag);
+    down_phase<FR, FS, RPL>(a, bid - a.nR - a.nGs - a.nGr, smem, &s_tmp, s_words, tag, done_ctr,
+                            arrived, d);
   }
-  // The last workgroup to finish advances the call counter and clears the
-  // unit counters. Completion is counted in two levels (per done group, then
-  // groups) so that no single counter takes an atomic from every workgroup.
-  const unsigned total = (unsigned)(a.nR + a.nGs + a.nGr + a.nDs + a.nDr);
-  const unsigned g = (unsigned)bid % kDoneGroups;
-  const unsigned in_group = (total - g + kDoneGroups - 1) / kDoneGroups;
-  const unsigned groups = total < (unsigned)kDoneGroups ? total : (unsigned)kDoneGroups;
-  const unsigned d = wg_signal(&a.ctl->group_done[g * kLineWords], &s_tmp, false);
+  if (!arrived) {
+    // (the barrier inside waits for every wave's loads, the tag's included)
+    d = wg_signal(done_ctr, &s_tmp, false);
+  } else if (threadIdx.x != 0) {
+    return;
+  }
   if (d + 1 != in_group) return;
   if (threadIdx.x == 0) {
     st_coh(&a.ctl->group_done[g * kLineWords], 0u);
