@@ -38,6 +38,7 @@ MALL_BYTES = 256 << 20
 KERNELS = {1: ["k_moe_decode"],
            5: ["k_g_router", "k_g_topk", "k_g_gate_up", "k_g_down", "k_g_combine"]}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_counters.json")
 
 
 def hip():
@@ -122,20 +123,42 @@ def kernel_sources_sha256() -> str:
     return h.hexdigest()
 
 
-def traffic_for(key: str):
-    """HBM bytes per launch from the committed counter summary, or None when
-    there is none for this kernel and workload or the sources changed since."""
+def _counter_file(path: str, key: str):
+    """(file record, entry) of a committed counter summary, or None when there
+    is none for this kernel and workload or the sources changed since."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(path) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
     if rec.get("sources_sha256") != kernel_sources_sha256():
         return None
     ent = rec.get("entries", {}).get(key)
-    if not ent:
+    return (rec, ent) if ent else None
+
+
+def traffic_for(key: str):
+    """(HBM bytes per launch, algorithmic bytes per launch) of the counter
+    run: FETCH_SIZE and WRITE_SIZE scaled by a copy kernel's readings, taken
+    on the profiling driver's layer of the same workload, whose routing (and
+    so its algorithmic bytes) differs a little from this run's."""
+    got = _counter_file(TRAFFIC_FILE, key)
+    if got is None:
         return None
-    return (ent["fetch_kib"] * rec["fetch_scale"] + ent["write_kib"] * rec["write_scale"]) * 1024.0
+    rec, ent = got
+    hbm = (ent["fetch_kib"] * rec["fetch_scale"] + ent["write_kib"] * rec["write_scale"]) * 1024.0
+    return hbm, ent.get("alg_bytes_per_launch")
+
+
+def mfma_counters_for(key: str):
+    """MFMA busy fraction and executed BF16 MFMA FLOP per launch from the
+    committed counter summary (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE
+    of one XCD times the 1024 SIMDs; SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)."""
+    got = _counter_file(MFMA_FILE, key)
+    if got is None:
+        return None
+    _, ent = got
+    return {"busy_frac": ent["busy_frac"], "mfma_flop_per_launch": ent["mfma_flop_per_launch"]}
 
 
 def measure(args, config, n, accum=None, layer=None, cpu_seconds=0.0):
@@ -270,8 +293,13 @@ def measure(args, config, n, accum=None, layer=None, cpu_seconds=0.0):
         traffic = traffic_for(key)
         roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None if traffic is None else round(traffic),
+                "traffic": None if traffic is None else round(traffic[0]),
                 "bytes_per_launch": float(dom_bytes.mean()), "avg_launch_us": float(dom_us.mean())}
+        if traffic is not None and traffic[1]:
+            # the counter run's own algorithmic bytes per launch (its layer
+            # routes a little differently), and the ratio of the two
+            roof["traffic_alg_bytes"] = traffic[1]
+            roof["traffic_over_alg"] = round(traffic[0] / traffic[1], 4)
         if nl > 1:
             gu_tf = flops_gu / (durs[:, 2].mean() * 1e-6) / 1e12
             dn_tf = flops_dn / (durs[:, 3].mean() * 1e-6) / 1e12
@@ -281,6 +309,11 @@ def measure(args, config, n, accum=None, layer=None, cpu_seconds=0.0):
                             "gate_up_util": round(gu_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                             "down_util": round(dn_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                             "flops_per_call": flops_gu + flops_dn}
+            for kn in ("k_g_gate_up", "k_g_down"):
+                mc = mfma_counters_for(f"{kn}:{config}:N={n}:{accum}")
+                if mc is not None:  # rocprofv3 counter readings (padding rows included)
+                    roof["mfma"][f"{kn}_counter_busy_frac"] = mc["busy_frac"]
+                    roof["mfma"][f"{kn}_counter_mfma_flop"] = mc["mfma_flop_per_launch"]
             roof["down_gbps"] = round(dn_gbs, 1)
         experts_gbs = float(expert_bytes.sum() / (durs.sum() * 1e-6) / 1e9)
         for row in ev:

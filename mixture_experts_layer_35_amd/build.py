@@ -60,6 +60,27 @@ def build(verbose: bool = False) -> str:
             sys.stderr.write(r.stdout + r.stderr)
             raise RuntimeError(f"hipcc link failed ({r.returncode})")
     os.replace(tmp, out)
+    build_driver(verbose)
+    return out
+
+
+DRIVER = "moe_profile_driver"
+
+
+def build_driver(verbose: bool = False) -> str:
+    """The stand-alone profiling driver (csrc/moe_profile_driver.cpp), linked
+    against the library next to it."""
+    out = os.path.join(PKG, DRIVER)
+    cmd = [hipcc()] + HIP_FLAGS + ["-I", os.path.join(ROOT, "include"), "-x", "hip",
+                                   os.path.join(PKG, "csrc", DRIVER + ".cpp"), "-o", out + ".tmp",
+                                   "-L", PKG, "-l:" + LIB_NAME, "-Wl,-rpath,$ORIGIN"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc (profiling driver) failed ({r.returncode})")
+    os.replace(out + ".tmp", out)
     return out
 
 
