@@ -399,3 +399,17 @@ def test_no_alloc_refuses_calls_beyond_the_static_scratch():
     st = lib.moe_forward_no_alloc(ctypes.byref(c), ctypes.byref(r), ctypes.byref(ex),
                                   ctypes.byref(sh), FAKE, 0, FAKE, None, None, None)
     assert st == B.MOE_ERR_INVALID_ARG and "n_tokens=0" in B.last_error()
+
+
+def test_profile_driver_refuses_bad_arguments():
+    """The stand-alone profiling driver (built next to the library) checks
+    its arguments on the host before it touches a GPU."""
+    import subprocess
+    drv = os.path.join(os.path.dirname(B.LIB_PATH), "moe_profile_driver")
+    if not os.path.exists(drv):
+        pytest.skip("profiling driver not built (run __graft_entry__.build())")
+    for args in ([], ["layer", "no_such_workload", "1", "1"], ["layer", "tiny_bf16", "0", "1"],
+                 ["layer", "tiny_bf16", "3", "1", "fp16"], ["copy", "0", "1"], ["read", "16", "1000"]):
+        r = subprocess.run([drv] + args, capture_output=True, text=True, timeout=60)
+        assert r.returncode == 2, (args, r.returncode, r.stderr)
+        assert "usage" in r.stderr or "unknown workload" in r.stderr, (args, r.stderr)
