@@ -214,7 +214,7 @@ GPlan gplan(const moe_cfg* c, int n, bool gated) {
   g.ksplit = (chunks + g.kcps - 1) / g.kcps;
   g.s_tg = (n + T - 1) / T;
   g.gu_r = c->inter / 64;
-  g.dn_r = c->hidden / moe::kGRowsPerWG;
+  g.dn_r = c->hidden / moe::g_down_rows(g.nt);
   g.gu_s = c->shared_inter > 0 ? (c->shared_inter / 64) * g.s_tg : 0;
   g.dn_s = c->shared_inter > 0 ? g.dn_r * g.s_tg : 0;
   g.mcap = align_up((size_t)slots + (size_t)15 * g.maxu, 16);

@@ -425,21 +425,23 @@ __global__ __launch_bounds__(kGThreads, NTMAX == 1 ? 4 : 1) void k_g_gate_up(Gro
 }
 
 // ---------------------------------------------------------------------------
-// Down. Workgroup = (unit, 128 output rows [, token group]); wave w owns rows
-// h0 + 32w + [0, 32) as two tiles.
+// Down. Workgroup = (unit, DR output rows [, token group]), DR = 64 or 128
+// (g_down_rows); wave w owns rows h0 + 16 NA w + [0, 16 NA) as NA = DR / 64
+// tiles.
 // ---------------------------------------------------------------------------
-template <int F, int NT>
+template <int F, int NT, int NA = 2>
 __device__ __forceinline__ void down_pass(const GroupedArgs& a, const MatView& md, int h0,
                                           const XRows& x, int nchunks, int rows, bool shared,
                                           int row0, uint4* lds) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  ARow ar[2] = {arow(md, h0 + 32 * wave + (lane & 15)),
-                arow(md, h0 + 32 * wave + 16 + (lane & 15))};
-  f32x4 acc[2][NT];
-  stream_gemm<F, 2, NT>(acc, ar, x, nchunks, lds);
+  ARow ar[NA];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int ho = h0 + 32 * wave + 16 * t + 4 * (lane >> 4);
+  for (int t = 0; t < NA; ++t) ar[t] = arow(md, h0 + 16 * NA * wave + 16 * t + (lane & 15));
+  f32x4 acc[NA][NT];
+  stream_gemm<F, NA, NT>(acc, ar, x, nchunks, lds);
+#pragma unroll
+  for (int t = 0; t < NA; ++t) {
+    const int ho = h0 + 16 * NA * wave + 16 * t + 4 * (lane >> 4);
     float sd[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) sd[r] = out_scale<F>(md, ho + r);
@@ -477,7 +479,8 @@ __global__ __launch_bounds__(kGThreads) void k_g_down(GroupedArgs a) {
   extern __shared__ uint4 g_lds[];
   const int bid = blockIdx.x;
   constexpr int T = 16 * NTMAX;
-  const int tiles = a.H / kGRowsPerWG;
+  constexpr int DR = g_down_rows(NTMAX);
+  const int tiles = a.H / DR;
   if (bid < a.dn_s) {
     if constexpr (FS != FMT_NONE) {
       const int tile = bid % tiles, tg = bid / tiles;
@@ -486,7 +489,7 @@ __global__ __launch_bounds__(kGThreads) void k_g_down(GroupedArgs a) {
       const XRows x{a.a_shared + (int64_t)t0 * a.I_s, a.I_s, nullptr, m};
       const MatView md = gview(a.sdown, 0);
       with_tiles<NTMAX>((m + 15) >> 4, [&](auto nt) {
-        down_pass<FS, decltype(nt)::value>(a, md, tile * kGRowsPerWG, x, a.I_s / kGKC, m, true,
+        down_pass<FS, decltype(nt)::value, DR / 64>(a, md, tile * DR, x, a.I_s / kGKC, m, true,
                                            t0, g_lds);
       });
     }
@@ -503,7 +506,7 @@ __global__ __launch_bounds__(kGThreads) void k_g_down(GroupedArgs a) {
   const int m = min(cnt - p0, T);
   const XRows x{a.a_perm + (int64_t)(rb + p0) * a.I, a.I, nullptr, m};
   with_tiles<NTMAX>((m + 15) >> 4, [&](auto nt) {
-    down_pass<FR, decltype(nt)::value>(a, md, tile * kGRowsPerWG, x, a.I / kGKC, m, false,
+    down_pass<FR, decltype(nt)::value, DR / 64>(a, md, tile * DR, x, a.I / kGKC, m, false,
                                        rb + p0, g_lds);
   });
 }

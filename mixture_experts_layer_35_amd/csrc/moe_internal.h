@@ -125,6 +125,10 @@ struct DecodeArgs {
 // ---------------------------------------------------------------------------
 constexpr int kGKC = 128;         // K columns per staged activation chunk
 constexpr int kGRowsPerWG = 128;  // weight rows per workgroup (4 waves x 2 tiles x 16)
+// Output rows of a down workgroup: 64 (one tile per wave) for batches of up to
+// 64 tokens, so that a grid just above one round of resident workgroups
+// leaves a tail half as long; 128 above.
+__host__ __device__ constexpr int g_down_rows(int nt) { return nt == 1 ? 64 : kGRowsPerWG; }
 constexpr int kGLaunches = 5;     // router, top-k (+ grouping), gate+up, down, combine
 
 // Result of the grouping step, read by the expert kernels.
