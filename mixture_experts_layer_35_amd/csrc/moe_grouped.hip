@@ -20,7 +20,7 @@
 //            unit's rows as two 16x16 tiles per wave, a = silu(g) * u in BF16
 //            into the permuted activation buffer; the shared expert is one
 //            more unit holding every token
-//   down     one workgroup per (unit, 128 output rows): d = Wd a; slot mode
+//   down     one workgroup per (unit, 64 or 128 output rows): d = Wd a; slot mode
 //            stores d per permuted row, atomic mode adds w * d into an FP32
 //            [N,H] accumulator
 //   combine  y[t] = sum_j w[t,j] d[row(t,j)] + shared[t] in slot order, BF16
