@@ -319,6 +319,20 @@ __device__ __forceinline__ void with_tiles(int nt, Fn&& fn) {
   if constexpr (NTMAX >= 8) fn(std::integral_constant<int, 8>{});
 }
 
+// Work item and tile of routed workgroup b of the large-batch gate+up kernel.
+// Workgroup b runs on XCD b mod 8 (counted from the routed part's start), so
+// items go in groups of eight, the tiles of item 8g + x all on one XCD and
+// interleaved with the group's other seven: the tiles of an item then share
+// that XCD's L2 copy of the item's token rows instead of each XCD fetching
+// them. (With up to 64 tokens the rows are few and the plain order, the
+// tiles of one item next to each other, measured faster.)
+__device__ __forceinline__ void xcd_item(int b, int tiles, int& item, int& tile) {
+  const int G = 8 * tiles;
+  const int g = b / G, r = b - g * G;
+  tile = r >> 3;
+  item = 8 * g + (r & 7);
+}
+
 __device__ __forceinline__ MatView gview(const DevProj& p, int e) {
   MatView m;
   m.data = p.data + (int64_t)e * p.expert_bytes;
@@ -409,7 +423,13 @@ __global__ __launch_bounds__(kGThreads, NTMAX == 1 ? 4 : 1) void k_g_gate_up(Gro
   }
   // one work item: T rows (a pass) of one unit
   const int b = bid - a.gu_s;
-  const int i = b / a.gu_r, tile = b % a.gu_r;
+  int i, tile;
+  if constexpr (NTMAX == 8) {
+    xcd_item(b, a.gu_r, i, tile);
+  } else {
+    i = b / a.gu_r;
+    tile = b - i * a.gu_r;
+  }
   if (i >= a.info->nitems) return;
   const int item = a.info->item[i];
   const int u = item >> 16, p0 = (item & 0xffff) * T;
@@ -533,9 +553,10 @@ hipError_t launch_experts<FMT_NVFP4>(const GroupedArgs&, int, hipStream_t, hipEv
 
 template <int FR, int FS, int NT>
 hipError_t launch_experts_t(const GroupedArgs& a, hipStream_t st, hipEvent_t* ev) {
+  // (the large-batch gate+up kernel takes its items in groups of eight: xcd_item)
+  const int gu_items = NT == 8 ? (a.max_items + 7) / 8 * 8 : a.max_items;
   hipError_t err = launch_one(reinterpret_cast<const void*>(&k_g_gate_up<FR, FS, NT>),
-                              a.gu_s + a.max_items * a.gu_r, kGThreads, gemm_lds(NT), st, a, ev,
-                              2);
+                              a.gu_s + gu_items * a.gu_r, kGThreads, gemm_lds(NT), st, a, ev, 2);
   if (err != hipSuccess) return err;
   return launch_one(reinterpret_cast<const void*>(&k_g_down<FR, FS, NT>),
                     a.dn_s + a.max_items * a.dn_r, kGThreads, gemm_lds(NT), st, a, ev, 3);
