@@ -189,16 +189,43 @@ struct GPlan {
   size_t mcap;  // rows of the permuted buffers
 };
 
-GPlan gplan(const moe_cfg* c, int n, bool gated) {
+// 16-token tiles per pass of the expert kernels for a call of n tokens.
+// Up to 64 tokens: one (a unit with more rows than that is split into several
+// work items, one workgroup each, so the kernel keeps the registers of one
+// tile and four workgroups per compute unit). Above, the kernels' registers
+// grow with the tile count (one workgroup per compute unit with eight tiles,
+// two with four, three with two), and FP8 and FP4 weights put fewer bytes in
+// flight per load than BF16, so they need the occupancy of fewer tiles. The
+// rule, from same-session timings of 1, 2, 4 and 8 tiles at 128 to 1024
+// tokens: BF16 experts take two tiles while the batch averages at most 8 rows
+// per expert and eight above; FP8 and FP4 experts take two while it averages
+// at most 16 rows per expert (with a shared expert, whose passes cover every
+// token: up to 128 tokens) and four above. Then more, if the work items would
+// not fit their list.
+int grouped_tiles(const moe_cfg* c, int n, int routed_fmt, bool has_shared) {
+  if (n <= 64) return 1;
+  const int64_t slots = (int64_t)n * c->top_k;
+  const int64_t per_expert = slots / c->num_experts;  // average rows per expert
+  int nt;
+  if (routed_fmt == MOE_FMT_BF16)
+    nt = per_expert <= 8 ? 2 : 8;
+  else
+    nt = (has_shared ? n <= 128 : per_expert <= 16) ? 2 : 4;
+  const int64_t maxu = slots < c->num_experts ? slots : c->num_experts;
+  while (nt < 8 && maxu + (slots + 16 * nt - 1) / (16 * nt) > moe::kMaxItems) nt <<= 1;
+  return nt;
+}
+
+// nt: the call's tiles per pass (grouped_tiles), or 0 for the workspace
+// layout, which takes the largest choice (one up to 64 tokens, eight above):
+// the router partials' buffer only grows with the tile count, and nothing
+// else in the layout depends on it.
+GPlan gplan(const moe_cfg* c, int n, bool gated, int nt = 0) {
   GPlan g;
   // router rows: E experts and Z zero experts in blocks of 128, plus a block
   // of its own for the shared gate's row
   const int EW = c->num_experts + c->zero_experts;
-  // 16-token tiles per pass of the expert kernels: one up to 64 tokens (a
-  // unit with more rows than that is split into several work items, one
-  // workgroup each, so the kernel keeps the registers of one tile and four
-  // workgroups per compute unit), eight above
-  g.nt = n <= 64 ? 1 : 8;
+  g.nt = nt > 0 ? nt : (n <= 64 ? 1 : 8);
   const int T = 16 * g.nt;
   g.W = (n + 31) / 32;
   const int64_t slots = (int64_t)n * c->top_k;
@@ -440,7 +467,7 @@ moe_status forward_grouped(const moe_cfg* cfg, const moe_router* router,
     a.sdown = to_dev(shared->down);
     fs = shared->gate.format;
   }
-  const GPlan g = gplan(cfg, n, gated);
+  const GPlan g = gplan(cfg, n, gated, grouped_tiles(cfg, n, fr, a.I_s > 0));
   a.nt = g.nt;
   a.W = g.W;
   a.maxu = g.maxu < a.EL ? g.maxu : a.EL;

@@ -319,7 +319,8 @@ __device__ __forceinline__ void with_tiles(int nt, Fn&& fn) {
   if constexpr (NTMAX >= 8) fn(std::integral_constant<int, 8>{});
 }
 
-// Work item and tile of routed workgroup b of the large-batch gate+up kernel.
+// Work item and tile of routed workgroup b of the gate+up kernels of two or
+// more token tiles (batches above 64 tokens).
 // Workgroup b runs on XCD b mod 8 (counted from the routed part's start), so
 // items go in groups of eight, the tiles of item 8g + x all on one XCD and
 // interleaved with the group's other seven: the tiles of an item then share
@@ -424,7 +425,7 @@ __global__ __launch_bounds__(kGThreads, NTMAX == 1 ? 4 : 1) void k_g_gate_up(Gro
   // one work item: T rows (a pass) of one unit
   const int b = bid - a.gu_s;
   int i, tile;
-  if constexpr (NTMAX == 8) {
+  if constexpr (NTMAX >= 2) {
     xcd_item(b, a.gu_r, i, tile);
   } else {
     i = b / a.gu_r;
@@ -553,8 +554,9 @@ hipError_t launch_experts<FMT_NVFP4>(const GroupedArgs&, int, hipStream_t, hipEv
 
 template <int FR, int FS, int NT>
 hipError_t launch_experts_t(const GroupedArgs& a, hipStream_t st, hipEvent_t* ev) {
-  // (the large-batch gate+up kernel takes its items in groups of eight: xcd_item)
-  const int gu_items = NT == 8 ? (a.max_items + 7) / 8 * 8 : a.max_items;
+  // (the gate+up kernels of two or more tiles take their items in groups of
+  // eight: xcd_item)
+  const int gu_items = NT >= 2 ? (a.max_items + 7) / 8 * 8 : a.max_items;
   hipError_t err = launch_one(reinterpret_cast<const void*>(&k_g_gate_up<FR, FS, NT>),
                               a.gu_s + gu_items * a.gu_r, kGThreads, gemm_lds(NT), st, a, ev, 2);
   if (err != hipSuccess) return err;

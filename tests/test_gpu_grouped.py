@@ -106,6 +106,28 @@ def test_decode_sized_batch_on_grouped_path():
     _case("tiny_bf16", 3, seed=346)
 
 
+# ---- token tiles per pass above 64 tokens -------------------------------------
+# The host picks 2, 4 or 8 tiles of 16 tokens from the weight format, the
+# average rows per expert (N*k/E) and the shared expert: each case below lands
+# on the tile count named with it.
+
+BF16_E128 = synth.reduced("prefill_bf16_h4096", H=512, I=256, E=128, k=8, name="bf16_e128_g")
+
+
+@pytest.mark.parametrize("cfg,n,tiles", [
+    (MX_G, 100, 2),        # FP4, no shared expert, 12.5 rows per expert
+    (MX_G, 300, 4),        # FP4, no shared expert, 37.5 rows per expert
+    (NV_G, 100, 2),        # FP4 with a shared expert, up to 128 tokens
+    (NV_G, 200, 4),        # FP4 with a shared expert, above 128 tokens
+    (FP8_G, 256, 4),       # FP8 with a shared expert (Zipf-skewed routing)
+    (BF16_E128, 128, 2),   # BF16, 8 rows per expert
+    (BF16_E128, 160, 8),   # BF16, 10 rows per expert
+], ids=["fp4-n100-t2", "fp4-n300-t4", "fp4sh-n100-t2", "fp4sh-n200-t4", "fp8sh-n256-t4",
+        "bf16-n128-t2", "bf16-n160-t8"])
+def test_token_tile_choices(cfg, n, tiles):
+    _case(cfg, n, seed=600 + n + tiles, label=f"grouped {cfg['name']} n={n} ({tiles} tiles)")
+
+
 # ---- full sizes -------------------------------------------------------------
 
 @pytest.mark.parametrize("n", [16, 32, 64])
@@ -120,6 +142,14 @@ def test_prefill_bf16_h4096_full_sampled_tokens():
     # oracle's expert work covers only those)
     tokens = np.sort(np.random.default_rng(9).choice(512, size=24, replace=False))
     _case("prefill_bf16_h4096", 512, seed=500, tokens=tokens)
+
+
+@pytest.mark.parametrize("name,n", [("qwen3_30b_a3b_mxfp4", 512), ("grouped_fp8_h4096", 256)])
+def test_quantised_full_shape_above_64_tokens_sampled(name, n):
+    # four tiles per pass at the full shapes (FP4 without and FP8 with a
+    # shared expert); every row of 8 sampled tokens, the grouping checked whole
+    tokens = np.sort(np.random.default_rng(13 + n).choice(n, size=8, replace=False))
+    _case(name, n, seed=502 + n, tokens=tokens)
 
 
 def test_prefill_bf16_h4096_max_tokens_sampled_tokens():
