@@ -215,6 +215,38 @@ def test_repeated_calls_reuse_workspace(accum):
 
 
 @pytest.mark.parametrize("accum", ["atomic", "slot"])
+@pytest.mark.parametrize("cfg", [NV_SMALL, "qwen3_30b_a3b_mxfp4"], ids=["nvfp4-small", "qwen3"])
+def test_back_to_back_calls_without_host_sync(cfg, accum):
+    # Calls enqueued back to back on one stream, one synchronisation at the
+    # end: each call takes its tag from the call counter that the previous
+    # kernel advanced (once every workgroup holds its tag, which can be before
+    # the last ones finish), so every output must still be its own call's.
+    # (The Qwen3-shaped layer's grid is resident at N = 1 and not at N = 3.)
+    name = cfg if isinstance(cfg, str) else cfg["name"]
+    print(f"[parity] back to back {name} {accum}", flush=True)
+    from mixture_experts_layer_35_amd import Layer
+    from parity_util import device_error
+    layer = synth.make_layer(cfg, device=DEV)
+    npl = synth.as_numpy(layer)
+    acc = tie_free_filter(npl)
+    L = Layer(layer, 4, accum=accum)
+    seq = [(110 + i, (1, 4, 2, 3)[i % 4]) for i in range(12 if isinstance(cfg, dict) else 6)]
+    xs = [synth.make_tokens(layer, n, seed, accept=acc) for seed, n in seq]
+    torch.cuda.synchronize()
+    outs = [L.forward(x) for x in xs]
+    torch.cuda.synchronize()
+    assert device_error(L) == 0
+    for (seed, n), x, out in zip(seq, xs, outs):
+        ref = moe_forward(npl["cfg"], npl, bits(x))
+        o = out.double().cpu().numpy()
+        err = np.linalg.norm(o - ref["y"], axis=1) / np.linalg.norm(ref["y"], axis=1)
+        assert err.max() <= OUT_RTOL, (seed, n, err)
+        assert_elementwise(o, ref["y"], ref["y_sq"], f"back to back n={n} seed={seed}")
+    head = L.workspace[:HEAD_BYTES].view(torch.int32).cpu().numpy()
+    assert head[0] == 0 and head[32] == 0 and head[64] == len(seq), head[[0, 32, 64]]
+
+
+@pytest.mark.parametrize("accum", ["atomic", "slot"])
 def test_decode_after_grouped_on_one_workspace(accum):
     # A grouped call leaves small integers (expert ids, counts, the ticket,
     # token masks) in its buffers, and a decode call's tags are small integers
