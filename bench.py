@@ -360,8 +360,9 @@ DEFAULT_POINTS = (("qwen3_30b_a3b_mxfp4", 3), ("deepseek_v3_nvfp4", 4))
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(expert parallelism would shard experts across GPUs; see the design notes).",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(expert parallelism would shard experts across GPUs; moe_forward_ep_partial "
+              "computes one GPU's share).",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
@@ -410,7 +411,8 @@ def main():
 
 def host_cores() -> int:
     """CPU threads this process may use: the OpenMP thread budget when one is
-    set (the GPU machine sets it to its CPU share), else the affinity mask."""
+    set (a scheduler that gives the process a CPU share sets it), else the affinity
+    mask."""
     env = os.environ.get("OMP_NUM_THREADS", "")
     if env.isdigit() and int(env) > 0:
         return int(env)
