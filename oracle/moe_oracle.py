@@ -1,7 +1,7 @@
 """FP64 CPU oracle for the routed mixture-of-experts layer forward.
 
-TEST INFRASTRUCTURE ONLY. This module is the checker the HIP path is compared
-against. Only the test suite, the smoke check of ``__graft_entry__`` and the
+TEST INFRASTRUCTURE ONLY. The HIP path's results are compared against this
+module's. Only the test suite, the smoke check of ``__graft_entry__`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or run it; the product path
 never does, and it shares no code, table or constant with the HIP kernels.
 
