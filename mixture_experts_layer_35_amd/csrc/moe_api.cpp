@@ -311,7 +311,7 @@ Layout layout(const moe_cfg* c, int32_t n, int path, bool gated, bool universal 
   L.dbuf = take((Nd * kh + Nd) * Hh * 8);
   if (path == MOE_PATH_GROUPED) {
     const GPlan g = gplan(c, n, gated);
-    L.g_mask = take(E * g.W * 4);
+    L.g_mask = take((E * (g.W | 1) + 1) * 4);  // rows of W | 1 words, one word more
     L.g_ticket = take(4);
     L.g_idx = take(N * k * 4);
     L.g_wts = take(N * k * 4);
@@ -470,6 +470,7 @@ moe_status forward_grouped(const moe_cfg* cfg, const moe_router* router,
   const GPlan g = gplan(cfg, n, gated, grouped_tiles(cfg, n, fr, a.I_s > 0));
   a.nt = g.nt;
   a.W = g.W;
+  a.WP = g.W | 1;
   a.maxu = g.maxu < a.EL ? g.maxu : a.EL;
   a.max_items = a.maxu + (g.max_items - g.maxu);
   if (a.max_items > moe::kMaxItems)

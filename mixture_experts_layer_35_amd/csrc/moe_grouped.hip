@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kGThreads) void k_g_router(GroupedArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // clear the token masks (the top-k kernel, launched next, sets them) and,
   // with FP32 accumulation, the accumulator the down kernel adds into
-  for (int i = blockIdx.x * kGThreads + tid; i < a.EL * a.W; i += gridDim.x * kGThreads)
+  for (int i = blockIdx.x * kGThreads + tid; i < a.EL * a.WP + 1; i += gridDim.x * kGThreads)
     a.mask[i] = 0u;
   if (a.atomic) {
     float4* acc4 = reinterpret_cast<float4*>(a.acc);
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kGThreads) void k_g_topk(GroupedArgs a) {
     if (lane < a.k) {
       st_dev(a.idx + t * a.k + lane, my_e);
       const int el = my_e - a.e_lo;  // only this call's experts are grouped
-      if (el >= 0 && el < a.EL) atomicOr(a.mask + (int64_t)el * a.W + (t >> 5), 1u << (t & 31));
+      if (el >= 0 && el < a.EL) atomicOr(a.mask + (int64_t)el * a.WP + (t >> 5), 1u << (t & 31));
     }
     gate_logit = g;
   }
@@ -220,42 +220,93 @@ __global__ __launch_bounds__(kGThreads) void k_g_topk(GroupedArgs a) {
 // ---------------------------------------------------------------------------
 // Grouping, by one workgroup (the last top-k workgroup).
 // ---------------------------------------------------------------------------
-constexpr int kMaskLdsWords = 8192;  // masks of up to 8192 words are copied to LDS
-constexpr int kPreBytes = 16384;     // LDS for word prefixes (one batch of experts)
+// The token masks are kept with an odd row stride WP = W | 1 (words), in
+// global memory and in LDS alike, so that threads walking the words of
+// consecutive experts hit different LDS banks; the global buffer holds one
+// word more than EL * WP, so it is copied in 8-byte words.
+// LDS: counts [256] and bases [257]; one 16-bit prefix (the expert's tokens
+// before it) per group of four mask words; the masks, plus four words of
+// padding (a slot reads the first three words of its four-word group, which
+// may end past its row). At the largest sizes (256 experts, 4096 tokens) this is 147 KB.
+struct GroupLds {
+  int pw;
+  size_t pre_off, m_off, bytes;
+};
 
-size_t grouped_group_lds(int E, int W) {
-  (void)E;
-  (void)W;
-  return (256 + 257) * 4 + kPreBytes + kMaskLdsWords * 4;
+inline __host__ __device__ GroupLds group_lds_layout(int E, int W) {
+  GroupLds L;
+  L.pw = (W + 3) / 4;
+  L.pre_off = (256 + 257) * 4;
+  L.m_off = (L.pre_off + (size_t)E * L.pw * 2 + 15) / 16 * 16;
+  L.bytes = L.m_off + ((size_t)(E * (W | 1) + 1) / 2 * 2 + 4) * 4;
+  return L;
 }
 
+size_t grouped_group_lds(int E, int W) { return group_lds_layout(E, W).bytes; }
+
+__device__ __forceinline__ uint64_t ld_dev64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// This code runs once per call, in one workgroup, with a cold instruction
+// cache: the loops exit as soon as the call's sizes are covered (uniform
+// conditions), so that small calls run little code.
 __device__ void group_slots(const GroupedArgs& a, uint4* g_lds) {
   constexpr int kT = kGThreads;  // one thread per expert (E <= 256)
-  int* cnt = reinterpret_cast<int*>(g_lds);  // [256]
-  int* base = cnt + 256;                     // [257]
-  uint16_t* pre = reinterpret_cast<uint16_t*>(base + 257);  // [EB * W] word prefixes
-  uint32_t* mlds = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(pre) + kPreBytes);
+  constexpr int kSL = 32;        // slots per thread per pass, in groups of four
+  constexpr int kML = 32;        // 8-byte mask loads per thread per batch
+  const int E = a.EL, W = a.W, WP = a.WP;  // the experts this call computes
+  const GroupLds L = group_lds_layout(E, W);
+  char* lb = reinterpret_cast<char*>(g_lds);
+  int* cnt = reinterpret_cast<int*>(lb);  // [256]
+  int* base = cnt + 256;                  // [257]
+  uint16_t* pre = reinterpret_cast<uint16_t*>(lb + L.pre_off);
+  uint32_t* mlds = reinterpret_cast<uint32_t*>(lb + L.m_off);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int E = a.EL, W = a.W;  // the experts this call computes
-  // the first 8 * kT slots' experts, requested together with the masks
   const int nslots = a.N * a.k;
-  int ev0[8];
+  // the first pass's experts, requested together with the masks
+  int ev[kSL];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
+  for (int q = 0; q < kSL; ++q) ev[q] = -1;
+#pragma unroll
+  for (int q = 0; q < kSL; ++q) {
+    if (q * kT >= nslots) break;
     const int sl = q * kT + tid;
-    ev0[q] = sl < nslots ? ld_dev(a.idx + sl) : -1;
+    if (sl < nslots) ev[q] = ld_dev(a.idx + sl);
   }
-  // the token masks, from LDS when they fit (one coalesced copy)
-  const bool staged = E * W <= kMaskLdsWords;
-  if (staged)
-    for (int i = tid; i < E * W; i += kT) mlds[i] = ld_dev(a.mask + i);
+  // the masks to LDS, a plain copy: kML loads in flight per thread, then
+  // their stores
+  {
+    const int n2 = (E * WP + 1) / 2;
+    const uint64_t* src = reinterpret_cast<const uint64_t*>(a.mask);
+    uint64_t* dst = reinterpret_cast<uint64_t*>(mlds);
+    for (int b0 = 0; b0 < n2; b0 += kML * kT) {
+      uint64_t v[kML];
+#pragma unroll
+      for (int q = 0; q < kML; ++q) {
+        if (b0 + q * kT >= n2) break;
+        const int i = b0 + q * kT + tid;
+        v[q] = i < n2 ? ld_dev64(src + i) : 0ull;
+      }
+#pragma unroll
+      for (int q = 0; q < kML; ++q) {
+        if (b0 + q * kT >= n2) break;
+        const int i = b0 + q * kT + tid;
+        if (i < n2) dst[i] = v[q];
+      }
+    }
+  }
   lds_barrier();
-  auto mword = [&](int i) { return staged ? mlds[i] : ld_dev(a.mask + i); };
-  // tokens per expert: thread e sums its mask words
+  // tokens per expert, and the prefix before every fourth word: thread e
+  // walks its words in order
   if (tid < E) {
-    int c = 0;
-    for (int i = 0; i < W; ++i) c += __popc(mword(tid * W + i));
-    cnt[tid] = c;
+    const uint32_t* m = mlds + tid * WP;
+    int run = 0;
+    for (int w = 0; w < W; ++w) {
+      if ((w & 3) == 0) pre[tid * L.pw + (w >> 2)] = (uint16_t)run;
+      run += __popc(m[w]);
+    }
+    cnt[tid] = run;
   }
   lds_barrier();
   // padded exclusive scan, the unit list and the work items (wave 0, four
@@ -319,49 +370,65 @@ __device__ void group_slots(const GroupedArgs& a, uint4* g_lds) {
       a.perm_slot[r] = -1;
     }
   }
-  // ranks, in batches of experts whose word prefixes fit in LDS: thread e
-  // writes the running popcount before each of its words
-  const int eb_max = kPreBytes / (2 * W);
-  for (int e0 = 0; e0 < E; e0 += eb_max) {
-    const int e1 = min(E, e0 + eb_max);
-    if (tid >= e0 && tid < e1) {
-      int run = 0;
-      for (int i = 0; i < W; ++i) {
-        pre[(tid - e0) * W + i] = (uint16_t)run;
-        run += __popc(mword(tid * W + i));
+  // the slots, kSL per thread per pass (the first pass's experts were
+  // requested above); slot sl belongs to token sl / k, stepped along with sl.
+  // A slot's row is its expert's base plus the expert's tokens before the
+  // slot's token (the stable order by token): the prefix of its four-word
+  // group, the whole words before its word in the group and the bits below
+  // the token in its word. A group of slots finds its rows from LDS with no
+  // branch (every read is used, selected), then stores them, so that no
+  // store stands between a load and the use of its value; lanes without a
+  // slot of this share read row 0.
+  const int k = a.k, dq = kT / k, dr = kT % k;
+  for (int s0 = 0; s0 < nslots; s0 += kSL * kT) {
+    if (s0 > 0) {
+#pragma unroll
+      for (int q = 0; q < kSL; ++q) {
+        if (s0 + q * kT >= nslots) break;
+        const int sl = s0 + q * kT + tid;
+        ev[q] = sl < nslots ? ld_dev(a.idx + sl) : -1;
       }
     }
-    lds_barrier();
-    // eight slots per thread per pass, their loads issued together
-    for (int s0 = 0; s0 < nslots; s0 += 8 * kT) {
-      int ev[8];
+    int t = (int)((unsigned)(s0 + tid) / (unsigned)k), r = s0 + tid - t * k;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int sl = s0 + q * kT + tid;
-        if (s0 == 0)
-          ev[q] = ev0[q];
-        else
-          ev[q] = sl < nslots ? ld_dev(a.idx + sl) : -1;
-      }
+    for (int g = 0; g < kSL; g += 4) {
+      if (s0 + g * kT >= nslots) break;
+      int pos[4], tk[4];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int sl = s0 + q * kT + tid;
-        const int e = ev[q] - a.e_lo;  // local expert index
-        if (sl < nslots && (e < 0 || e >= E)) {
-          a.inv[sl] = -1;  // another share's expert, or a zero expert
-          continue;
+      for (int j = 0; j < 4; ++j) {
+        const int e = ev[g + j] - a.e_lo;  // local expert index
+        const bool ok = (unsigned)e < (unsigned)E;  // else another share's or none
+        const int ec = ok ? e : 0, te = ok ? t : 0;
+        const int wq = te >> 5, jm = wq & 3;
+        const uint32_t* m = mlds + ec * WP;
+        const int w0 = wq & ~3;
+        const uint32_t m0 = m[w0], m1 = m[w0 + 1], m2 = m[w0 + 2], mw = m[wq];
+        int rank = pre[ec * L.pw + (wq >> 2)] + base[ec];
+        rank += __popc(m0 & (0u - (uint32_t)(jm > 0))) + __popc(m1 & (0u - (uint32_t)(jm > 1))) +
+                __popc(m2 & (0u - (uint32_t)(jm > 2)));
+        rank += __popc(mw & ((1u << (te & 31)) - 1u));
+        pos[j] = ok ? rank : -1;
+        tk[j] = t;
+        t += dq;
+        r += dr;
+        if (r >= k) {
+          r -= k;
+          ++t;
         }
-        if (e < e0 || e >= e1) continue;
-        const int t = sl / a.k;
-        const uint32_t wd = mword(e * W + (t >> 5));
-        const int rank = pre[(e - e0) * W + (t >> 5)] + __popc(wd & ((1u << (t & 31)) - 1u));
-        const int pos = base[e] + rank;
-        a.perm_tok[pos] = t;
-        a.perm_slot[pos] = sl;
-        a.inv[sl] = pos;
       }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int sl = s0 + (g + j) * kT + tid;
+        if (sl < nslots) {
+          a.inv[sl] = pos[j];
+          if (pos[j] >= 0) {
+            a.perm_tok[pos[j]] = tk[j];
+            a.perm_slot[pos[j]] = sl;
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    lds_barrier();
   }
 }
 

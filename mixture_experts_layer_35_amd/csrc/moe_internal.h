@@ -170,6 +170,7 @@ struct GroupedArgs {
   float rsf;
   int nt;      // 16-token MFMA tiles per pass (1, 2, 4 or 8)
   int W;       // token-mask words per expert, ceil(N / 32)
+  int WP;      // token-mask row stride in words, W | 1 (odd)
   int maxu;    // min(E, N * k)
   int max_items;  // bound on the work items: maxu + ceil(N * k / (16 * nt))
   int ksplit;  // router: H split into ksplit ranges of kcps 128-column chunks

@@ -101,6 +101,15 @@ def test_many_experts_many_tokens():
     _case(cfg, 300, seed=345)
 
 
+def test_many_experts_max_tokens():
+    # 256 experts and the largest batch: 128 mask words per expert, so the
+    # grouping workgroup holds its largest LDS (about 147 KB); the grouping is
+    # checked whole, the output on every row of 16 sampled tokens
+    cfg = synth.reduced("deepseek_v3_nvfp4", H=256, I=128, E=256, k=8, I_s=0, name="e256_n4096")
+    tokens = np.sort(np.random.default_rng(17).choice(4096, size=16, replace=False))
+    _case(cfg, 4096, seed=347, tokens=tokens)
+
+
 def test_decode_sized_batch_on_grouped_path():
     # the grouped path takes any N, also the decode sizes
     _case("tiny_bf16", 3, seed=346)
