@@ -275,6 +275,12 @@ struct Layout {
 // Largest decode-path widths (the decode path stages kNmax rows of each in
 // 64 KiB of LDS) and top-k: the universal layout sizes its head and decode
 // region for them.
+// the grouping workgroup of the largest call the library takes fits the 160 KB
+// of LDS a workgroup may hold
+static_assert(moe::group_lds_layout(MOE_MAX_EXPERTS, (MOE_MAX_TOKENS + 31) / 32).bytes <=
+                  160 * 1024,
+              "grouping LDS");
+
 constexpr size_t kDecodeMaxWidth = 8192;
 constexpr size_t kUniversalTopk = MOE_MAX_TOPK;
 

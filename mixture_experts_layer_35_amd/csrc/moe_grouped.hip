@@ -220,28 +220,7 @@ __global__ __launch_bounds__(kGThreads) void k_g_topk(GroupedArgs a) {
 // ---------------------------------------------------------------------------
 // Grouping, by one workgroup (the last top-k workgroup).
 // ---------------------------------------------------------------------------
-// The token masks are kept with an odd row stride WP = W | 1 (words), in
-// global memory and in LDS alike, so that threads walking the words of
-// consecutive experts hit different LDS banks; the global buffer holds one
-// word more than EL * WP, so it is copied in 8-byte words.
-// LDS: counts [256] and bases [257]; one 16-bit prefix (the expert's tokens
-// before it) per group of four mask words; the masks, plus four words of
-// padding (a slot reads the first three words of its four-word group, which
-// may end past its row). At the largest sizes (256 experts, 4096 tokens) this is 147 KB.
-struct GroupLds {
-  int pw;
-  size_t pre_off, m_off, bytes;
-};
-
-inline __host__ __device__ GroupLds group_lds_layout(int E, int W) {
-  GroupLds L;
-  L.pw = (W + 3) / 4;
-  L.pre_off = (256 + 257) * 4;
-  L.m_off = (L.pre_off + (size_t)E * L.pw * 2 + 15) / 16 * 16;
-  L.bytes = L.m_off + ((size_t)(E * (W | 1) + 1) / 2 * 2 + 4) * 4;
-  return L;
-}
-
+// (The layout of the grouping's LDS, group_lds_layout, is in moe_internal.h.)
 size_t grouped_group_lds(int E, int W) { return group_lds_layout(E, W).bytes; }
 
 __device__ __forceinline__ uint64_t ld_dev64(const uint64_t* p) {

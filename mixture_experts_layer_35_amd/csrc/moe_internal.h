@@ -207,6 +207,28 @@ struct GroupedArgs {
 // Enqueue the grouped path. ev: null, or 2 events per launch (start, stop).
 hipError_t launch_grouped(const GroupedArgs& a, int fr, int fs, hipStream_t stream,
                           hipEvent_t* ev);
+// The token masks are kept with an odd row stride WP = W | 1 (words), in
+// global memory and in LDS alike, so that threads walking the words of
+// consecutive experts hit different LDS banks; the global buffer holds one
+// word more than EL * WP, so it is copied in 8-byte words.
+// LDS: counts [256] and bases [257]; one 16-bit prefix (the expert's tokens
+// before it) per group of four mask words; the masks, plus four words of
+// padding (a slot reads the first three words of its four-word group, which
+// may end past its row). At the largest sizes (256 experts, 4096 tokens) this is 147 KB.
+struct GroupLds {
+  int pw;
+  size_t pre_off, m_off, bytes;
+};
+
+constexpr __host__ __device__ GroupLds group_lds_layout(int E, int W) {
+  GroupLds L{};
+  L.pw = (W + 3) / 4;
+  L.pre_off = (256 + 257) * 4;
+  L.m_off = (L.pre_off + (size_t)E * L.pw * 2 + 15) / 16 * 16;
+  L.bytes = L.m_off + ((size_t)(E * (W | 1) + 1) / 2 * 2 + 4) * 4;
+  return L;
+}
+
 size_t grouped_group_lds(int E, int W);
 
 int lanes_per_row(int fmt, int cols);
