@@ -190,3 +190,53 @@ def check_against_oracle(layer, x, accum=None, rows=None, label="", path="auto",
     ratio = assert_elementwise(o[tok][:, sel], ref["y"], ref["y_sq"], label)
     assert device_error(L) == 0, f"{label}: device error word set"
     return {"rel_l2": float(err.max()), "elem_ratio": ratio, "out": out, "grouped": grouped}
+
+
+# ---- guard regions after the caller's buffers ---------------------------
+# 0xFF bytes: NaN in BF16, FP8 E4M3, E8M0, E4M3 and FP32; -6 in FP4 E2M1.
+
+GUARD = 4096  # bytes of 0xFF after each buffer
+
+
+class Guards:
+    """Copies tensors into allocations with a 0xFF tail and remembers them."""
+
+    def __init__(self):
+        self.bufs = []
+
+    def wrap(self, t):
+        if t is None:
+            return None
+        t = t.contiguous()
+        nb = t.numel() * t.element_size()
+        buf = torch.full((nb + GUARD,), 0xFF, dtype=torch.uint8, device=t.device)
+        buf[:nb].copy_(t.view(torch.uint8).reshape(-1))
+        self.bufs.append(buf)
+        return buf[:nb].view(t.dtype).view(t.shape)
+
+    def intact(self):
+        return all(bool((b[-GUARD:] == 0xFF).all().item()) for b in self.bufs)
+
+
+def _guard_proj(p, G):
+    if p is None:
+        return None
+    q = dict(p)
+    for key in ("data", "scales", "tensor_scale"):
+        if q.get(key) is not None:
+            q[key] = G.wrap(q[key])
+    return q
+
+
+def guard_layer(layer, G):
+    r = dict(layer["router"])
+    for key in ("weight", "bias", "shared_gate"):
+        if r.get(key) is not None:
+            r[key] = G.wrap(r[key])
+    if r.get("weight_q") is not None:
+        r["weight_q"] = _guard_proj(r["weight_q"], G)
+    experts = {k: _guard_proj(v, G) for k, v in layer["experts"].items()}
+    shared = None
+    if layer["shared"] is not None:
+        shared = {k: _guard_proj(v, G) for k, v in layer["shared"].items()}
+    return {"cfg": layer["cfg"], "router": r, "experts": experts, "shared": shared}

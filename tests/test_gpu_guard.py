@@ -1,0 +1,80 @@
+"""Reads and writes stay inside the caller's buffers.
+
+Every weight, scale, router and token buffer the library is given is followed
+by a guard region of 0xFF bytes: NaN in BF16, FP8 E4M3, the E8M0 and E4M3
+block scales and FP32, and -6 in FP4 E2M1. A kernel that read past a buffer
+and used what it read would fail the parity bar (indices bit-exact, every
+output element within the element-wise bound). The output and the workspace
+of a second run are guarded the same way, and every guard must still hold
+0xFF afterwards (no write past a buffer). The second run's output must match
+the first's: bit for bit in slot order, within one BF16 unit in the last
+place with FP32 atomics (whose order of addition varies).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from parity_util import (Guards, bf16_to_f64, bits, check_against_oracle, device_error,
+                         guard_layer, tie_free_filter)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+NV_R = synth.reduced("deepseek_v3_nvfp4", H=1024, I=256, E=32, k=8, I_s=384,
+                     name="nvfp4_h1024_guard")
+NV_RQ = synth.reduced("deepseek_v3_nvfp4", H=1024, I=256, E=32, k=8, I_s=384,
+                      router_fmt="nvfp4", name="nvfp4_router_guard")
+FP8_R = synth.reduced("grouped_fp8_h4096", H=512, I=384, E=16, k=4, I_s=256,
+                      name="fp8_h512_guard")
+MX_R = synth.reduced("qwen3_30b_a3b_mxfp4", H=512, I=256, E=32, k=4, name="mxfp4_h512_guard")
+BF16_R = synth.reduced("prefill_bf16_h4096", H=512, I=256, E=128, k=8, name="bf16_e128_guard")
+
+CASES = [
+    ("tiny_bf16", 3, "slot", "auto"),
+    ("tiny_bf16", 17, "atomic", "grouped"),
+    ("qwen3_30b_a3b_mxfp4", 1, "atomic", "auto"),   # full size, decode
+    ("qwen3_30b_a3b_mxfp4", 3, "slot", "auto"),     # full size, decode
+    (NV_R, 4, "atomic", "auto"),                    # NVFP4 experts, BF16 shared expert
+    (NV_R, 20, "slot", "grouped"),
+    (NV_RQ, 4, "slot", "auto"),                     # NVFP4 router
+    (FP8_R, 33, "slot", "grouped"),                 # FP8 row scales, FP8 shared expert
+    (MX_R, 24, "slot", "grouped"),                  # down K = 256: a short last FP4 block
+    (BF16_R, 160, "slot", "grouped"),               # eight token tiles per pass
+]
+
+
+def _name(c):
+    return c if isinstance(c, str) else c["name"]
+
+
+@pytest.mark.parametrize("cfg,n,accum,path", CASES,
+                         ids=[f"{_name(c)}-n{n}-{a}-{p}" for c, n, a, p in CASES])
+def test_no_access_outside_buffers(cfg, n, accum, path):
+    from mixture_experts_layer_35_amd import Layer
+
+    label = f"guard {_name(cfg)} n={n} {accum} {path}"
+    print(f"[guard] {label}", flush=True)
+    G = Guards()
+    layer = guard_layer(synth.make_layer(cfg, device=DEV), G)
+    npl = synth.as_numpy(layer)
+    x = G.wrap(synth.make_tokens(layer, n, 700 + n, accept=tie_free_filter(npl)))
+    # reads: parity with every input followed by poison
+    res = check_against_oracle(layer, x, accum=accum, path=path, label=label)
+    # writes: a second run into a guarded output and workspace
+    L = Layer(layer, n, accum=accum, path=path)
+    L.workspace = G.wrap(L.workspace)
+    out = G.wrap(torch.full_like(x, float("nan")))
+    L.forward(x, out=out)
+    torch.cuda.synchronize()
+    assert device_error(L) == 0, f"{label}: device error word set"
+    assert G.intact(), f"{label}: a guard region was written"
+    a = bf16_to_f64(bits(out))
+    b = bf16_to_f64(bits(res["out"]))
+    if accum == "slot":
+        assert np.array_equal(a, b), f"{label}: the guarded run's output differs"
+    else:
+        assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b))), label
+    print(f"[guard] {label}: rel L2 {res['rel_l2']:.2e}, guards intact", flush=True)
