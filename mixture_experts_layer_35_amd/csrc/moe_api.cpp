@@ -192,7 +192,12 @@ struct GPlan {
 // 16-token tiles per pass of the expert kernels for a call of n tokens.
 // Up to 64 tokens: one (a unit with more rows than that is split into several
 // work items, one workgroup each, so the kernel keeps the registers of one
-// tile and four workgroups per compute unit). Above, the kernels' registers
+// tile and four workgroups per compute unit), except FP8 experts above 48
+// tokens, which take the rule for larger batches (two tiles at these sizes):
+// same-session timings of the grouped FP8 layer (H = 4096, E = 128, k = 8,
+// FP8 shared expert) read 3.5% faster with two at 56 and 64 tokens and 1-3%
+// slower at 40 and 48, while the DeepSeek-V3-shaped NVFP4 layer read 17%
+// slower with two at 48 tokens. Above 64 tokens the kernels' registers
 // grow with the tile count (one workgroup per compute unit with eight tiles,
 // two with four, three with two), and FP8 and FP4 weights put fewer bytes in
 // flight per load than BF16, so they need the occupancy of fewer tiles. The
@@ -203,7 +208,7 @@ struct GPlan {
 // token: up to 128 tokens) and four above. Then more, if the work items would
 // not fit their list.
 int grouped_tiles(const moe_cfg* c, int n, int routed_fmt, bool has_shared) {
-  if (n <= 64) return 1;
+  if (n <= (routed_fmt == MOE_FMT_FP8_ROWSCALE ? 48 : 64)) return 1;
   const int64_t slots = (int64_t)n * c->top_k;
   const int64_t per_expert = slots / c->num_experts;  // average rows per expert
   int nt;
@@ -217,7 +222,7 @@ int grouped_tiles(const moe_cfg* c, int n, int routed_fmt, bool has_shared) {
 }
 
 // nt: the call's tiles per pass (grouped_tiles), or 0 for the workspace
-// layout, which takes the largest choice (one up to 64 tokens, eight above):
+// layout, which takes the largest choice (one up to 48 tokens, eight above):
 // the router partials' buffer only grows with the tile count, and nothing
 // else in the layout depends on it.
 GPlan gplan(const moe_cfg* c, int n, bool gated, int nt = 0) {
@@ -225,7 +230,7 @@ GPlan gplan(const moe_cfg* c, int n, bool gated, int nt = 0) {
   // router rows: E experts and Z zero experts in blocks of 128, plus a block
   // of its own for the shared gate's row
   const int EW = c->num_experts + c->zero_experts;
-  g.nt = nt > 0 ? nt : (n <= 64 ? 1 : 8);
+  g.nt = nt > 0 ? nt : (n <= 48 ? 1 : 8);
   const int T = 16 * g.nt;
   g.W = (n + 31) / 32;
   const int64_t slots = (int64_t)n * c->top_k;

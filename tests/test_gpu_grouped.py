@@ -128,10 +128,12 @@ BF16_E128 = synth.reduced("prefill_bf16_h4096", H=512, I=256, E=128, k=8, name="
     (MX_G, 300, 4),        # FP4, no shared expert, 37.5 rows per expert
     (NV_G, 100, 2),        # FP4 with a shared expert, up to 128 tokens
     (NV_G, 200, 4),        # FP4 with a shared expert, above 128 tokens
+    (FP8_G, 56, 2),        # FP8 above 48 tokens takes the rule for larger batches
     (FP8_G, 256, 4),       # FP8 with a shared expert (Zipf-skewed routing)
     (BF16_E128, 128, 2),   # BF16, 8 rows per expert
     (BF16_E128, 160, 8),   # BF16, 10 rows per expert
-], ids=["fp4-n100-t2", "fp4-n300-t4", "fp4sh-n100-t2", "fp4sh-n200-t4", "fp8sh-n256-t4",
+], ids=["fp4-n100-t2", "fp4-n300-t4", "fp4sh-n100-t2", "fp4sh-n200-t4", "fp8sh-n56-t2",
+        "fp8sh-n256-t4",
         "bf16-n128-t2", "bf16-n160-t8"])
 def test_token_tile_choices(cfg, n, tiles):
     _case(cfg, n, seed=600 + n + tiles, label=f"grouped {cfg['name']} n={n} ({tiles} tiles)")
