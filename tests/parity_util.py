@@ -230,7 +230,7 @@ def _guard_proj(p, G):
 
 def guard_layer(layer, G):
     r = dict(layer["router"])
-    for key in ("weight", "bias", "shared_gate"):
+    for key in ("weight", "bias", "shared_gate", "tid2eid"):
         if r.get(key) is not None:
             r[key] = G.wrap(r[key])
     if r.get("weight_q") is not None:

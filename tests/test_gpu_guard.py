@@ -2,7 +2,8 @@
 
 Every weight, scale, router and token buffer the library is given is followed
 by a guard region of 0xFF bytes: NaN in BF16, FP8 E4M3, the E8M0 and E4M3
-block scales and FP32, and -6 in FP4 E2M1. A kernel that read past a buffer
+block scales and FP32, -6 in FP4 E2M1, and -1 in the int32 token ids and
+hash table (which the kernels flag in the device error word). A kernel that read past a buffer
 and used what it read would fail the parity bar (indices bit-exact, every
 output element within the element-wise bound). The output and the workspace
 of a second run are guarded the same way, and every guard must still hold
@@ -31,6 +32,13 @@ FP8_R = synth.reduced("grouped_fp8_h4096", H=512, I=384, E=16, k=4, I_s=256,
                       name="fp8_h512_guard")
 MX_R = synth.reduced("qwen3_30b_a3b_mxfp4", H=512, I=256, E=32, k=4, name="mxfp4_h512_guard")
 BF16_R = synth.reduced("prefill_bf16_h4096", H=512, I=256, E=128, k=8, name="bf16_e128_guard")
+# hash routing (the token-id table and the token ids are guarded too; their
+# poison reads as id -1, which the kernels flag in the error word) and zero
+# experts
+HASH_R = synth.reduced("deepseek_v3_nvfp4", H=1024, I=256, E=32, Z=4, k=8, I_s=256,
+                       hash_vocab=300, name="hash_zero_experts_guard")
+ZE_R = synth.reduced("deepseek_v3_nvfp4", H=1024, I=256, E=24, Z=8, k=6, I_s=256,
+                     name="zero_experts_sigmoid_guard")
 
 CASES = [
     ("tiny_bf16", 3, "slot", "auto"),
@@ -43,6 +51,9 @@ CASES = [
     (FP8_R, 33, "slot", "grouped"),                 # FP8 row scales, FP8 shared expert
     (MX_R, 24, "slot", "grouped"),                  # down K = 256: a short last FP4 block
     (BF16_R, 160, "slot", "grouped"),               # eight token tiles per pass
+    (HASH_R, 4, "slot", "auto"),
+    (HASH_R, 64, "atomic", "grouped"),
+    (ZE_R, 40, "slot", "grouped"),
 ]
 
 
@@ -61,13 +72,16 @@ def test_no_access_outside_buffers(cfg, n, accum, path):
     layer = guard_layer(synth.make_layer(cfg, device=DEV), G)
     npl = synth.as_numpy(layer)
     x = G.wrap(synth.make_tokens(layer, n, 700 + n, accept=tie_free_filter(npl)))
+    ids = None
+    if layer["cfg"].get("hash_vocab"):
+        ids = G.wrap(synth.make_token_ids(layer, n, 740 + n))
     # reads: parity with every input followed by poison
-    res = check_against_oracle(layer, x, accum=accum, path=path, label=label)
+    res = check_against_oracle(layer, x, accum=accum, path=path, label=label, token_ids=ids)
     # writes: a second run into a guarded output and workspace
     L = Layer(layer, n, accum=accum, path=path)
     L.workspace = G.wrap(L.workspace)
     out = G.wrap(torch.full_like(x, float("nan")))
-    L.forward(x, out=out)
+    L.forward(x, out=out, token_ids=ids)
     torch.cuda.synchronize()
     assert device_error(L) == 0, f"{label}: device error word set"
     assert G.intact(), f"{label}: a guard region was written"
